@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle to facts fixed outside it (the pages, library routines,
+exact arithmetic, invariants).  CPU only.
+
+Each check is chosen so that a plausible slip in the oracle (a swapped nibble, a
+wrong exponent bias, a dropped scale, a sign error, a transposed index, a wrong
+tie rule) fails at least one of them.
+"""
+import json
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import datagen
+import oracle
+from oracle import layout
+
+# ---- independent decoders used by the checks (library routines and the pages) ----
+
+
+def grid_from_page(golden_dir):
+    line = [l for l in (golden_dir / "e2m1_grid.txt").read_text().splitlines() if not l.startswith("#")][0]
+    return [Fraction(v) for v in line.split()]
+
+
+def e2m1_fraction_table(golden_dir):
+    pos = grid_from_page(golden_dir)
+    # sign bit is the top bit of the nibble; magnitude grows with the low 3 bits
+    return pos + [-v for v in pos]
+
+
+def torch_e4m3(b):
+    return float(torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).float())
+
+
+def torch_e8m0(b):
+    return float(torch.tensor([b], dtype=torch.uint8).view(torch.float8_e8m0fnu).float())
+
+
+def torch_bf16(bits_u16):
+    return torch.from_numpy(np.asarray(bits_u16, dtype=np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+# ---- scalar decoders ------------------------------------------------------------
+
+
+def test_e2m1_values_are_the_page_grid(golden_dir):
+    pos = grid_from_page(golden_dir)
+    vals = [oracle.e2m1(c) for c in range(16)]
+    assert sorted(set(abs(v) for v in vals)) == [float(v) for v in pos]
+    # codes 0..7 are the grid in ascending order; 8..15 their negatives (8 = -0)
+    assert vals[:8] == [float(v) for v in pos]
+    assert vals[8:] == [-float(v) for v in pos]
+    assert math.copysign(1.0, vals[8]) == -1.0
+
+
+def test_e4m3_all_codes_match_torch():
+    for b in range(256):
+        ref = torch_e4m3(b)
+        got = oracle.e4m3(b)
+        if math.isnan(ref):
+            assert math.isnan(got), b
+            assert (b & 0x7F) == 0x7F
+        else:
+            assert got == ref and math.copysign(1, got) == math.copysign(1, ref), b
+    assert oracle.e4m3(0x7E) == 448.0 and oracle.e4m3(0x01) == 2.0 ** -9
+
+
+def test_e8m0_all_codes_match_torch():
+    for b in range(256):
+        ref = torch_e8m0(b)
+        got = oracle.e8m0(b)
+        if b == 255:
+            assert math.isnan(got) and math.isnan(ref)
+        else:
+            assert got == ref == 2.0 ** (b - 127), b
+
+
+def test_bf16_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, 4000, dtype=np.uint32).astype(np.uint16)
+    bits = bits[(bits & 0x7F80) != 0x7F80]  # finite only
+    ref = torch_bf16(bits)
+    got = np.array([oracle.bf16(int(b)) for b in bits])
+    assert np.array_equal(got, ref)
+
+
+def test_silu_matches_torch():
+    z = np.linspace(-30, 30, 601)
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    got = np.array([oracle.silu(v) for v in z])
+    np.testing.assert_allclose(got, ref, rtol=1e-15, atol=1e-300)
+    got2 = oracle.silu_mul(z, np.ones_like(z))
+    np.testing.assert_allclose(got2, ref, rtol=1e-15, atol=1e-300)
+
+
+# ---- brute force on 16 x 32 matrices against exact rationals ---------------------
+
+
+def exact_gemv(fmt, codes, scales, ts, X, golden_dir):
+    e2 = e2m1_fraction_table(golden_dir)
+    d_out = codes.shape[0]
+    d_in = codes.shape[1] * (1 if fmt == oracle.FP8_ROW else 2)
+    xs = torch_bf16(X)
+    Y = np.zeros((X.shape[0], d_out), dtype=object)
+    A = np.zeros((X.shape[0], d_out), dtype=object)
+    for r in range(d_out):
+        row = []
+        for k in range(d_in):
+            if fmt == oracle.FP8_ROW:
+                w = Fraction(torch_e4m3(int(codes[r, k]))) * Fraction(float(scales[r]))
+            else:
+                byte = int(codes[r, k // 2])
+                nib = (byte >> 4) if (k % 2) else (byte & 15)
+                if fmt == oracle.NVFP4:
+                    w = e2[nib] * Fraction(torch_e4m3(int(scales[r, k // 16]))) * Fraction(ts)
+                else:
+                    w = e2[nib] * Fraction(torch_e8m0(int(scales[r, k // 32])))
+            row.append(w)
+        for m in range(X.shape[0]):
+            terms = [row[k] * Fraction(float(xs[m, k])) for k in range(d_in)]
+            Y[m, r] = sum(terms, Fraction(0))
+            A[m, r] = sum((abs(t) for t in terms), Fraction(0))
+    return Y, A
+
+
+@pytest.mark.parametrize("fmt", [oracle.NVFP4, oracle.MXFP4, oracle.FP8_ROW])
+@pytest.mark.parametrize("seed", range(6))
+def test_brute_force_16x32(fmt, seed, golden_dir):
+    d_out, d_in, M = 16, 32, 3
+    mat = datagen.matrix(fmt, d_out, d_in, datagen.tensor_seed("bf", fmt, seed))
+    codes, scales = mat["codes"].numpy(), mat["scales"].numpy()
+    if fmt == oracle.NVFP4 and seed % 2:
+        # sweep every finite E4M3 scale code over the seeds
+        codes_all = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+        scales = np.resize(np.roll(codes_all, seed * 7), scales.shape).astype(np.uint8)
+    if fmt == oracle.MXFP4 and seed % 2:
+        scales = np.resize(np.arange(0, 255, dtype=np.uint8)[seed * 13 % 200:], scales.shape).astype(np.uint8)
+        scales = np.clip(scales, 100, 150).astype(np.uint8)
+    ts = 1.0 if fmt != oracle.NVFP4 else [1.0, 0.5, 3.25, 2.0 ** -7, 1.0, 96.0][seed]
+    X = datagen.bf16_normal((M, d_in), datagen.tensor_seed("bfx", seed)).view(torch.int16).numpy().view(np.uint16)
+    Y, A = oracle.gemv(fmt, codes, scales, ts, X)
+    Ye, Ae = exact_gemv(fmt, codes, scales, ts, X, golden_dir)
+    eps = 2.0 ** -53
+    for m in range(M):
+        for r in range(d_out):
+            bound = d_in * eps * float(Ae[m, r])
+            assert abs(Fraction(Y[m, r]) - Ye[m, r]) <= Fraction(bound), (m, r)
+            assert abs(Fraction(A[m, r]) - Ae[m, r]) <= Fraction(bound), (m, r)
+
+
+def test_all_codes_appear_over_brute_force_seeds():
+    seen_codes = set()
+    seen_scales = set()
+    for seed in range(6):
+        mat = datagen.matrix(oracle.NVFP4, 16, 32, datagen.tensor_seed("bf", oracle.NVFP4, seed))
+        c = mat["codes"].numpy()
+        seen_codes |= set((c & 15).ravel().tolist()) | set((c >> 4).ravel().tolist())
+    assert seen_codes == set(range(16))
+
+
+# ---- special cases ---------------------------------------------------------------
+
+
+def test_one_hot_picks_a_column():
+    mat = datagen.matrix(oracle.NVFP4, 64, 256, datagen.tensor_seed("onehot"))
+    W = oracle.dequant(oracle.NVFP4, mat["codes"], mat["scales"], 1.0)
+    for k in (0, 1, 17, 128, 255):
+        X = np.zeros((1, 256), np.uint16)
+        X[0, k] = 0x3F80  # bf16 1.0
+        Y, _ = oracle.gemv(oracle.NVFP4, mat["codes"], mat["scales"], 1.0, X)
+        assert np.array_equal(Y[0], W[:, k])
+        # column k of the dequantised matrix: nibble (k odd: high) of byte k//2 times block scale
+        codes = mat["codes"].numpy()
+        nib = (codes[:, k // 2] >> 4) if k % 2 else (codes[:, k // 2] & 15)
+        sc = np.array([torch_e4m3(int(b)) for b in mat["scales"].numpy()[:, k // 16]])
+        table = np.array([float(v) for v in [0, .5, 1, 1.5, 2, 3, 4, 6]] + [-float(v) for v in [0, .5, 1, 1.5, 2, 3, 4, 6]])
+        assert np.array_equal(W[:, k], table[nib] * sc)
+
+
+def test_sign_flip_negates_exactly():
+    mat = datagen.matrix(oracle.NVFP4, 32, 512, datagen.tensor_seed("flip"))
+    X = datagen.bf16_normal((2, 512), 5).view(torch.int16).numpy().view(np.uint16)
+    Y, _ = oracle.gemv(oracle.NVFP4, mat["codes"], mat["scales"], 1.0, X)
+    flipped = (mat["codes"].numpy() ^ 0x88).astype(np.uint8)
+    Y2, _ = oracle.gemv(oracle.NVFP4, flipped, mat["scales"], 1.0, X)
+    assert np.array_equal(Y2, -Y)
+
+
+def test_zero_scale_block_contributes_nothing():
+    mat = datagen.matrix(oracle.NVFP4, 8, 64, datagen.tensor_seed("zs"))
+    X = datagen.bf16_normal((1, 64), 9).view(torch.int16).numpy().view(np.uint16)
+    sc = mat["scales"].numpy().copy()
+    sc[:, 1] = 0  # second block of every row
+    codes = mat["codes"].numpy().copy()
+    Y, _ = oracle.gemv(oracle.NVFP4, codes, sc, 1.0, X)
+    codes2 = codes.copy()
+    codes2[:, 8:16] = 0x77  # change the codes of the zero-scaled block
+    Y2, _ = oracle.gemv(oracle.NVFP4, codes2, sc, 1.0, X)
+    assert np.array_equal(Y, Y2)
+
+
+def test_tensor_scale_multiplies():
+    mat = datagen.matrix(oracle.NVFP4, 8, 64, datagen.tensor_seed("ts"))
+    X = datagen.bf16_normal((1, 64), 3).view(torch.int16).numpy().view(np.uint16)
+    Y1, _ = oracle.gemv(oracle.NVFP4, mat["codes"], mat["scales"], 1.0, X)
+    Y4, _ = oracle.gemv(oracle.NVFP4, mat["codes"], mat["scales"], 4.0, X)
+    assert np.array_equal(Y4, 4.0 * Y1)
+
+
+def test_rows_subset_matches_full():
+    mat = datagen.matrix(oracle.MXFP4, 40, 96, datagen.tensor_seed("rows"))
+    X = datagen.bf16_normal((2, 96), 4).view(torch.int16).numpy().view(np.uint16)
+    Y, A = oracle.gemv(oracle.MXFP4, mat["codes"], mat["scales"], 1.0, X)
+    rows = [39, 0, 7, 7]
+    Ys, As = oracle.gemv(oracle.MXFP4, mat["codes"], mat["scales"], 1.0, X, rows=rows)
+    assert np.array_equal(Ys, Y[:, rows]) and np.array_equal(As, A[:, rows])
+
+
+def test_matches_numpy_matmul_of_dequantised():
+    # the same product by a library matmul of the dequantised matrix (different
+    # summation order: agreement to FP64 rounding)
+    for fmt in (oracle.NVFP4, oracle.MXFP4, oracle.FP8_ROW):
+        mat = datagen.matrix(fmt, 70, 320, datagen.tensor_seed("mm", fmt))
+        X = datagen.bf16_normal((4, 320), 11).view(torch.int16).numpy().view(np.uint16)
+        W = oracle.dequant(fmt, mat["codes"], mat["scales"], 1.0)
+        Y, A = oracle.gemv(fmt, mat["codes"], mat["scales"], 1.0, X)
+        ref = torch_bf16(X) @ W.T
+        assert np.all(np.abs(Y - ref) <= 1e-12 * A)
+
+
+# ---- routing ---------------------------------------------------------------------
+
+
+def test_topk_matches_python_sort_with_ties():
+    rng = np.random.default_rng(7)
+    for trial in range(50):
+        E = int(rng.choice([16, 64, 512]))
+        k = int(rng.integers(1, 9))
+        # few distinct values so that ties are common
+        logits = rng.integers(-4, 5, size=(3, E)).astype(np.float32) * 0.5
+        ids, w = oracle.topk_softmax(logits, k)
+        for m in range(3):
+            order = sorted(range(E), key=lambda e: (-float(logits[m, e]), e))[:k]
+            assert list(ids[m]) == order
+            ref = scipy.special.softmax(logits[m, order].astype(np.float64))
+            np.testing.assert_allclose(w[m], ref, rtol=1e-14)
+
+
+def test_topk_all_equal_logits():
+    ids, w = oracle.topk_softmax(np.zeros((2, 512), np.float32), 8)
+    assert (ids == np.arange(8)).all()
+    assert (w == 0.125).all()
+
+
+def test_expected_distinct_experts_matches_page(golden_dir):
+    page = json.loads((golden_dir / "page_numbers.json").read_text())["moe_expected_distinct_experts_m4"]
+    E, k, M = page["experts"], page["top_k"], page["tokens"]
+    expect = E * (1 - (1 - k / E) ** M)
+    assert round(expect, 1) == page["value"]
+    # the oracle's router over i.i.d. normal logits reproduces it statistically
+    n = 1500
+    counts = []
+    for t in range(n):
+        logits = datagen.router_logits(M, E, datagen.tensor_seed("distinct", t)).numpy()
+        ids, _ = oracle.topk_softmax(logits, k)
+        counts.append(len(set(ids.ravel().tolist())))
+    counts = np.array(counts, dtype=np.float64)
+    sem = counts.std() / math.sqrt(n)
+    assert abs(counts.mean() - expect) < 4 * sem + 1e-9
+
+
+# ---- MoE composition invariants ----------------------------------------------------
+
+
+def _expert(seed, hidden=64, dff=32):
+    return {
+        "gate": datagen.matrix(oracle.MXFP4, dff, hidden, datagen.tensor_seed(seed, "g")),
+        "up": datagen.matrix(oracle.MXFP4, dff, hidden, datagen.tensor_seed(seed, "u")),
+        "down": datagen.matrix(oracle.MXFP4, hidden, dff, datagen.tensor_seed(seed, "d")),
+    }
+
+
+def test_moe_identical_experts_ignore_routing():
+    ex = _expert("same")
+    sh = _expert("shared")
+    X = datagen.bf16_normal((3, 64), 2).view(torch.int16).numpy().view(np.uint16)
+    logits = datagen.router_logits(3, 16, 5).numpy()
+    out = oracle.moe(lambda e: ex, sh, X, logits, 4)
+    for m in range(3):
+        d = oracle.moe_expert(ex, X[m])["d"]
+        ds = oracle.moe_expert(sh, X[m])["d"]
+        np.testing.assert_allclose(out["y"][m], d + ds, rtol=1e-13, atol=1e-13 * np.abs(d).max())
+
+
+def test_moe_top1_is_the_argmax_expert():
+    experts = {e: _expert(("e", e)) for e in range(8)}
+    X = datagen.bf16_normal((2, 64), 3).view(torch.int16).numpy().view(np.uint16)
+    logits = datagen.router_logits(2, 8, 6).numpy()
+    out = oracle.moe(lambda e: experts[e], None, X, logits, 1)
+    for m in range(2):
+        e = int(np.argmax(logits[m]))
+        assert out["ids"][m, 0] == e and out["w"][m, 0] == 1.0
+        assert np.array_equal(out["y"][m], oracle.moe_expert(experts[e], X[m])["d"])
+
+
+def test_moe_is_the_weighted_sum():
+    experts = {e: _expert(("w", e)) for e in range(6)}
+    X = datagen.bf16_normal((1, 64), 8).view(torch.int16).numpy().view(np.uint16)
+    logits = datagen.router_logits(1, 6, 9).numpy()
+    out = oracle.moe(lambda e: experts[e], None, X, logits, 3)
+    ids, w = out["ids"][0], out["w"][0]
+    ref = sum(w[j] * oracle.moe_expert(experts[int(ids[j])], X[0])["d"] for j in range(3))
+    np.testing.assert_allclose(out["y"][0], ref, rtol=1e-14, atol=1e-14 * np.abs(ref).max())
+
+
+# ---- byte and rate accounting against the pages -------------------------------------
+
+
+def test_byte_counts_match_pages(golden_dir):
+    page = json.loads((golden_dir / "page_numbers.json").read_text())
+    # 4.5 bits per NVFP4 weight: packed image of an aligned matrix
+    d_out, d_in = 17408, 5120
+    assert layout.packed_bytes(oracle.NVFP4, d_out, d_in) * 8 / (d_out * d_in) == page["nvfp4_bits_per_weight"]["value"]
+    # FP8 output layer 248320 x 5120 at one byte per weight: 1.27 GB
+    v, d = page["output_layer_gb"]["shape"]
+    assert round(v * d / 1e9, 2) == page["output_layer_gb"]["value"]
+    # reduced draft head 100,032 rows: 0.51 GB
+    r = page["reduced_draft_head_gb"]
+    assert round(r["rows"] * r["d"] / 1e9, 2) == r["value"]
+    # MoE LM head: 402.39 M parameters, 0.402 GB in FP8, 0.805 GB in BF16
+    h = page["moe_lm_head"]
+    assert round(h["shape"][0] * h["shape"][1] / 1e6, 2) == h["params_m"]
+    assert round(h["shape"][0] * h["shape"][1] / 1e9, 3) == h["fp8_gb"]
+    assert round(2 * h["shape"][0] * h["shape"][1] / 1e9, 3) == h["bf16_gb"]
+    # 168 packed 4-bit tensors = 56 layers x 3 MLP matrices
+    t = page["nvfp4_tensors_4bit"]
+    assert t["layers"] * t["per_layer"] == t["value"]
+
+
+def test_rate_arithmetic_matches_pages(golden_dir):
+    page = json.loads((golden_dir / "page_numbers.json").read_text())
+    M_gb = page["bytes_per_step_gb"]["value"]
+    W = page["bandwidth_gbps"]["value"]
+    assert round(page["bytes_per_step_gb"]["layers_gb"] + page["output_layer_gb"]["value"], 2) == M_gb
+    assert round(M_gb / W * 1e3, 1) == page["bound_ms_per_token"]["value"]
+    assert round(W / M_gb, 1) == page["bound_tok_s"]["value"]
+    assert round(M_gb / page["measured_step_ms"]["value"] * 1e3) == page["measured_step_ms"]["achieved_gbps"]
+    # 16/b flop per byte
+    for b, v in page["intensity_flop_per_byte"]["value"].items():
+        assert 2 * 1 * 1 / (int(b) / 8) == v
+
+
+# ---- the layout reference against its per-element definition ------------------------
+
+
+@pytest.mark.parametrize("fmt", [oracle.NVFP4, oracle.MXFP4, oracle.FP8_ROW])
+def test_layout_reference_places_each_element(fmt):
+    d_out, d_in = 70, 288  # ragged in both directions
+    mat = datagen.matrix(fmt, d_out, d_in, datagen.tensor_seed("lay", fmt))
+    codes, scales = mat["codes"].numpy(), mat["scales"].numpy()
+    img = layout.pack(fmt, codes, scales)
+    assert img.size == layout.packed_bytes(fmt, d_out, d_in)
+    R, C = -(-d_out // 64), -(-d_in // 256)
+    tile = {oracle.NVFP4: 9216, oracle.MXFP4: 8704, oracle.FP8_ROW: 16384}[fmt]
+    rng = np.random.default_rng(0)
+    for _ in range(400):
+        r, k = int(rng.integers(d_out)), int(rng.integers(d_in))
+        g, l, c = r // 64, r % 64, k // 256
+        base = (g * C + c) * tile
+        if fmt == oracle.FP8_ROW:
+            j, b = (k % 256) // 16, k % 16
+            assert img[base + j * 1024 + l * 16 + b] == codes[r, k]
+        else:
+            j, b = (k % 256) // 32, (k % 32) // 2
+            assert img[base + j * 1024 + l * 16 + b] == codes[r, k // 2]
+            if fmt == oracle.NVFP4:
+                assert img[base + 8192 + l * 16 + (k // 16) % 16] == scales[r, k // 16]
+            else:
+                assert img[base + 8192 + l * 8 + (k // 32) % 8] == scales[r, k // 32]
+    if fmt == oracle.FP8_ROW:
+        rs = img[R * C * tile:].view(np.float32)
+        assert np.array_equal(rs[:d_out], scales) and not rs[d_out:].any()
