@@ -1,0 +1,110 @@
+// common.hpp -- shared definitions of the gfx950 kernels and the host-side
+// validation of the C ABI (include/fp4gemv.h).
+//
+// Nothing in here is shared with the CPU oracle: the oracle decodes E2M1, E4M3
+// and E8M0 from their closed forms in double precision, while the kernels use the
+// gfx950 conversion instructions (v_cvt_scalef32_pk_bf16_fp4, v_cvt_f32_fp8,
+// v_cvt_scalef32_pk_bf16_fp8) and FP32 dot products (v_dot2_f32_bf16).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fp4gemv.h"
+
+namespace fp4g {
+
+// ---- packed layout (see fp4g_packed_bytes in the header) ---------------------
+constexpr int kRowsPerGroup = 64;   // one row per lane of a wave64
+constexpr int kChunkK = 256;        // columns per tile
+constexpr int kPieceK = 32;         // columns per 16-byte code load of one lane
+constexpr int kPiecesNv = 8;        // NVFP4/MXFP4: 8 x 16 B code loads per tile and lane
+constexpr int kSlotsFp8 = 16;       // FP8: 16 x 16 B code loads per tile and lane
+constexpr int kTileNv = 9216;       // 8 KiB codes + 64 x 16 B E4M3 scales
+constexpr int kTileMx = 8704;       // 8 KiB codes + 64 x 8 B E8M0 scales
+constexpr int kTileF8 = 16384;      // 16 KiB codes (row scales follow all tiles)
+constexpr int kCodeBytes = 8192;
+constexpr int kMaxM = 8;
+constexpr int kWavesPerWg = 4;
+constexpr int kThreads = 256;
+// Every workspace starts with a fixed region of hand-off counters.  No call ever
+// writes anything else there, so counters left at zero by one call are still zero
+// for the next, whatever the shapes.  Partial sums and tables start after it.
+constexpr uint64_t kCounterBytes = 65536;
+constexpr int kMaxCounters = (int)(kCounterBytes / 4);
+
+__host__ __device__ inline int tile_bytes(uint32_t fmt) {
+  return fmt == FP4G_NVFP4 ? kTileNv : fmt == FP4G_MXFP4 ? kTileMx : kTileF8;
+}
+__host__ __device__ inline int64_t row_groups(int64_t d_out) { return (d_out + 63) / 64; }
+__host__ __device__ inline int64_t chunks(int64_t d_in) { return (d_in + 255) / 256; }
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- device helpers ---------------------------------------------------------
+
+__device__ __forceinline__ u32x4 ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x2 ld_stream2(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// Two E2M1 codes (byte SEL of dw: bits 0-3 -> .x, bits 4-7 -> .y) to exact bf16.
+template <int SEL>
+__device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t dw) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, 1.0f, SEL);
+}
+// Two E4M3FN codes (bytes 0,1 or 2,3 of dw) to exact bf16.
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3x2_bf16(uint32_t dw) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(dw, 1.0f, HI);
+}
+// One E4M3FN code (byte SEL of dw) to FP32 (exact).
+template <int SEL>
+__device__ __forceinline__ float e4m3_f32(uint32_t dw) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)dw, SEL);
+}
+// acc + w.x*x.x + w.y*x.y, products exact in FP32.
+__device__ __forceinline__ float dot2(bf16x2 w, uint32_t x2, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(w, as_bf16x2(x2), acc, false);
+}
+
+// FP32 -> bf16 bit pattern, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---- host-side validation helpers -----------------------------------------------
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+inline bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+uint64_t packed_bytes_of(uint32_t format, int64_t d_out, int64_t d_in);
+
+// Checks a weight descriptor: pointer, tag, shape, alignment, size, scale.
+fp4g_status check_weight(const fp4g_weight* w, bool want_fp4);
+
+// Workspace bytes of moe_route_gemv (0 for invalid arguments).
+uint64_t moe_ws_bytes(const fp4g_moe* mo, int M);
+
+}  // namespace fp4g

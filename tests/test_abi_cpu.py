@@ -1,0 +1,209 @@
+"""The C ABI library loads without a GPU, exports every declared symbol, and
+refuses every bad argument before any HIP call.  CPU only: no call here reaches a
+kernel launch (each one fails validation first)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import bit_weight_gemv_fp4_amd as fg
+from oracle import layout
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "fp4gemv.h"
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_FORMAT, E_WORKSPACE, E_PATH, E_ALIAS, E_HIP = range(9)
+FAKE = 0x7F0000000000  # a 256-B aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 12, names
+    L = fg.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert fg.abi_version() == 1
+    for s in range(9):
+        assert fg.status_string(s) and fg.status_string(s) != "unknown status"
+    assert fg.status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4, fg.FP8_ROW])
+@pytest.mark.parametrize("shape", [(1, 32), (64, 256), (70, 288), (5120, 5120), (17408, 5120), (248320, 5120)])
+def test_packed_bytes_match_layout_reference(fmt, shape):
+    assert fg.packed_bytes(fmt, *shape) == layout.packed_bytes(fmt, *shape)
+
+
+def test_packed_bytes_bad_shapes_are_zero():
+    for fmt, d_out, d_in in [(1, 0, 32), (1, 5, 16), (1, 5, 48), (4, 5, 64), (0, 5, 64)]:
+        assert fg.packed_bytes(fmt, d_out, d_in) == 0
+
+
+def good_desc(fmt=fg.NVFP4, d_out=128, d_in=512):
+    d = fg.WeightDesc()
+    d.format, d.layout_tag, d.d_out, d.d_in = fmt, fg.LAYOUT_TILE64x256, d_out, d_in
+    d.packed = FAKE
+    d.packed_bytes = fg.packed_bytes(fmt, d_out, d_in)
+    d.tensor_scale = 1.0
+    return d
+
+
+def call_gemv(d, x=FAKE + (1 << 30), y=FAKE + (2 << 30), ws=None, wsb=0):
+    return fg.lib().fp4_gemv(ctypes.byref(d), x, y, ws, wsb, None)
+
+
+def test_gemv_error_paths():
+    L = fg.lib()
+    assert L.fp4_gemv(None, FAKE, FAKE, None, 0, None) == E_NULL
+    d = good_desc()
+    assert call_gemv(d, x=None) == E_NULL
+    assert call_gemv(d, y=None) == E_NULL
+    d2 = good_desc(); d2.packed = None
+    assert call_gemv(d2) == E_NULL
+    d2 = good_desc(); d2.layout_tag = 0
+    assert call_gemv(d2) == E_FORMAT
+    d2 = good_desc(fmt=fg.FP8_ROW)
+    assert call_gemv(d2) == E_FORMAT          # FP8 rows are not an fp4_gemv format
+    d2 = good_desc(); d2.d_in = 48
+    assert call_gemv(d2) == E_SHAPE
+    d2 = good_desc(); d2.d_out = 0
+    assert call_gemv(d2) == E_SHAPE
+    d2 = good_desc(); d2.packed_bytes -= 1
+    assert call_gemv(d2) == E_SHAPE
+    d2 = good_desc(); d2.packed = FAKE + 16
+    assert call_gemv(d2) == E_ALIGN
+    assert call_gemv(d, x=FAKE + (1 << 30) + 2) == E_ALIGN
+    d2 = good_desc(); d2.tensor_scale = float("nan")
+    assert call_gemv(d2) == E_FORMAT
+    d2 = good_desc(fmt=fg.MXFP4); d2.tensor_scale = 2.0
+    assert call_gemv(d2) == E_FORMAT
+    # output overlapping the weights
+    assert call_gemv(d, y=FAKE + 256) == E_ALIAS
+    # a shape that needs split-K workspace
+    big = good_desc(d_out=5120, d_in=5120)
+    need = fg.workspace_bytes(fg.OP_GEMV, big, 1)
+    assert need > 0
+    assert call_gemv(big, ws=None, wsb=0) == E_NULL
+    assert call_gemv(big, ws=FAKE + (3 << 30), wsb=need - 1) == E_WORKSPACE
+    assert call_gemv(big, ws=FAKE + (3 << 30) + 16, wsb=need) == E_ALIGN
+
+
+def test_skinny_and_lmhead_error_paths():
+    L = fg.lib()
+    d = good_desc()
+    X, Y = FAKE + (1 << 30), FAKE + (2 << 30)
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 0, Y, 0, None, 0, None) == E_SHAPE
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 9, Y, 0, None, 0, None) == E_SHAPE
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, fg.PATH_MFMA, None, 0, None) == E_PATH
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, 7, None, 0, None) == E_PATH
+    assert L.fp8_lmhead_gemv(ctypes.byref(d), X, 1, Y, None, 0, None) == E_FORMAT  # NVFP4 given
+    f8 = good_desc(fmt=fg.FP8_ROW)
+    assert L.fp8_lmhead_gemv(ctypes.byref(f8), X, 9, Y, None, 0, None) == E_SHAPE
+    assert L.fp8_lmhead_gemv(ctypes.byref(f8), None, 1, Y, None, 0, None) == E_NULL
+
+
+def test_gate_up_error_paths():
+    L = fg.lib()
+    g, u = good_desc(), good_desc()
+    X, H = FAKE + (1 << 30), FAKE + (2 << 30)
+    u2 = good_desc(d_out=256)
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u2), X, 1, H, 0, None, 0, None) == E_SHAPE
+    u3 = good_desc(fmt=fg.MXFP4)
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u3), X, 1, H, 0, None, 0, None) == E_FORMAT
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, fg.PATH_MFMA, None, 0, None) == E_PATH
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, None, 0, None, 0, None) == E_NULL
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, X, 0, None, 0, None) == E_ALIAS
+
+
+def moe_desc(E=16, k=4, hidden=256, dff=128, shared=True):
+    m = fg.MoeDesc()
+    m.num_experts, m.top_k, m.hidden, m.d_ff = E, k, hidden, dff
+    pg = fg.packed_bytes(fg.MXFP4, dff, hidden)
+    pd = fg.packed_bytes(fg.MXFP4, hidden, dff)
+    for name, (o, i, base, p) in {"gate": (dff, hidden, 0, pg), "up": (dff, hidden, 1, pg),
+                                  "down": (hidden, dff, 2, pd)}.items():
+        d = good_desc(fg.MXFP4, o, i)
+        d.packed = FAKE + (base << 32)
+        d.packed_bytes = p * E
+        setattr(m, name, d)
+    m.stride_gate = m.stride_up = pg
+    m.stride_down = pd
+    if shared:
+        m.has_shared = 1
+        m.sh_gate = good_desc(fg.MXFP4, dff, hidden); m.sh_gate.packed = FAKE + (3 << 32)
+        m.sh_up = good_desc(fg.MXFP4, dff, hidden); m.sh_up.packed = FAKE + (4 << 32)
+        m.sh_down = good_desc(fg.MXFP4, hidden, dff); m.sh_down.packed = FAKE + (5 << 32)
+    return m
+
+
+def call_moe(m, M=1, ws=FAKE + (9 << 32), wsb=None, **kw):
+    if wsb is None:
+        wsb = fg.workspace_bytes(fg.OP_MOE, m, M)
+    a = dict(X=FAKE + (6 << 32), logits=FAKE + (7 << 32), Y=FAKE + (8 << 32), ids=FAKE + (10 << 32),
+             w=FAKE + (11 << 32), H=None)
+    a.update(kw)
+    return fg.lib().moe_route_gemv(ctypes.byref(m), a["X"], a["logits"], M, a["Y"], a["ids"], a["w"], a["H"], ws,
+                                   wsb, None)
+
+
+def test_moe_error_paths():
+    m = moe_desc()
+    assert fg.workspace_bytes(fg.OP_MOE, m, 1) > 0
+    assert fg.workspace_bytes(fg.OP_MOE, m, 9) == 0
+    assert call_moe(m, M=0) == E_SHAPE
+    assert call_moe(m, M=9) == E_SHAPE
+    m2 = moe_desc(); m2.top_k = 9
+    assert call_moe(m2, wsb=1 << 30) == E_SHAPE
+    m2 = moe_desc(); m2.top_k = 17; m2.num_experts = 16
+    assert call_moe(m2, wsb=1 << 30) == E_SHAPE
+    m2 = moe_desc(); m2.down.d_out = 128
+    assert call_moe(m2, wsb=1 << 30) == E_SHAPE
+    m2 = moe_desc(); m2.up.format = fg.NVFP4
+    assert call_moe(m2, wsb=1 << 30) == E_FORMAT
+    m2 = moe_desc(); m2.gate.packed_bytes -= 1
+    assert call_moe(m2, wsb=1 << 30) == E_SHAPE
+    m2 = moe_desc(); m2.stride_up += 16
+    assert call_moe(m2, wsb=1 << 30) in (E_ALIGN, E_SHAPE)
+    assert call_moe(m, ws=None) == E_NULL
+    assert call_moe(m, wsb=fg.workspace_bytes(fg.OP_MOE, m, 1) - 1) == E_WORKSPACE
+    assert call_moe(m, Y=FAKE + (6 << 32)) == E_ALIAS          # output on top of X
+    assert call_moe(m, ids=FAKE + (8 << 32)) == E_ALIAS        # two outputs overlap
+    assert call_moe(m, logits=FAKE + (7 << 32) + 4) == E_ALIGN
+
+
+def test_pack_error_paths():
+    L = fg.lib()
+    out = fg.WeightDesc()
+    C, S, P = FAKE, FAKE + (1 << 30), FAKE + (2 << 30)
+    nb = fg.packed_bytes(fg.NVFP4, 64, 256)
+    assert L.fp4g_pack(fg.NVFP4, 64, 256, None, S, 1.0, P, nb, ctypes.byref(out), None) == E_NULL
+    assert L.fp4g_pack(9, 64, 256, C, S, 1.0, P, nb, ctypes.byref(out), None) == E_FORMAT
+    assert L.fp4g_pack(fg.NVFP4, 64, 250, C, S, 1.0, P, nb, ctypes.byref(out), None) == E_SHAPE
+    assert L.fp4g_pack(fg.NVFP4, 64, 256, C, S, 1.0, P, nb - 1, ctypes.byref(out), None) == E_SHAPE
+    assert L.fp4g_pack(fg.NVFP4, 64, 256, C, S, 1.0, P + 16, nb, ctypes.byref(out), None) == E_ALIGN
+    assert L.fp4g_pack(fg.NVFP4, 64, 256, C, S, float("inf"), P, nb, ctypes.byref(out), None) == E_FORMAT
+    nb8 = fg.packed_bytes(fg.FP8_ROW, 64, 256)
+    assert L.fp4g_pack(fg.FP8_ROW, 64, 256, C, S, 2.0, P, nb8, ctypes.byref(out), None) == E_FORMAT
+    assert L.fp4g_pack(fg.NVFP4, 64, 256, C, S, 1.0, C + 256, nb, ctypes.byref(out), None) == E_ALIAS
+    d = good_desc(); d.layout_tag = 3
+    assert L.fp4g_unpack(ctypes.byref(d), C, S, None) == E_FORMAT
+    assert L.fp4g_validate(ctypes.byref(d), FAKE, None) == E_FORMAT
+    assert L.fp4g_validate(ctypes.byref(good_desc()), None, None) == E_NULL
+
+
+def test_workspace_queries():
+    assert fg.workspace_bytes(fg.OP_GEMV, good_desc(d_out=64, d_in=256), 1) == 0  # one row group, one chunk
+    assert fg.workspace_bytes(99, good_desc(), 1) == 0
+    assert fg.workspace_bytes(fg.OP_GEMV, good_desc(), 0) == 0
+    bad = good_desc(); bad.layout_tag = 0
+    assert fg.workspace_bytes(fg.OP_GEMV, bad, 1) == 0

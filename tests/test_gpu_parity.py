@@ -1,0 +1,401 @@
+"""GPU parity of every C-ABI entry point against the FP64 oracle.  Needs gfx950.
+
+Bars (derived in the design doc):
+  * packing / unpacking and top-k ids: bit-exact;
+  * products: |y_gpu - y_ref| <= 2e-3 * sum_k |w x| per row;
+  * fused h = bf16(SiLU(g) u): |h - h_ref| <= 1.1 tg (|u| + tu) + |SiLU(g)| tu + 2^-8 |h_ref|,
+    with tg, tu the product bounds of g and u;
+  * MoE gate weights: relative 1e-5; MoE output given the GPU's own h and gate
+    weights: 2e-3 * (sum_j g_j A_down,j + A_down,shared).
+Inputs are seeded synthetic tensors from datagen, drawn on the GPU and copied to
+the host for the oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_gemv_fp4_amd as fg
+import datagen
+import oracle
+from oracle import layout
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_and_native_library():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    assert fg.LIB_PATH.exists(), "the HIP library must be built"
+    fg.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bits(x_bf16: torch.Tensor) -> np.ndarray:
+    return x_bf16.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def make(fmt, d_out, d_in, seed):
+    mat = datagen.matrix(fmt, d_out, d_in, datagen.tensor_seed("gpu", fmt, d_out, d_in, seed), device=DEV)
+    W = fg.pack(fmt, mat["codes"], mat["scales"], mat["tensor_scale"])
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in mat.items()}
+    return W, host
+
+
+def sample_rows(d_out, n=192, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, 63, 64, d_out - 1, d_out // 2}
+    rows = sorted(fixed | set(rng.integers(0, d_out, n).tolist()))
+    return np.array([r for r in rows if 0 <= r < d_out], dtype=np.int64)
+
+
+def check_product(y_gpu, host, X_bits, rows=None, tol=TOL):
+    Y, A = oracle.gemv(host["format"], host["codes"], host["scales"], host["tensor_scale"], X_bits, rows=rows)
+    y = y_gpu.detach().cpu().double().numpy().reshape(Y.shape[0], -1)
+    if rows is not None:
+        y = y[:, rows]
+    err = np.abs(y - Y)
+    bound = tol * A
+    bad = err > bound
+    assert not bad.any(), f"{bad.sum()} outputs out of bound; worst ratio {np.max(err / np.maximum(bound, 1e-300)):.3g}"
+    return float(np.max(err / np.maximum(A, 1e-300)))
+
+
+# ---- packing -------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4, fg.FP8_ROW])
+@pytest.mark.parametrize("shape", [(1, 32), (64, 256), (70, 288), (130, 544), (5120, 5120)])
+def test_pack_is_bit_exact_and_invertible(fmt, shape):
+    log("pack", fmt, shape)
+    W, host = make(fmt, *shape, seed=1)
+    img = W.buf.cpu().numpy()
+    ref = layout.pack(fmt, host["codes"].numpy(), host["scales"].numpy())
+    assert img.size == ref.size and np.array_equal(img, ref)
+    codes, scales = fg.unpack(W)
+    assert torch.equal(codes.cpu(), host["codes"])
+    assert torch.equal(scales.cpu().view(torch.uint8), host["scales"].contiguous().view(torch.uint8))
+    assert fg.validate(W) == 0
+
+
+def test_validate_counts_nan_codes():
+    log("validate")
+    mat = datagen.matrix(fg.NVFP4, 70, 288, 5, device=DEV)
+    sc = mat["scales"].clone()
+    sc[3, 2] = 0x7F
+    sc[69, 17] = 0xFF
+    W = fg.pack(fg.NVFP4, mat["codes"], sc)
+    assert fg.validate(W) == 2
+    mx = datagen.matrix(fg.MXFP4, 64, 256, 6, device=DEV)
+    s2 = mx["scales"].clone()
+    s2[0, 0] = 0xFF
+    assert fg.validate(fg.pack(fg.MXFP4, mx["codes"], s2)) == 1
+    f8 = datagen.matrix(fg.FP8_ROW, 64, 256, 7, device=DEV)
+    c3 = f8["codes"].clone()
+    c3[5, 5] = 0x7F
+    s3 = f8["scales"].clone()
+    s3[9] = float("inf")
+    assert fg.validate(fg.pack(fg.FP8_ROW, c3, s3)) == 2
+
+
+# ---- single vector products ---------------------------------------------------------------
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+@pytest.mark.parametrize("shape", [(1, 32), (64, 256), (70, 288), (200, 1056), (777, 4128), (5120, 5120)])
+def test_gemv_matches_oracle(fmt, shape):
+    log("gemv", fmt, shape)
+    W, host = make(fmt, *shape, seed=2)
+    x = datagen.bf16_normal((shape[1],), datagen.tensor_seed("x", shape), device=DEV)
+    y = fg.fp4_gemv(W, x)
+    check_product(y, host, bits(x)[None, :])
+
+
+def test_gemv_tensor_scale():
+    log("tensor scale")
+    mat = datagen.matrix(fg.NVFP4, 130, 544, 8, device=DEV)
+    x = datagen.bf16_normal((544,), 3, device=DEV)
+    for ts in (0.5, 3.75, 1e-3):
+        W = fg.pack(fg.NVFP4, mat["codes"], mat["scales"], ts)
+        host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in mat.items()}
+        host["tensor_scale"] = ts
+        check_product(fg.fp4_gemv(W, x), host, bits(x)[None, :])
+
+
+@pytest.mark.parametrize("M", [2, 3, 4, 8])
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_skinny_matches_oracle(fmt, M):
+    log("skinny", fmt, M)
+    for shape in ((200, 1056), (5120, 5120)):
+        W, host = make(fmt, *shape, seed=3)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("X", M, shape), device=DEV)
+        Y = fg.fp4_skinny_gemm(W, X)
+        check_product(Y, host, bits(X))
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_lmhead_matches_oracle(M):
+    log("lmhead", M)
+    for shape in ((300, 544), (1, 32), (2048, 2560)):
+        W, host = make(fg.FP8_ROW, *shape, seed=4)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("Xh", M, shape), device=DEV)
+        check_product(fg.fp8_lmhead_gemv(W, X), host, bits(X))
+
+
+def h_bound(r, h_ref):
+    tg, tu = TOL * r["Ag"], TOL * r["Au"]
+    silu_g = r["g"] / (1.0 + np.exp(-r["g"]))
+    return 1.1 * tg * (np.abs(r["u"]) + tu) + np.abs(silu_g) * tu + 2.0 ** -8 * np.abs(h_ref)
+
+
+def check_h(H_gpu, gate, up, X_bits, rows=None):
+    r = oracle.gate_up_silu(gate, up, X_bits, rows=rows)
+    h = H_gpu.detach().float().cpu().double().numpy().reshape(r["h"].shape[0], -1)
+    if rows is not None:
+        h = h[:, rows]
+    err = np.abs(h - r["h"])
+    bad = err > h_bound(r, r["h"])
+    assert not bad.any(), f"{bad.sum()} h values out of bound"
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_gate_up_silu_matches_oracle(fmt, M):
+    log("gate_up", fmt, M)
+    for shape in ((200, 1056), (130, 544)):
+        Wg, hg = make(fmt, *shape, seed=5)
+        Wu, hu = make(fmt, *shape, seed=6)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("Xg", M, shape), device=DEV)
+        H = fg.fp4_gate_up_silu(Wg, Wu, X)
+        check_h(H, hg, hu, bits(X))
+
+
+# ---- special cases: bit-exact ------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4, fg.FP8_ROW])
+def test_one_hot_gives_exact_column(fmt):
+    log("one-hot", fmt)
+    d_out, d_in = 130, 544
+    W, host = make(fmt, d_out, d_in, seed=9)
+    Wd = oracle.dequant(fmt, host["codes"], host["scales"], host["tensor_scale"])
+    for k in (0, 1, 31, 256, 543):
+        x = torch.zeros(d_in, dtype=torch.bfloat16, device=DEV)
+        x[k] = 1.0
+        y = fg.fp8_lmhead_gemv(W, x) if fmt == fg.FP8_ROW else fg.fp4_gemv(W, x)
+        # one exact product per output, rounded once to FP32 (FP8: code x row scale
+        # can exceed 24 significant bits; FP4 products are exact in FP32)
+        assert np.array_equal(y.cpu().double().numpy(), Wd[:, k].astype(np.float32).astype(np.float64)), k
+
+
+def test_exact_sums_are_bit_exact():
+    # scales all 1.0 (E4M3 0x38) and x in {-1, 0, 1}: every partial sum is a multiple
+    # of 0.5 far below 2^24, so any summation order is exact
+    log("exact sums")
+    d_out, d_in = 640, 5120
+    mat = datagen.matrix(fg.NVFP4, d_out, d_in, 10, device=DEV)
+    sc = torch.full_like(mat["scales"], 0x38)
+    W = fg.pack(fg.NVFP4, mat["codes"], sc)
+    x = (torch.randint(-1, 2, (d_in,), generator=torch.Generator(DEV).manual_seed(4), device=DEV)).to(torch.bfloat16)
+    Y, _ = oracle.gemv(fg.NVFP4, mat["codes"].cpu(), sc.cpu(), 1.0, bits(x)[None, :])
+    assert np.array_equal(fg.fp4_gemv(W, x).cpu().double().numpy(), Y[0])
+
+
+def test_sign_flip_and_determinism():
+    log("sign flip")
+    mat = datagen.matrix(fg.NVFP4, 5120, 5120, 11, device=DEV)
+    x = datagen.bf16_normal((5120,), 12, device=DEV)
+    W = fg.pack(fg.NVFP4, mat["codes"], mat["scales"])
+    Wn = fg.pack(fg.NVFP4, mat["codes"] ^ 0x88, mat["scales"])
+    y1 = fg.fp4_gemv(W, x).clone()
+    y2 = fg.fp4_gemv(W, x).clone()
+    yn = fg.fp4_gemv(Wn, x).clone()
+    assert torch.equal(y1, y2)
+    assert torch.equal(yn, -y1)
+    assert torch.equal(fg.fp4_gemv(W, -x), -y1)
+
+
+# ---- the workloads at full size (sampled rows where the oracle would be slow) -----------
+
+
+def test_config1_gemv_5120():
+    log("C1")
+    W, host = make(fg.NVFP4, 5120, 5120, seed=100)
+    x = datagen.bf16_normal((5120,), 101, device=DEV)
+    check_product(fg.fp4_gemv(W, x), host, bits(x)[None, :])
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_config2_and_4_mlp(M):
+    """Dense MLP: gate/up 17408x5120 fused with SiLU*mul, then down 5120x17408."""
+    log("C2/C4 MLP", M)
+    Wg, hg = make(fg.NVFP4, 17408, 5120, seed=200)
+    Wu, hu = make(fg.NVFP4, 17408, 5120, seed=201)
+    Wd, hd = make(fg.NVFP4, 5120, 17408, seed=202)
+    X = datagen.bf16_normal((M, 5120), datagen.tensor_seed("C2x", M), device=DEV)
+    H = fg.fp4_gate_up_silu(Wg, Wu, X)
+    Y = fg.fp4_skinny_gemm(Wd, H) if M > 1 else fg.fp4_gemv(Wd, H.view(-1)).view(1, -1)
+    rows = sample_rows(17408, 160, seed=M)
+    check_h(H, hg, hu, bits(X), rows=rows)
+    drows = sample_rows(5120, 160, seed=M + 10)
+    check_product(Y, hd, bits(H), rows=drows)  # down, given the GPU's own h
+
+
+@pytest.mark.parametrize("shape", [(12288, 5120), (5120, 12288), (7680, 5120)])
+def test_config3_attention_shapes(shape):
+    log("C3 attn", shape)
+    W, host = make(fg.NVFP4, *shape, seed=300)
+    x = datagen.bf16_normal((shape[1],), 301, device=DEV)
+    check_product(fg.fp4_gemv(W, x), host, bits(x)[None, :], rows=sample_rows(shape[0]))
+
+
+def test_config3_lm_head():
+    log("C3 head")
+    W, host = make(fg.FP8_ROW, 248320, 5120, seed=310)
+    x = datagen.bf16_normal((1, 5120), 311, device=DEV)
+    check_product(fg.fp8_lmhead_gemv(W, x), host, bits(x), rows=sample_rows(248320, 400))
+
+
+# ---- MoE --------------------------------------------------------------------------------------
+
+
+def build_moe(fmt, E, k, hidden, dff, seed, shared=True):
+    pg = fg.packed_bytes(fmt, dff, hidden)
+    pd = fg.packed_bytes(fmt, hidden, dff)
+    bufs = {n: torch.empty(E * (pd if n == "down" else pg), dtype=torch.uint8, device=DEV) for n in ("gate", "up", "down")}
+    logical = {}
+    descs = {}
+    for n, (o, i) in (("gate", (dff, hidden)), ("up", (dff, hidden)), ("down", (hidden, dff))):
+        mats = datagen.matrix(fmt, o, i, datagen.tensor_seed("moe", seed, n), device=DEV, batch=E)
+        stride = pd if n == "down" else pg
+        first = None
+        for e in range(E):
+            w = fg.pack(fmt, mats["codes"][e], mats["scales"][e], 1.0, out=bufs[n], offset=e * stride)
+            if first is None:
+                first = w
+        first.desc.packed_bytes = bufs[n].numel()
+        descs[n] = first
+        logical[n] = mats
+    sh = None
+    sh_host = None
+    if shared:
+        sh, sh_host = [], {}
+        for n, (o, i) in (("gate", (dff, hidden)), ("up", (dff, hidden)), ("down", (hidden, dff))):
+            W, host = make(fmt, o, i, seed=("shared", seed, n))
+            sh.append(W)
+            sh_host[n] = host
+    layer = fg.moe_layer(descs["gate"], descs["up"], descs["down"], E, k, pg, pg, pd, shared=sh)
+    layer.keep.append(bufs)
+
+    def expert(e):
+        return {n: {"format": fmt, "codes": logical[n]["codes"][e].cpu(), "scales": logical[n]["scales"][e].cpu(),
+                    "tensor_scale": 1.0} for n in ("gate", "up", "down")}
+
+    return layer, expert, sh_host
+
+
+def check_moe(layer, expert, sh_host, X, logits, k, has_shared=True):
+    M = X.shape[0]
+    dff = layer.desc.d_ff
+    nh = k + (1 if has_shared else 0)
+    H = torch.empty((M, nh, dff), dtype=torch.bfloat16, device=DEV)
+    Y, ids, w = fg.moe_route_gemv(layer, X, logits, H=H)
+    torch.cuda.synchronize()
+    rid, rw = oracle.topk_softmax(logits.cpu().numpy(), k)
+    assert np.array_equal(ids.cpu().numpy(), rid), "top-k ids differ"
+    wg = w.cpu().double().numpy()
+    assert np.all(np.abs(wg - rw) <= 1e-5 * rw), "gate weights"
+    Xb = bits(X)
+    Hb = bits(H.view(M * nh, dff)).reshape(M, nh, dff)
+    # stage 1: every (token, expert) intermediate
+    for m in range(M):
+        for j in range(nh):
+            ex = expert(int(rid[m, j])) if j < k else sh_host
+            r = oracle.gate_up_silu(ex["gate"], ex["up"], Xb[m][None, :])
+            h = H[m, j].float().cpu().double().numpy()[None, :]
+            assert np.all(np.abs(h - r["h"]) <= h_bound(r, r["h"])), (m, j)
+    # stage 2: combine given the GPU's own h and gate weights
+    yg = Y.cpu().double().numpy()
+    e2e = 0.0
+    for m in range(M):
+        ref = np.zeros(layer.desc.hidden)
+        tol = np.zeros(layer.desc.hidden)
+        for j in range(nh):
+            ex = expert(int(rid[m, j])) if j < k else sh_host
+            d, Ad = oracle.gemv(ex["down"]["format"], ex["down"]["codes"], ex["down"]["scales"], 1.0,
+                                Hb[m, j][None, :])
+            c = wg[m, j] if j < k else 1.0
+            ref += c * d[0]
+            tol += c * Ad[0]
+        assert np.all(np.abs(yg[m] - ref) <= TOL * tol), m
+    # end to end against the pure FP64 oracle (reported)
+    full = oracle.moe(expert, sh_host if has_shared else None, Xb, logits.cpu().numpy(), k)
+    e2e = float(np.max(np.abs(yg - full["y"]) / np.maximum(full["tol"], 1e-300)))
+    log(f"moe end-to-end max |y - y_oracle| / sum(g A_down) = {e2e:.3g}")
+    assert e2e < 0.05
+    return ids
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+def test_moe_small(M):
+    log("moe small", M)
+    layer, expert, sh = build_moe(fg.MXFP4, 16, 4, 256, 128, seed=1)
+    X = datagen.bf16_normal((M, 256), datagen.tensor_seed("mx", M), device=DEV)
+    logits = datagen.router_logits(M, 16, datagen.tensor_seed("ml", M), device=DEV)
+    check_moe(layer, expert, sh, X, logits, 4)
+
+
+def test_moe_ties_and_repeat():
+    log("moe ties")
+    layer, expert, sh = build_moe(fg.MXFP4, 16, 4, 256, 128, seed=2)
+    X = datagen.bf16_normal((3, 256), 1, device=DEV)
+    logits = torch.zeros((3, 16), dtype=torch.float32, device=DEV)
+    logits[1, 5] = 1.0
+    logits[2] = torch.tensor([0.5, -1, 0.5, 0.25] * 4, device=DEV)
+    ids = check_moe(layer, expert, sh, X, logits, 4)
+    assert ids[0].tolist() == [0, 1, 2, 3]
+    Y1, _, _ = fg.moe_route_gemv(layer, X, logits)
+    Y2, _, _ = fg.moe_route_gemv(layer, X, logits)
+    assert torch.equal(Y1, Y2)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_config5_moe_layer(M):
+    """Ling-3.0-flash-shaped MoE layer: 512 MXFP4 experts 768x2560 / 2560x768, top-8 + shared."""
+    log("C5 moe", M)
+    layer, expert, sh = build_moe(fg.MXFP4, 512, 8, 2560, 768, seed=5)
+    X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("C5x", M), device=DEV)
+    logits = datagen.router_logits(M, 512, datagen.tensor_seed("C5l", M), device=DEV)
+    check_moe(layer, expert, sh, X, logits, 8)
+
+
+def test_config5_lm_head():
+    log("C5 head")
+    W, host = make(fg.FP8_ROW, 157184, 2560, seed=500)
+    X = datagen.bf16_normal((4, 2560), 501, device=DEV)
+    check_product(fg.fp8_lmhead_gemv(W, X), host, bits(X), rows=sample_rows(157184, 300))
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace shared by calls of different shapes (split-K counters must
+    start at zero for each)."""
+    log("workspace reuse")
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    for shape in ((777, 4128), (5120, 5120), (200, 1056), (5120, 17408), (777, 4128)):
+        W, host = make(fg.NVFP4, *shape, seed=20)
+        x = datagen.bf16_normal((shape[1],), 21, device=DEV)
+        y = fg.fp4_gemv(W, x, ws=ws)
+        check_product(y, host, bits(x)[None, :], rows=sample_rows(shape[0], 64))
+        X = datagen.bf16_normal((3, shape[1]), 22, device=DEV)
+        Y = fg.fp4_skinny_gemm(W, X, ws=ws)
+        check_product(Y, host, bits(X), rows=sample_rows(shape[0], 64))
