@@ -85,6 +85,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// ---- split-K hand-off between workgroups ---------------------------------------
+// Partial sums are published with device-scope stores (written through to the
+// point where all XCDs see them) and read back with device-scope loads, so no
+// full-L2 write-back or invalidate is needed.  The s_waitcnt makes this wave's
+// partial stores complete before the arrival counter is incremented; the loads
+// of the last arriver are issued after its atomic returned.
+__device__ __forceinline__ void publish_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect_partial(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Called by one whole wave after it published its partials; true in the wave of
+// the workgroup that arrives last (`expected_prev` earlier arrivals).
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected_prev) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  unsigned prev = 0;
+  if ((threadIdx.x & 63) == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);
+  return prev == expected_prev;
+}
+// The last arriver leaves the counter at zero for the next call.
+__device__ __forceinline__ void reset_counter(unsigned* counter) {
+  if ((threadIdx.x & 63) == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }

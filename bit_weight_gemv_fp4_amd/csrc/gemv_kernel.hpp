@@ -266,21 +266,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
   // split-K hand-off: publish partials, count arrivals, the last one finishes
   const int64_t rpad = (int64_t)p.R * 64;
 #pragma unroll
-  for (int i = 0; i < NA; ++i) p.part[((int64_t)s * NA + i) * rpad + row] = v[i];
-  __threadfence();
-  unsigned prev = 0;
-  if (lane == 0) prev = atomicAdd(p.counters + g, 1u);
-  prev = __shfl(prev, 0, 64);
-  if (prev != (unsigned)(p.S - 1)) return;
-  __threadfence();
+  for (int i = 0; i < NA; ++i) publish_partial(p.part + ((int64_t)s * NA + i) * rpad + row, v[i]);
+  if (!arrive_last(p.counters + g, (unsigned)(p.S - 1))) return;
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
     float t = 0.0f;
-    for (int q = 0; q < p.S; ++q) t += __builtin_nontemporal_load(p.part + ((int64_t)q * NA + i) * rpad + row);
+    for (int q = 0; q < p.S; ++q) t += collect_partial(p.part + ((int64_t)q * NA + i) * rpad + row);
     v[i] = t;
   }
   finish_row<FMT, M, NMAT, EPI>(p, row, v);
-  if (lane == 0) p.counters[g] = 0u;
+  reset_counter(p.counters + g);
 }
 
 template <uint32_t FMT, int NMAT, int EPI>

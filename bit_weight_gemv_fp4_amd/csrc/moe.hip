@@ -236,22 +236,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_up(MoeParams p) {
     const int64_t rpad = (int64_t)p.Rg * 64;
     float* base = p.part_up + ((int64_t)s * p.n_slots_max + slot) * NA * rpad;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) base[i * rpad + row] = v[i];
-    __threadfence();
-    unsigned prev = 0;
+    for (int i = 0; i < NA; ++i) publish_partial(base + i * rpad + row, v[i]);
     unsigned* cnt = p.cnt_up + slot * p.Rg + g;
-    if (lane == 0) prev = atomicAdd(cnt, 1u);
-    prev = __shfl(prev, 0, 64);
-    if (prev != (unsigned)(p.S_up - 1)) return;
-    __threadfence();
+    if (!arrive_last(cnt, (unsigned)(p.S_up - 1))) return;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
       float t = 0.0f;
       for (int q = 0; q < p.S_up; ++q)
-        t += __builtin_nontemporal_load(p.part_up + (((int64_t)q * p.n_slots_max + slot) * NA + i) * rpad + row);
+        t += collect_partial(p.part_up + (((int64_t)q * p.n_slots_max + slot) * NA + i) * rpad + row);
       v[i] = t;
     }
-    if (lane == 0) *cnt = 0u;
+    reset_counter(cnt);
   }
   if (row >= p.dff) return;
   const int nh = p.K + p.has_shared;
@@ -315,24 +310,18 @@ __global__ __launch_bounds__(kThreads) void k_moe_down(MoeParams p) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const float v = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
-    base[m * rpad + row] = v * tsd * p.coef[slot * M + m];
+    publish_partial(base + m * rpad + row, v * tsd * p.coef[slot * M + m]);
   }
-  __threadfence();
-  unsigned prev = 0;
-  if (lane == 0) prev = atomicAdd(p.cnt_dn + g, 1u);
-  prev = __shfl(prev, 0, 64);
-  if (prev != (unsigned)(n_slots * p.S_dn - 1)) return;
-  __threadfence();
+  if (!arrive_last(p.cnt_dn + g, (unsigned)(n_slots * p.S_dn - 1))) return;
   if (row < p.hidden) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float t = 0.0f;
-      for (int q = 0; q < n_slots * p.S_dn; ++q)
-        t += __builtin_nontemporal_load(p.part_dn + ((int64_t)q * M + m) * rpad + row);
+      for (int q = 0; q < n_slots * p.S_dn; ++q) t += collect_partial(p.part_dn + ((int64_t)q * M + m) * rpad + row);
       p.y[(int64_t)m * p.hidden + row] = t;
     }
   }
-  if (lane == 0) p.cnt_dn[g] = 0u;
+  reset_counter(p.cnt_dn + g);
 }
 
 // ---- host side ------------------------------------------------------------------
