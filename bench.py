@@ -31,12 +31,30 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBPS = 8000.0
 
 
+def counter_traffic(kind):
+    """HBM bytes per launch of `kind` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (profiles/counters.json), or None when the kernel sources
+    have changed since the counters were taken."""
+    import hashlib
+
+    p = ROOT / "profiles" / "counters.json"
+    if not p.exists():
+        return None
+    d = json.loads(p.read_text())
+    src = sorted((ROOT / "bit_weight_gemv_fp4_amd" / "csrc").glob("*"))
+    h = hashlib.sha256(b"".join(q.read_bytes() for q in src)).hexdigest()[:16]
+    k = d.get("kernels", {}).get(kind)
+    if d.get("source_sha256_16") != h or not k:
+        return None
+    return round(k["fetch_bytes"] + k["write_bytes"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -302,6 +320,8 @@ def main():
     import datagen
 
     torch.cuda.set_device(0)
+    if args.workload == "copy":
+        return copy_calibration(torch)
     dev = "cuda"
     M = args.M or (4 if args.workload in ("c4",) else 1)
     t_setup = time.perf_counter()
@@ -372,7 +392,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": counter_traffic(dominant),
             "avg_us": round(dom_avg, 3),
             "launches_timed": n_dom,
             "timed_by": dom_how,
@@ -384,6 +404,17 @@ def main():
     if not args.no_cpu_baseline and args.workload == "c3":
         out["cpu_baseline"] = cpu_baseline_dense(fg, datagen, torch, args.cpu_sample_layers, bytes_per_step)
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(torch, nbytes=1 << 30):
+    """A plain device-to-device copy of known size: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters of rocprofv3 into HBM bytes."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"workload": "copy", "bytes_read": nbytes, "bytes_written": nbytes, "launches": 3}), flush=True)
 
 
 def kind_avg_us(step, torch, kind, reps=5):
