@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
+    ap.add_argument("--engine", default="launches", choices=["stream", "launches"],
+                    help="stream: one persistent launch per step (fp4_stream_run); launches: one launch per product")
     return ap.parse_args()
 
 
@@ -95,10 +97,14 @@ class Step:
 
 
 def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
+    """The dense decode chain; returns (step of separate launches, keep, stream ops).
+    In the stream every op waits for the one before it (the order of a decoder
+    layer: projections, gate/up, down, next layer), as the separate launches do."""
     dev = "cuda"
     H, F = datagen.HIDDEN, datagen.FFN
     step = Step()
     keep = []
+    sops = []
     x = datagen.bf16_normal((M, H), datagen.tensor_seed("c3", "x"), device=dev)
     x_attn_in = datagen.bf16_normal((M, 12288), datagen.tensor_seed("c3", "x12288"), device=dev)
     h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
@@ -117,19 +123,49 @@ def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
         keep += [Wg, Wu, Wd] + att
         gu_bytes = 2 * fg.packed_bytes(fg.NVFP4, F, H) + M * H * 2 + M * F * 2
         step.add("gate_up_silu", (lambda Wg=Wg, Wu=Wu: fg.fp4_gate_up_silu(Wg, Wu, x, h)), gu_bytes)
+        # stream ops: per layer its own outputs (each buffer is written once per
+        # run), in the order of a decoder layer: the three projections of x run
+        # together after the previous layer, the 5120x12288 output projection
+        # waits for them, then gate/up + SiLU, then down
+        prev = len(sops) - 1
+        for j in (0, 1, 3, 2):
+            o, i = datagen.ATTN_SHAPES[j]
+            out = torch.empty((M, o), dtype=torch.float32, device=dev)
+            keep.append(out)
+            if j == 2:
+                w_op, w_cnt = len(sops) - 1, 3
+            else:
+                w_op, w_cnt = prev, 1
+            sops.append({"kind": fg.OP_GEMV, "w": att[j], "x": x if i == H else x_attn_in, "out": out,
+                         "wait_op": w_op, "wait_count": w_cnt})
+        hl = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        yl = torch.empty((M, H), dtype=torch.float32, device=dev)
+        keep += [hl, yl]
+        sops.append({"kind": fg.OP_GATE_UP, "w": Wg, "w_up": Wu, "x": x, "out": hl, "wait_op": len(sops) - 1})
+        sops.append({"kind": fg.OP_GEMV, "w": Wd, "x": hl, "out": yl, "wait_op": len(sops) - 1})
         if M == 1:
             step.add("down", (lambda Wd=Wd: fg.fp4_gemv(Wd, h.view(-1), y.view(-1))),
                      algorithmic_gemv_bytes(fg, fg.NVFP4, H, F, M))
         else:
             step.add("down", (lambda Wd=Wd: fg.fp4_skinny_gemm(Wd, h, y)), algorithmic_gemv_bytes(fg, fg.NVFP4, H, F, M))
-        for W, (o, i) in zip(att, datagen.ATTN_SHAPES):
-            xin = x if i == H else x_attn_in
-            out = y if o == H else ya
+        # the projections that read x go out as one grouped launch, the output
+        # projection (reads the 12288-wide attention result) as its own
+        qkv = [j for j, (o, i) in enumerate(datagen.ATTN_SHAPES) if i == H]
+        G = fg.Group([att[j] for j in qkv])
+        ys = [torch.empty((M, datagen.ATTN_SHAPES[j][0]), dtype=torch.float32, device=dev) for j in qkv]
+        keep += [G, ys]
+        step.add("qkv", (lambda G=G, ys=ys: fg.fp4_gemv_grouped(G, x, ys)),
+                 sum(algorithmic_gemv_bytes(fg, fg.NVFP4, *datagen.ATTN_SHAPES[j], M) - M * H * 2 for j in qkv)
+                 + M * H * 2)
+        for j, (o, i) in enumerate(datagen.ATTN_SHAPES):
+            if j in qkv:
+                continue
+            W = att[j]
             if M == 1:
-                fn = (lambda W=W, xin=xin, out=out, o=o: fg.fp4_gemv(W, xin.view(-1), out[:, :o].reshape(-1)))
+                fn = (lambda W=W: fg.fp4_gemv(W, x_attn_in.view(-1), y.view(-1)))
             else:
-                fn = (lambda W=W, xin=xin, out=out: fg.fp4_skinny_gemm(W, xin, out))
-            step.add("attn", fn, algorithmic_gemv_bytes(fg, fg.NVFP4, o, i, M))
+                fn = (lambda W=W: fg.fp4_skinny_gemm(W, x_attn_in, y))
+            step.add("o_proj", fn, algorithmic_gemv_bytes(fg, fg.NVFP4, o, i, M))
     if with_head:
         m = datagen.matrix(fg.FP8_ROW, datagen.VOCAB, H, datagen.tensor_seed("c3", "head"), device=dev)
         Wh = fg.pack(fg.FP8_ROW, m["codes"], m["scales"])
@@ -138,7 +174,10 @@ def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
         keep += [Wh, logits]
         step.add("lm_head", (lambda: fg.fp8_lmhead_gemv(Wh, x, logits)),
                  algorithmic_gemv_bytes(fg, fg.FP8_ROW, datagen.VOCAB, H, M))
-    return step, keep
+        lg2 = torch.empty((M, datagen.VOCAB), dtype=torch.float32, device=dev)
+        keep.append(lg2)
+        sops.append({"kind": fg.OP_LMHEAD, "w": Wh, "x": x, "out": lg2, "wait_op": len(sops) - 1})
+    return step, keep, sops
 
 
 def weights_only_bytes_dense(fg, datagen, layers, with_head=True):
@@ -326,13 +365,22 @@ def main():
     M = args.M or (4 if args.workload in ("c4",) else 1)
     t_setup = time.perf_counter()
     if args.workload == "c3":
-        step, keep = build_dense_stream(fg, datagen, torch, datagen.LAYERS, True, M=M)
-        workload = "full dense weight stream, M=1: 64 x [NVFP4 gate/up 17408x5120 + SiLU*mul, down 5120x17408, " \
-                   "attention 12288x5120, 12288x5120, 5120x12288, 7680x5120] + FP8 LM head 248320x5120"
+        step, keep, sops = build_dense_stream(fg, datagen, torch, datagen.LAYERS, True, M=M)
+        workload = "full dense weight stream, M=1: 64 x [NVFP4 attention 12288x5120, 12288x5120, 5120x12288, " \
+                   "7680x5120, gate/up 17408x5120 + SiLU*mul, down 5120x17408] + FP8 LM head 248320x5120"
         dominant = "gate_up_silu"
+        if args.engine == "stream":
+            st = fg.Stream(sops, M)
+            keep.append(st)
+            sstep = Step()
+            sstep.add("decode_stream", st.run, step.bytes())
+            step_launches = step
+            step = sstep
+            dominant = "decode_stream"
     else:
         step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch)
     bytes_per_step = step.bytes() / step.steps_per_replay
+    engine = args.engine if args.workload == "c3" else "launches"
     # one eager pass allocates the workspace and checks every launch
     step.run()
     torch.cuda.synchronize()
@@ -383,8 +431,8 @@ def main():
         "vs_baseline": None,
         "dtype": "e2m1/e4m3 weights x bf16 -> f32",
         "data": "synthetic (seeded; weights and activations resident in HBM)",
-        "config": {"workload": workload, "M": M, "bytes_per_step": bytes_per_step, "launches_per_step": len(step.calls),
-                   "setup_s": round(setup_s, 1)},
+        "config": {"workload": workload, "M": M, "engine": engine, "bytes_per_step": bytes_per_step,
+                   "launches_per_step": len(step.calls), "setup_s": round(setup_s, 1)},
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
@@ -399,8 +447,14 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
         },
     }
+    if engine == "stream":
+        err = keep[-1].error()
+        out["stream_error_flag"] = err
+        if err:
+            print(json.dumps({"error": "decode stream reported a time-out; results invalid"}), file=sys.stderr)
+            sys.exit(3)
     if args.breakdown:
-        out["breakdown"] = breakdown(step, torch)
+        out["breakdown"] = breakdown(step_launches if engine == "stream" else step, torch)
     if not args.no_cpu_baseline and args.workload == "c3":
         out["cpu_baseline"] = cpu_baseline_dense(fg, datagen, torch, args.cpu_sample_layers, bytes_per_step)
     print(json.dumps(out), flush=True)

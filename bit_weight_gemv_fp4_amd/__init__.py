@@ -16,15 +16,16 @@ import torch
 
 __all__ = [
     "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
-    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "Fp4gError", "PackedWeight", "MoeLayer",
+    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "MAX_GROUP", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
-    "validate", "fp4_gemv", "fp4_skinny_gemm", "fp4_gate_up_silu", "moe_route_gemv",
-    "fp8_lmhead_gemv", "LIB_PATH",
+    "validate", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
+    "fp8_lmhead_gemv", "LIB_PATH", "Stream",
 ]
 
 NVFP4, MXFP4, FP8_ROW = 1, 2, 3
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
-OP_GEMV, OP_GATE_UP, OP_MOE, OP_LMHEAD = 1, 2, 3, 4
+OP_GEMV, OP_GATE_UP, OP_MOE, OP_LMHEAD, OP_GROUPED = 1, 2, 3, 4, 5
+MAX_GROUP = 4
 LAYOUT_TILE64x256 = 0x46344731
 
 LIB_PATH = Path(__file__).resolve().parent / "libfp4gemv.so"
@@ -41,6 +42,10 @@ class WeightDesc(ctypes.Structure):
         ("tensor_scale", ctypes.c_float),
         ("reserved", ctypes.c_uint32),
     ]
+
+
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("reserved", ctypes.c_int32), ("w", WeightDesc * MAX_GROUP)]
 
 
 class MoeDesc(ctypes.Structure):
@@ -63,6 +68,32 @@ class MoeDesc(ctypes.Structure):
     ]
 
 
+class StreamOpDesc(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("wait_op", ctypes.c_int32),
+        ("wait_count", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("w", ctypes.POINTER(WeightDesc)),
+        ("w_up", ctypes.POINTER(WeightDesc)),
+        ("x_dev", ctypes.c_void_p),
+        ("out_dev", ctypes.c_void_p),
+    ]
+
+
+class StreamPlan(ctypes.Structure):
+    _fields_ = [
+        ("magic", ctypes.c_uint32),
+        ("M", ctypes.c_int32),
+        ("n_ops", ctypes.c_int32),
+        ("n_items", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_uint64),
+    ]
+
+
 _VP, _I32, _U32, _U64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float
 _SIGNATURES = {
     "fp4g_abi_version": (_U32, []),
@@ -74,10 +105,15 @@ _SIGNATURES = {
     "fp4g_workspace_bytes": (_U64, [_I32, _VP, _I32]),
     "fp4_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP, _VP, _U64, _VP]),
     "fp4_skinny_gemm": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32, _VP, _U64, _VP]),
+    "fp4_gemv_grouped": (_I32, [ctypes.POINTER(GroupDesc), _VP, _I32, ctypes.POINTER(_VP), _VP, _U64, _VP]),
     "fp4_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32,
                                 _VP, _U64, _VP]),
     "moe_route_gemv": (_I32, [ctypes.POINTER(MoeDesc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _U64, _VP]),
     "fp8_lmhead_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _VP, _U64, _VP]),
+    "fp4g_stream_workspace_bytes": (_U64, [ctypes.POINTER(StreamOpDesc), _I32, _I32]),
+    "fp4g_stream_build": (_I32, [ctypes.POINTER(StreamOpDesc), _I32, _I32, _VP, _U64, ctypes.POINTER(StreamPlan), _VP]),
+    "fp4_stream_run": (_I32, [ctypes.POINTER(StreamPlan), _VP]),
+    "fp4g_stream_error": (_I32, [ctypes.POINTER(StreamPlan), ctypes.POINTER(ctypes.c_int32), _VP]),
 }
 
 _lib = None
@@ -213,7 +249,7 @@ def validate(W: PackedWeight, stream=None) -> int:
 
 
 def workspace_bytes(op: int, desc, M: int) -> int:
-    d = desc.desc if isinstance(desc, (PackedWeight, MoeLayer)) else desc
+    d = desc.desc if isinstance(desc, (PackedWeight, MoeLayer, Group)) else desc
     return lib().fp4g_workspace_bytes(op, ctypes.addressof(d), M)
 
 
@@ -262,6 +298,34 @@ def fp4_skinny_gemm(W: PackedWeight, X: torch.Tensor, Y: torch.Tensor | None = N
     _check(lib().fp4_skinny_gemm(ctypes.byref(W.desc), _bits(X), M, Y.data_ptr(), path, _ptr(wsb),
                                  wsb.numel() if wsb is not None else 0, _stream(stream)), "fp4_skinny_gemm")
     return Y
+
+
+class Group:
+    """Matrices of one format and d_in that multiply the same input."""
+
+    def __init__(self, members):
+        members = list(members)
+        if not 1 <= len(members) <= MAX_GROUP:
+            raise ValueError(f"a group holds 1..{MAX_GROUP} matrices")
+        self.members = members  # keeps the buffers alive
+        self.desc = GroupDesc()
+        self.desc.n = len(members)
+        for i, W in enumerate(members):
+            self.desc.w[i] = W.desc
+
+
+def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, ws=None, stream=None):
+    """Ys[i][m] = W_i X[m] for every member W_i of G, X bf16 [M, d_in] (or [d_in]);
+    returns the list of float32 [M, d_out_i] outputs."""
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    M = X2.shape[0]
+    if Ys is None:
+        Ys = [torch.empty((M, W.d_out), dtype=torch.float32, device=X.device) for W in G.members]
+    ptrs = (_VP * len(Ys))(*[y.data_ptr() for y in Ys])
+    wsb, need = _workspace(OP_GROUPED, G, M, X.device, ws)
+    _check(lib().fp4_gemv_grouped(ctypes.byref(G.desc), _bits(X2), M, ptrs, _ptr(wsb),
+                                  wsb.numel() if wsb is not None else 0, _stream(stream)), "fp4_gemv_grouped")
+    return Ys
 
 
 def fp4_gate_up_silu(Wg: PackedWeight, Wu: PackedWeight, X: torch.Tensor, H: torch.Tensor | None = None,
@@ -335,3 +399,43 @@ def moe_route_gemv(layer: MoeLayer, X: torch.Tensor, logits: torch.Tensor, Y: to
                                 topk_w.data_ptr(), _ptr(H), _ptr(wsb), wsb.numel() if wsb is not None else 0,
                                 _stream(stream)), "moe_route_gemv")
     return Y, topk_ids, topk_w
+
+
+class Stream:
+    """A decode step's chain of products run by one persistent launch.
+
+    ops: list of dicts {"kind": OP_GEMV | OP_GATE_UP | OP_LMHEAD, "w": PackedWeight,
+    "w_up": PackedWeight (GATE_UP), "x": bf16 tensor [M, d_in], "out": tensor
+    [M, d_out] (float32, or bfloat16 for GATE_UP), "wait_op": index or -1,
+    "wait_count": ops ending at wait_op to wait for (default 1)}."""
+
+    def __init__(self, ops, M: int, stream=None):
+        n = len(ops)
+        self.M = M
+        self.keep = ops
+        self.arr = (StreamOpDesc * n)()
+        for i, o in enumerate(ops):
+            d = self.arr[i]
+            d.kind = o["kind"]
+            d.wait_op = o.get("wait_op", -1)
+            d.wait_count = o.get("wait_count", 1)
+            d.w = ctypes.pointer(o["w"].desc)
+            d.w_up = ctypes.pointer(o["w_up"].desc) if o.get("w_up") is not None else None
+            assert o["x"].dtype == torch.bfloat16 and o["x"].is_contiguous() and o["out"].is_contiguous()
+            d.x_dev = o["x"].data_ptr()
+            d.out_dev = o["out"].data_ptr()
+        nb = lib().fp4g_stream_workspace_bytes(self.arr, n, M)
+        if nb == 0:
+            raise Fp4gError(2, "fp4g_stream_workspace_bytes")
+        self.ws = torch.zeros(nb, dtype=torch.uint8, device=ops[0]["x"].device)
+        self.plan = StreamPlan()
+        _check(lib().fp4g_stream_build(self.arr, n, M, self.ws.data_ptr(), nb, ctypes.byref(self.plan),
+                                       _stream(stream)), "fp4g_stream_build")
+
+    def run(self, stream=None):
+        _check(lib().fp4_stream_run(ctypes.byref(self.plan), _stream(stream)), "fp4_stream_run")
+
+    def error(self, stream=None) -> int:
+        e = ctypes.c_int32(0)
+        _check(lib().fp4g_stream_error(ctypes.byref(self.plan), ctypes.byref(e), _stream(stream)), "fp4g_stream_error")
+        return e.value

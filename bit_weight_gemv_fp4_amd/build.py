@@ -25,6 +25,9 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep lane-0 atomics as issued: the aggregating rewrite consumes the result
+    # at once, which would stall the weight prefetch behind it
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -1,6 +1,6 @@
 // gemv.hip -- launch planning, host-side validation and the product entry points
-// fp4_gemv, fp4_skinny_gemm, fp4_gate_up_silu and fp8_lmhead_gemv.  The kernel
-// itself is in gemv_kernel.hpp.
+// fp4_gemv, fp4_skinny_gemm, fp4_gemv_grouped, fp4_gate_up_silu and
+// fp8_lmhead_gemv.  The kernel itself is in gemv_kernel.hpp.
 #include "gemv_kernel.hpp"
 
 namespace fp4g {
@@ -13,47 +13,93 @@ extern template hipError_t launch_m<FP4G_MXFP4, 1, EPI_STORE>(int, const GemvPar
 extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, const GemvParams&, unsigned, hipStream_t);
 
-// Shared validation + launch of the single-matrix product (any format).
-int32_t run_gemv(const fp4g_weight* W, bool want_fp4, const uint16_t* X, int32_t M, float* Y, void* ws,
-                 uint64_t ws_bytes, void* stream) {
-  fp4g_status st = check_weight(W, want_fp4);
-  if (st != FP4G_OK) return st;
-  if (!X || !Y) return FP4G_E_NULL;
-  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
-  if (!aligned(X, 16) || !aligned(Y, 16)) return FP4G_E_ALIGN;
-  const int64_t R = row_groups(W->d_out), C = chunks(W->d_in);
-  const uint64_t need = gemv_ws_bytes(R, C, 1, M);
+// Workspace check shared by every entry point: NULL only when nothing is needed,
+// large enough, 256-B aligned.
+static fp4g_status check_ws(const void* ws, uint64_t ws_bytes, uint64_t need) {
   if (need && !ws) return FP4G_E_NULL;
   if (ws_bytes < need) return FP4G_E_WORKSPACE;
   if (need && !aligned(ws, 256)) return FP4G_E_ALIGN;
-  const size_t ybytes = (size_t)M * W->d_out * 4, xbytes = (size_t)M * W->d_in * 2;
-  if (overlap(Y, ybytes, X, xbytes) || overlap(Y, ybytes, W->packed, W->packed_bytes) ||
-      overlap(Y, ybytes, ws, need) || overlap(ws, need, X, xbytes) || overlap(ws, need, W->packed, W->packed_bytes))
-    return FP4G_E_ALIAS;
-  const Plan pl = plan_for(R, C, 1);
+  return FP4G_OK;
+}
+
+// Validation + launch of n products of one input (n = 1: fp4_gemv,
+// fp4_skinny_gemm, fp8_lmhead_gemv).  Members share format and d_in.
+static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, const uint16_t* X, int32_t M,
+                         float* const* Y, void* ws, uint64_t ws_bytes, void* stream) {
+  if (n < 1 || n > kMaxGroup) return FP4G_E_SHAPE;
+  for (int i = 0; i < n; ++i) {
+    const fp4g_status st = check_weight(W[i], want_fp4);
+    if (st != FP4G_OK) return st;
+  }
+  for (int i = 1; i < n; ++i) {
+    if (W[i]->format != W[0]->format) return FP4G_E_FORMAT;
+    if (W[i]->d_in != W[0]->d_in) return FP4G_E_SHAPE;
+  }
+  if (!X) return FP4G_E_NULL;
+  for (int i = 0; i < n; ++i)
+    if (!Y[i]) return FP4G_E_NULL;
+  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
+  if (!aligned(X, 16)) return FP4G_E_ALIGN;
+  for (int i = 0; i < n; ++i)
+    if (!aligned(Y[i], 16)) return FP4G_E_ALIGN;
+  int64_t R_total = 0;
+  for (int i = 0; i < n; ++i) R_total += row_groups(W[i]->d_out);
+  const int64_t C = chunks(W[0]->d_in);
+  const uint64_t need = gemv_ws_bytes(R_total, C, 1, M);
+  const fp4g_status wst = check_ws(ws, ws_bytes, need);
+  if (wst != FP4G_OK) return wst;
+  const size_t xbytes = (size_t)M * W[0]->d_in * 2;
+  if (overlap(ws, need, X, xbytes)) return FP4G_E_ALIAS;
+  for (int i = 0; i < n; ++i) {
+    const size_t yb = (size_t)M * W[i]->d_out * 4;
+    if (overlap(Y[i], yb, X, xbytes) || overlap(Y[i], yb, ws, need) || overlap(ws, need, W[i]->packed, W[i]->packed_bytes))
+      return FP4G_E_ALIAS;
+    for (int j = 0; j < n; ++j) {
+      if (overlap(Y[i], yb, W[j]->packed, W[j]->packed_bytes)) return FP4G_E_ALIAS;
+      if (j > i && overlap(Y[i], yb, Y[j], (size_t)M * W[j]->d_out * 4)) return FP4G_E_ALIAS;
+    }
+  }
+  const Plan pl = plan_for(R_total, C, 1);
   GemvParams p{};
-  p.w[0] = p.w[1] = (const uint8_t*)W->packed;
-  p.tscale[0] = p.tscale[1] = W->tensor_scale;
+  p.n = n;
+  int64_t gb = 0;
+  for (int i = 0; i < n; ++i) {
+    p.w[i] = (const uint8_t*)W[i]->packed;
+    p.tscale[i] = W[i]->tensor_scale;
+    p.y[i] = Y[i];
+    p.d_out[i] = W[i]->d_out;
+    p.gbase[i] = (int)gb;
+    gb += row_groups(W[i]->d_out);
+  }
+  p.gbase[n] = (int)gb;
   p.x = X;
-  p.y = Y;
-  p.counters = (unsigned*)ws;
-  p.part = need ? (float*)((uint8_t*)ws + kCounterBytes) : nullptr;
-  p.d_out = W->d_out;
-  p.d_in = W->d_in;
-  p.R = (int)R;
+  p.slots = need ? (unsigned long long*)ws : nullptr;
+  p.d_in = W[0]->d_in;
   p.C = (int)C;
   p.S = pl.S;
   p.wg_chunks = pl.wg_chunks;
-  const unsigned grid = (unsigned)(R * pl.S);
+  const unsigned grid = (unsigned)(R_total * pl.S);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (W->format == FP4G_NVFP4)
+  if (W[0]->format == FP4G_NVFP4)
     e = launch_m<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, s);
-  else if (W->format == FP4G_MXFP4)
+  else if (W[0]->format == FP4G_MXFP4)
     e = launch_m<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, s);
   else
     e = launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(M, p, grid, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
+}
+
+static int32_t run_gemv(const fp4g_weight* W, bool want_fp4, const uint16_t* X, int32_t M, float* Y, void* ws,
+                        uint64_t ws_bytes, void* stream) {
+  if (!W) return FP4G_E_NULL;
+  return run_group(&W, 1, want_fp4, X, M, &Y, ws, ws_bytes, stream);
+}
+
+static fp4g_status check_group(const fp4g_group* G) {
+  if (!G) return FP4G_E_NULL;
+  if (G->n < 1 || G->n > kMaxGroup) return FP4G_E_SHAPE;
+  return FP4G_OK;
 }
 
 }  // namespace fp4g
@@ -68,11 +114,18 @@ int32_t fp4_gemv(const fp4g_weight* W, const uint16_t* x, float* y, void* ws, ui
 
 int32_t fp4_skinny_gemm(const fp4g_weight* W, const uint16_t* X, int32_t M, float* Y, int32_t path, void* ws,
                         uint64_t ws_bytes, void* stream) {
-  if (path != FP4G_PATH_AUTO && path != FP4G_PATH_VALU) {
-    if (path == FP4G_PATH_MFMA) return FP4G_E_PATH;
-    return FP4G_E_PATH;
-  }
+  if (path != FP4G_PATH_AUTO && path != FP4G_PATH_VALU) return FP4G_E_PATH;
   return run_gemv(W, true, X, M, Y, ws, ws_bytes, stream);
+}
+
+int32_t fp4_gemv_grouped(const fp4g_group* G, const uint16_t* X, int32_t M, float* const* Y, void* ws,
+                         uint64_t ws_bytes, void* stream) {
+  const fp4g_status st = check_group(G);
+  if (st != FP4G_OK) return st;
+  if (!Y) return FP4G_E_NULL;
+  const fp4g_weight* W[kMaxGroup];
+  for (int i = 0; i < G->n; ++i) W[i] = &G->w[i];
+  return run_group(W, G->n, true, X, M, Y, ws, ws_bytes, stream);
 }
 
 int32_t fp8_lmhead_gemv(const fp4g_weight* W, const uint16_t* X, int32_t M, float* logits, void* ws,
@@ -94,9 +147,8 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   if (!aligned(X, 16) || !aligned(H, 16)) return FP4G_E_ALIGN;
   const int64_t R = row_groups(Wg->d_out), C = chunks(Wg->d_in);
   const uint64_t need = gemv_ws_bytes(R, C, 2, M);
-  if (need && !ws) return FP4G_E_NULL;
-  if (ws_bytes < need) return FP4G_E_WORKSPACE;
-  if (need && !aligned(ws, 256)) return FP4G_E_ALIGN;
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FP4G_OK) return st;
   const size_t hbytes = (size_t)M * Wg->d_out * 2, xbytes = (size_t)M * Wg->d_in * 2;
   if (overlap(H, hbytes, X, xbytes) || overlap(H, hbytes, Wg->packed, Wg->packed_bytes) ||
       overlap(H, hbytes, Wu->packed, Wu->packed_bytes) || overlap(H, hbytes, ws, need) ||
@@ -105,17 +157,18 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
     return FP4G_E_ALIAS;
   const Plan pl = plan_for(R, C, 2);
   GemvParams p{};
+  p.n = 1;
   p.w[0] = (const uint8_t*)Wg->packed;
   p.w[1] = (const uint8_t*)Wu->packed;
   p.tscale[0] = Wg->tensor_scale;
   p.tscale[1] = Wu->tensor_scale;
+  p.d_out[0] = Wg->d_out;
+  p.gbase[0] = 0;
+  p.gbase[1] = (int)R;
   p.x = X;
   p.h = H;
-  p.counters = (unsigned*)ws;
-  p.part = need ? (float*)((uint8_t*)ws + kCounterBytes) : nullptr;
-  p.d_out = Wg->d_out;
+  p.slots = need ? (unsigned long long*)ws : nullptr;
   p.d_in = Wg->d_in;
-  p.R = (int)R;
   p.C = (int)C;
   p.S = pl.S;
   p.wg_chunks = pl.wg_chunks;
@@ -129,6 +182,17 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
   if (!desc || M < 1 || M > kMaxM) return 0;
   if (op == FP4G_OP_MOE) return moe_ws_bytes((const fp4g_moe*)desc, M);
+  if (op == FP4G_OP_GROUPED) {
+    const fp4g_group* G = (const fp4g_group*)desc;
+    if (check_group(G) != FP4G_OK) return 0;
+    int64_t R = 0;
+    for (int i = 0; i < G->n; ++i) {
+      if (check_weight(&G->w[i], true) != FP4G_OK) return 0;
+      if (G->w[i].format != G->w[0].format || G->w[i].d_in != G->w[0].d_in) return 0;
+      R += row_groups(G->w[i].d_out);
+    }
+    return gemv_ws_bytes(R, chunks(G->w[0].d_in), 1, M);
+  }
   const fp4g_weight* W = (const fp4g_weight*)desc;
   const bool fp4 = op != FP4G_OP_LMHEAD;
   if (op != FP4G_OP_GEMV && op != FP4G_OP_GATE_UP && op != FP4G_OP_LMHEAD) return 0;

@@ -19,10 +19,13 @@
 //    the epilogue.
 //  * Split-K: a row group's chunks are divided over S workgroups of four waves so
 //    that there are enough waves to keep all 256 CUs streaming.  The four waves of
-//    a workgroup reduce through LDS in a fixed order; across workgroups, partial
-//    sums go to the workspace and the last workgroup to arrive (device-scope
-//    counter) adds them in split order and runs the epilogue.  Results are
-//    therefore deterministic.
+//    a workgroup reduce through LDS in a fixed order; across workgroups the sums
+//    meet in a binary tree of device-scope atomic exchanges (one round trip per
+//    level, no counters, no fences).  Each pair sum is commutative and the tree
+//    shape is fixed, so results are deterministic.
+//  * Grouped launch: up to four matrices of one format and input width (the Q, K
+//    and V projections of a layer) share one launch; each row group knows its
+//    member from the group's row-group offsets.
 #pragma once
 #include "common.hpp"
 
@@ -31,17 +34,23 @@ namespace fp4g {
 
 enum { EPI_STORE = 0, EPI_SILU = 1 };
 
+constexpr int kMaxGroup = 4;  // matrices sharing one input in one launch
+
 struct GemvParams {
-  const uint8_t* w[2];     // packed images (tiles) of up to two matrices of one shape
-  float tscale[2];         // NVFP4 tensor scales (1.0 otherwise)
-  const uint16_t* x;       // bf16 [M][d_in]
-  float* y;                // EPI_STORE: f32 [M][d_out]
-  uint16_t* h;             // EPI_SILU: bf16 [M][d_out]
-  float* part;             // split-K partial sums [S][NMAT][M][R*64]
-  unsigned* counters;      // [R] arrival counters (zero between calls)
-  int d_out, d_in, R, C;
-  int S;                   // workgroups per row group
-  int wg_chunks;           // chunks per workgroup (the last one may get fewer)
+  // NMAT == 1: n members (matrices sharing x), each with its own output;
+  // NMAT == 2: one gate/up pair (w[0], w[1]) of one shape, fused epilogue.
+  const uint8_t* w[kMaxGroup];
+  float tscale[kMaxGroup];
+  float* y[kMaxGroup];        // EPI_STORE: f32 [M][d_out[i]]
+  int d_out[kMaxGroup];
+  int gbase[kMaxGroup + 1];   // first global 64-row group of member i; gbase[n] = all groups
+  int n;
+  const uint16_t* x;          // bf16 [M][d_in]
+  uint16_t* h;                // EPI_SILU: bf16 [M][d_out[0]]
+  unsigned long long* slots;  // split-K exchange slots, zero between calls
+  int d_in, C;
+  int S;                      // workgroups per row group
+  int wg_chunks;              // chunks per workgroup (the last ones may get fewer)
 };
 
 template <uint32_t FMT>
@@ -153,25 +162,37 @@ __device__ __forceinline__ void tile_dot(const Frag<FMT>& f, const uint32_t* __r
   }
 }
 
-// Epilogue for one row of one 64-row group, given the full dot products v.
+// Split-K results travel as 64-bit units: EPI_STORE packs the values of tokens
+// 2u and 2u+1, EPI_SILU the (gate, up) pair of token u.  Encoding: low word =
+// bits(a) + 1, high word = bits(b), so that 0 (a zero-filled slot) never
+// encodes a value (that would need bits(a) = 0xFFFFFFFF, a NaN arithmetic never
+// produces).
+__device__ __forceinline__ unsigned long long enc_unit(float a, float b) {
+  return (unsigned long long)(__float_as_uint(a) + 1u) | ((unsigned long long)__float_as_uint(b) << 32);
+}
+__device__ __forceinline__ void dec_unit(unsigned long long v, float& a, float& b) {
+  a = __uint_as_float((uint32_t)v - 1u);
+  b = __uint_as_float((uint32_t)(v >> 32));
+}
+
+// Epilogue for unit u of one row of member `mem` (row local to that member).
 template <uint32_t FMT, int M, int NMAT, int EPI>
-__device__ __forceinline__ void finish_row(const GemvParams& p, int row, const float (&v)[NMAT * M]) {
-  if (row >= p.d_out) return;
+__device__ __forceinline__ void finish_unit(const GemvParams& p, int mem, int row, int u, float a, float b) {
+  if (row >= p.d_out[mem]) return;
   if constexpr (EPI == EPI_STORE) {
-    float sc = p.tscale[0];
+    float sc = p.tscale[mem];
     if constexpr (FMT == FP4G_FP8_ROW) {
-      const float* rs = reinterpret_cast<const float*>(p.w[0] + (int64_t)p.R * p.C * kTileF8);
-      sc = rs[row];
+      const int64_t R = p.gbase[1] - p.gbase[0];
+      const int64_t C = p.C;
+      sc = reinterpret_cast<const float*>(p.w[0] + R * C * kTileF8)[row];
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) p.y[(int64_t)m * p.d_out + row] = v[m] * sc;
+    const int m0 = 2 * u;
+    p.y[mem][(int64_t)m0 * p.d_out[mem] + row] = a * sc;
+    if (m0 + 1 < M) p.y[mem][(int64_t)(m0 + 1) * p.d_out[mem] + row] = b * sc;
   } else {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float g = v[m] * p.tscale[0];
-      const float u = v[M + m] * p.tscale[1];
-      p.h[(int64_t)m * p.d_out + row] = f32_to_bf16_rne(silu_f32(g) * u);
-    }
+    const float g = a * p.tscale[0];
+    const float v = b * p.tscale[1];
+    p.h[(int64_t)u * p.d_out[0] + row] = f32_to_bf16_rne(silu_f32(g) * v);
   }
 }
 
@@ -183,8 +204,17 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int g = uniform(blockIdx.x / p.S);
+  const int gt = uniform(blockIdx.x / p.S);  // global row group
   const int s = uniform(blockIdx.x % p.S);
+  int mem = 0;
+  if constexpr (NMAT == 1) {
+#pragma unroll
+    for (int i = 1; i < kMaxGroup; ++i)
+      if (i < p.n && gt >= p.gbase[i]) mem = i;
+  }
+  const int g = gt - p.gbase[mem];
+  const uint8_t* w0 = p.w[mem];
+  const uint8_t* w1 = NMAT == 2 ? p.w[1] : w0;
   const int wg_c0 = s * p.wg_chunks;
   const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
   const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
@@ -206,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
   // alternate: the tile of item it+1 is in flight while item it is consumed.
   const int n_items = (c1 - c0) * NMAT;
   const int64_t tile0 = (int64_t)g * p.C;
-  auto item_tile = [&](int it) { return p.w[it % NMAT] + (tile0 + c0 + it / NMAT) * TILE; };
+  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE; };
   auto consume = [&](const Frag<FMT>& f, int it) {
     const int c = c0 + it / NMAT;
     const uint32_t* xc = x32 + (int64_t)c * (kChunkK / 2);
@@ -258,24 +288,62 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
 #pragma unroll
   for (int i = 0; i < NA; ++i) v[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
 
+  // units: EPI_STORE (v[2u], v[2u+1]); EPI_SILU (gate v[u], up v[M+u])
+  constexpr int NU = EPI == EPI_SILU ? M : (M + 1) / 2;
+  float ua[NU], ub[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if constexpr (EPI == EPI_SILU) {
+      ua[u] = v[u];
+      ub[u] = v[M + u];
+    } else {
+      ua[u] = v[2 * u];
+      ub[u] = 2 * u + 1 < M ? v[2 * u + 1] : 0.0f;
+    }
+  }
   const int row = g * 64 + lane;
-  if (p.S == 1) {
-    finish_row<FMT, M, NMAT, EPI>(p, row, v);
-    return;
-  }
-  // split-K hand-off: publish partials, count arrivals, the last one finishes
-  const int64_t rpad = (int64_t)p.R * 64;
+  // Split-K: a binary tree of exchanges.  At each level the two subtrees of a
+  // node swap their sums into the node's slot; the first to arrive deposits, the
+  // second receives the first's sum in the same round trip, adds (a + b == b + a,
+  // so the result does not depend on who is second) and carries on.  One
+  // device-scope atomic round trip per level; slots are left zero.
+  bool live[NU];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) publish_partial(p.part + ((int64_t)s * NA + i) * rpad + row, v[i]);
-  if (!arrive_last(p.counters + g, (unsigned)(p.S - 1))) return;
+  for (int u = 0; u < NU; ++u) live[u] = true;
+  const int64_t unit_stride = (int64_t)p.gbase[p.n] * 64;  // slots per (node, unit)
+  // level l has n nodes; node idx pairs with idx ^ 1, an unpaired last one passes up
+  int node_off = 0, n = p.S, idx = s;
+  while (n > 1) {
+    if ((idx ^ 1) < n) {
+      unsigned long long* base =
+          p.slots + ((int64_t)(node_off + (idx >> 1)) * NU) * unit_stride + (int64_t)gt * 64 + lane;
+      unsigned long long old[NU];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    float t = 0.0f;
-    for (int q = 0; q < p.S; ++q) t += collect_partial(p.part + ((int64_t)q * NA + i) * rpad + row);
-    v[i] = t;
+      for (int u = 0; u < NU; ++u)
+        old[u] = live[u] ? __hip_atomic_exchange(base + u * unit_stride, enc_unit(ua[u], ub[u]), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                         : 0ull;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (!live[u]) continue;
+        if (old[u] == 0ull) {
+          live[u] = false;  // deposited: the partner carries the pair sum on
+        } else {
+          float oa, ob;
+          dec_unit(old[u], oa, ob);
+          ua[u] = oa + ua[u];
+          ub[u] = ob + ub[u];
+          __hip_atomic_store(base + u * unit_stride, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    node_off += n >> 1;
+    n = (n + 1) >> 1;
+    idx >>= 1;
   }
-  finish_row<FMT, M, NMAT, EPI>(p, row, v);
-  reset_counter(p.counters + g);
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    if (live[u]) finish_unit<FMT, M, NMAT, EPI>(p, mem, row, u, ua[u], ub[u]);
 }
 
 template <uint32_t FMT, int NMAT, int EPI>
@@ -305,7 +373,6 @@ inline Plan plan_for(int64_t R, int64_t C, int nmat) {
   const int64_t target_waves = 2048;
   int64_t q = (R * C) / target_waves;  // chunks per wave
   if (q < 1) q = 1;
-  if (R > kMaxCounters) return Plan{1, (int)C};  // (S > 1 needs R < 512 anyway)
   int64_t S = (C + kWavesPerWg * q - 1) / (kWavesPerWg * q);
   if (S < 1) S = 1;
   const int64_t wg_chunks = (C + S - 1) / S;
@@ -315,10 +382,22 @@ inline Plan plan_for(int64_t R, int64_t C, int nmat) {
 
 inline uint64_t align256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
 
-inline uint64_t gemv_ws_bytes(int64_t R, int64_t C, int nmat, int M) {
-  const Plan pl = plan_for(R, C, nmat);
+// Pair nodes of the split-K exchange tree over S leaves (S - 1 when S is a power
+// of two; an unpaired node passes up without one).
+inline int64_t tree_nodes(int64_t S) {
+  int64_t t = 0;
+  for (int64_t n = S; n > 1; n = (n + 1) / 2) t += n / 2;
+  return t;
+}
+
+// Units per row: EPI_SILU exchanges (gate, up) per token, EPI_STORE two tokens.
+inline int64_t exchange_units(int nmat, int M) { return nmat == 2 ? M : (M + 1) / 2; }
+
+// Exchange slots: tree nodes x units x all rows of all members, 8 bytes each.
+inline uint64_t gemv_ws_bytes(int64_t R_total, int64_t C, int nmat, int M) {
+  const Plan pl = plan_for(R_total, C, nmat);
   if (pl.S == 1) return 0;
-  return kCounterBytes + (uint64_t)pl.S * nmat * M * R * 64 * 4;
+  return (uint64_t)tree_nodes(pl.S) * exchange_units(nmat, M) * R_total * 64 * 8;
 }
 
 }  // namespace fp4g

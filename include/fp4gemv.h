@@ -89,8 +89,12 @@ typedef enum {
   FP4G_OP_GEMV = 1,     /* fp4_gemv and fp4_skinny_gemm; desc = fp4g_weight */
   FP4G_OP_GATE_UP = 2,  /* fp4_gate_up_silu; desc = fp4g_weight (gate) */
   FP4G_OP_MOE = 3,      /* moe_route_gemv; desc = fp4g_moe */
-  FP4G_OP_LMHEAD = 4    /* fp8_lmhead_gemv; desc = fp4g_weight */
+  FP4G_OP_LMHEAD = 4,   /* fp8_lmhead_gemv; desc = fp4g_weight */
+  FP4G_OP_GROUPED = 5   /* fp4_gemv_grouped; desc = fp4g_group */
 } fp4g_op;
+
+/* Most matrices one fp4_gemv_grouped call takes. */
+#define FP4G_MAX_GROUP 4
 
 /* A packed weight matrix.  A plain view: it owns nothing.  Filled in by
  * fp4g_pack; callers must not edit it. */
@@ -122,6 +126,16 @@ typedef struct {
   int32_t reserved;
   fp4g_weight sh_gate, sh_up, sh_down;          /* used when has_shared == 1 */
 } fp4g_moe;
+
+/* Matrices that multiply the same input: the query, key and value projections of
+ * an attention layer, all read by one decode step (feed, section "Decode speed is
+ * bytes divided by bandwidth").  All members share format (NVFP4 or MXFP4) and
+ * d_in; d_out may differ.  Only w[0..n) are read. */
+typedef struct {
+  int32_t n;            /* 1..FP4G_MAX_GROUP */
+  int32_t reserved;
+  fp4g_weight w[FP4G_MAX_GROUP];
+} fp4g_group;
 
 /* --- library info ------------------------------------------------------- */
 
@@ -177,14 +191,14 @@ int32_t fp4g_validate(const fp4g_weight* W_host, int64_t* bad_dev, void* stream)
 /* --- workspace ---------------------------------------------------------------- */
 
 /* Bytes of device workspace the call `op` needs for descriptor `desc_host`
- * (fp4g_weight or fp4g_moe, see fp4g_op) and M vectors; 0 means none (then ws_dev
- * may be NULL).  A call given less returns FP4G_E_WORKSPACE.  Every workspace
- * begins with a fixed 64 KiB region of hand-off counters (split-K arrival counts)
- * which no call uses for anything else; partial sums and routing tables follow
- * it.  The caller zero-fills that first 64 KiB once, before a workspace's first
- * use; every call leaves the counters at zero again when its kernels complete, so
- * one workspace serves calls of any shape.  Calls that share a workspace must be
- * ordered on one stream.  Returns 0 also for invalid arguments. */
+ * (fp4g_weight, fp4g_group or fp4g_moe, see fp4g_op) and M vectors; 0 means none
+ * (then ws_dev may be NULL).  A call given less returns FP4G_E_WORKSPACE.  The
+ * workspace holds split-K exchange slots, hand-off counters, routing tables and
+ * partial sums.  The caller zero-fills a workspace once, before its first use;
+ * every call leaves the slots and counters at zero again when its kernels
+ * complete, so one zero-filled workspace (of the largest size needed) serves
+ * calls of any shape.  Calls that share a workspace must be ordered on one
+ * stream.  Returns 0 also for invalid arguments. */
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc_host, int32_t M);
 
 /* --- products --------------------------------------------------------------- */
@@ -200,6 +214,14 @@ int32_t fp4_gemv(const fp4g_weight* W_host, const uint16_t* x_dev, float* y_dev,
  * path: fp4g_path. */
 int32_t fp4_skinny_gemm(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M, float* Y_dev,
                         int32_t path, void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* Several products of one input in one launch: Y_dev[i][m][r] = sum_k
+ * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..8.  X_dev: bf16
+ * [M][d_in]; Y_dev: host array of G->n device pointers, each f32 [M][w_i.d_out],
+ * 16-B aligned and disjoint.  Each member's results are those of fp4_skinny_gemm
+ * on it alone up to the order of the FP32 additions. */
+int32_t fp4_gemv_grouped(const fp4g_group* G_host, const uint16_t* X_dev, int32_t M,
+                         float* const* Y_host, void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* Fused MLP front half: g = Wg X_m, u = Wu X_m, H_dev[m][r] = bf16_rne(SiLU(g[r]) *
  * u[r]) with SiLU(z) = z / (1 + e^-z), for m < M in 1..8.  Wg and Wu are NVFP4 or
@@ -236,6 +258,69 @@ int32_t moe_route_gemv(const fp4g_moe* moe_host, const uint16_t* X_dev, const fl
  * X_dev: bf16 [M][d_in]; logits_dev: f32 [M][d_out]. */
 int32_t fp8_lmhead_gemv(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M,
                         float* logits_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* --- a whole decode step in one launch --------------------------------------- */
+
+/* One product of a decode step.  Decoding a token runs every matrix of the model
+ * once, each on the previous one's output (feed, section "Decode speed is bytes
+ * divided by bandwidth"); a stream is that chain, executed by one persistent
+ * launch that keeps HBM busy across the boundaries between products.
+ *   kind     FP4G_OP_GEMV: NVFP4/MXFP4 matrix, out = f32 [M][d_out];
+ *            FP4G_OP_GATE_UP: gate (w) and up (w_up) of one shape, out = bf16
+ *            [M][d_out] = bf16(SiLU(gate x) * (up x)) as fp4_gate_up_silu;
+ *            FP4G_OP_LMHEAD: FP8_ROW matrix, out = f32 [M][d_out].
+ *   wait_op  -1, or the index of an earlier op: this op reads x only after every
+ *            output row of ops wait_op-wait_count+1 .. wait_op is written.
+ *   wait_count  how many consecutive ops end at wait_op (0 is taken as 1); ops
+ *            that read the same input and wait for the same ops run concurrently
+ *            (e.g. the projections of one input).  The op's x may overlap the
+ *            outputs of the ops it waits for and of no other op.
+ *   w, w_up  host pointers to descriptors; d_out % 64 == 0, d_in % 256 == 0.
+ *   x_dev    bf16 [M][d_in], 16-B aligned.  out_dev: 256-B aligned; outputs of
+ *            different ops must not overlap each other, any weights or any x
+ *            except as above. */
+typedef struct {
+  int32_t kind;
+  int32_t wait_op;
+  int32_t wait_count;
+  int32_t reserved;
+  const fp4g_weight* w;
+  const fp4g_weight* w_up;
+  const uint16_t* x_dev;
+  void* out_dev;
+} fp4g_stream_op;
+
+/* Filled in by fp4g_stream_build; passed by value to the calls below. */
+typedef struct {
+  uint32_t magic;
+  int32_t M;        /* vectors per product, 1..8 */
+  int32_t n_ops;
+  int32_t n_items;  /* work items (op, 64-row group, column range) */
+  int32_t grid;     /* workgroups per launch */
+  int32_t reserved;
+  void* ws;         /* the stream's workspace (device) */
+  uint64_t ws_bytes;
+} fp4g_stream_plan;
+
+/* Workspace bytes for a stream of n_ops ops at M vectors (0 if invalid). */
+uint64_t fp4g_stream_workspace_bytes(const fp4g_stream_op* ops_host, int32_t n_ops, int32_t M);
+
+/* Validate the ops, write the op table into ws_dev, zero its counters, and fill
+ * *plan_host.  Synchronises `stream`.  The workspace then belongs to this stream
+ * (do not pass it to other calls).  The descriptors and device buffers the ops
+ * name must stay valid for every run. */
+int32_t fp4g_stream_build(const fp4g_stream_op* ops_host, int32_t n_ops, int32_t M, void* ws_dev, uint64_t ws_bytes,
+                          fp4g_stream_plan* plan_host, void* stream);
+
+/* Run every op of the stream once, in one asynchronous launch (capturable in a
+ * HIP graph).  Runs of one plan must be ordered on one stream.  A run that hits
+ * an internal time-out sets a sticky error flag (see fp4g_stream_error) instead
+ * of hanging; its outputs are then unspecified. */
+int32_t fp4_stream_run(const fp4g_stream_plan* plan_host, void* stream);
+
+/* Read (into *err_host: 0 = every run since the last check was complete) and
+ * clear the sticky error flag.  Synchronises `stream`. */
+int32_t fp4g_stream_error(const fp4g_stream_plan* plan_host, int32_t* err_host, void* stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 17, names
     L = fg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -110,6 +110,50 @@ def test_skinny_and_lmhead_error_paths():
     f8 = good_desc(fmt=fg.FP8_ROW)
     assert L.fp8_lmhead_gemv(ctypes.byref(f8), X, 9, Y, None, 0, None) == E_SHAPE
     assert L.fp8_lmhead_gemv(ctypes.byref(f8), None, 1, Y, None, 0, None) == E_NULL
+
+
+def group_desc(*members):
+    G = fg.GroupDesc()
+    G.n = len(members)
+    for i, d in enumerate(members):
+        G.w[i] = d
+    return G
+
+
+def call_grouped(G, M=1, x=FAKE + (1 << 30), ys=None, ws=None, wsb=0):
+    if ys is None:
+        ys = [FAKE + ((2 + i) << 30) for i in range(max(G.n, 1))]
+    arr = (ctypes.c_void_p * len(ys))(*ys)
+    return fg.lib().fp4_gemv_grouped(ctypes.byref(G), x, M, arr, ws, wsb, None)
+
+
+def test_grouped_error_paths():
+    L = fg.lib()
+    q = good_desc(d_out=128); k = good_desc(d_out=64); k.packed = FAKE + (8 << 30)
+    assert L.fp4_gemv_grouped(None, FAKE, 1, None, None, 0, None) == E_NULL
+    assert call_grouped(group_desc()) == E_SHAPE                       # n = 0
+    G = group_desc(q, k); G.n = 5
+    assert call_grouped(G) == E_SHAPE                                  # n > 4
+    assert call_grouped(group_desc(q, k), M=9) == E_SHAPE
+    k2 = good_desc(fg.MXFP4, d_out=64); k2.packed = FAKE + (8 << 30)
+    assert call_grouped(group_desc(q, k2)) == E_FORMAT                 # mixed formats
+    k3 = good_desc(d_out=64, d_in=256); k3.packed = FAKE + (8 << 30)
+    assert call_grouped(group_desc(q, k3)) == E_SHAPE                  # mixed d_in
+    f8 = good_desc(fg.FP8_ROW)
+    assert call_grouped(group_desc(f8)) == E_FORMAT                    # FP8 rows go to the head call
+    assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), 0]) == E_NULL
+    assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (3 << 30) + 4]) == E_ALIGN
+    assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (2 << 30) + 256]) == E_ALIAS
+    assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (8 << 30) + 512]) == E_ALIAS  # into k's weights
+    assert fg.lib().fp4_gemv_grouped(ctypes.byref(group_desc(q, k)), FAKE, 1, None, None, 0, None) == E_NULL
+    # QKV-shaped group: more row groups than any member, so split-K workspace
+    qq = good_desc(d_out=5120, d_in=5120); kk = good_desc(d_out=1024, d_in=5120); kk.packed = FAKE + (8 << 30)
+    G = group_desc(qq, kk)
+    need = L.fp4g_workspace_bytes(fg.OP_GROUPED, ctypes.byref(G), 1)
+    assert need > 0
+    assert call_grouped(G) == E_NULL
+    assert call_grouped(G, ws=FAKE + (12 << 30), wsb=need - 8) == E_WORKSPACE
+    assert L.fp4g_workspace_bytes(fg.OP_GROUPED, ctypes.byref(group_desc(q, k2)), 1) == 0
 
 
 def test_gate_up_error_paths():
@@ -207,3 +251,49 @@ def test_workspace_queries():
     assert fg.workspace_bytes(fg.OP_GEMV, good_desc(), 0) == 0
     bad = good_desc(); bad.layout_tag = 0
     assert fg.workspace_bytes(fg.OP_GEMV, bad, 1) == 0
+
+
+def stream_op(kind=fg.OP_GEMV, wait=-1, d_out=128, d_in=512, fmt=fg.NVFP4, x=FAKE + (20 << 32), out=FAKE + (21 << 32),
+              w_base=0):
+    w = good_desc(fmt, d_out, d_in)
+    w.packed = FAKE + ((30 + w_base) << 32)
+    o = fg.StreamOpDesc()
+    o.kind, o.wait_op = kind, wait
+    o.w = ctypes.pointer(w)
+    o.w_up = ctypes.pointer(good_desc(fmt, d_out, d_in)) if kind == fg.OP_GATE_UP else None
+    if kind == fg.OP_GATE_UP:
+        o.w_up.contents.packed = FAKE + ((60 + w_base) << 32)
+    o.x_dev, o.out_dev = x, out
+    return o, w
+
+
+def build_stream(ops, M=1, ws=FAKE + (50 << 32), wsb=None):
+    arr = (fg.StreamOpDesc * len(ops))(*[o for o, _ in ops])
+    if wsb is None:
+        wsb = fg.lib().fp4g_stream_workspace_bytes(arr, len(ops), M)
+    plan = fg.StreamPlan()
+    return fg.lib().fp4g_stream_build(arr, len(ops), M, ws, wsb, ctypes.byref(plan), None)
+
+
+def test_stream_error_paths():
+    L = fg.lib()
+    ok = [stream_op(), stream_op(wait=0, out=FAKE + (22 << 32), w_base=1)]
+    arr = (fg.StreamOpDesc * 2)(*[o for o, _ in ok])
+    assert L.fp4g_stream_workspace_bytes(arr, 2, 1) > 0
+    assert L.fp4g_stream_workspace_bytes(arr, 2, 9) == 0
+    assert L.fp4g_stream_workspace_bytes(arr, 0, 1) == 0
+    assert build_stream([stream_op(d_in=288)]) == E_SHAPE           # d_in % 256
+    assert build_stream([stream_op(d_out=70)]) == E_SHAPE           # d_out % 64
+    assert build_stream([stream_op(wait=0)]) == E_SHAPE             # waits on itself
+    assert build_stream([stream_op(kind=9)]) == E_FORMAT
+    assert build_stream([stream_op(kind=fg.OP_LMHEAD)]) == E_FORMAT  # NVFP4 given to an FP8 op
+    assert build_stream([stream_op(out=FAKE + (21 << 32) + 16)]) == E_ALIGN
+    assert build_stream([stream_op(), stream_op(wait=0, w_base=1)]) == E_ALIAS  # same output twice
+    # op 1 reads op 0's output without waiting for it
+    assert build_stream([stream_op(), stream_op(x=FAKE + (21 << 32), out=FAKE + (22 << 32), w_base=1)]) == E_ALIAS
+    assert build_stream(ok, ws=None) == E_NULL
+    assert build_stream(ok, wsb=1024) == E_WORKSPACE
+    plan = fg.StreamPlan()
+    assert L.fp4_stream_run(ctypes.byref(plan), None) == E_NULL
+    plan.ws = FAKE
+    assert L.fp4_stream_run(ctypes.byref(plan), None) == E_FORMAT   # not built

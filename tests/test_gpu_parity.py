@@ -225,6 +225,63 @@ def test_sign_flip_and_determinism():
     assert torch.equal(fg.fp4_gemv(W, -x), -y1)
 
 
+# ---- split-K exchange tree and grouped launches ----------------------------------------------
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_split_k_tree_exact_for_every_split_count(M):
+    """Exact-sum inputs (scales 1.0, x in {-1,0,1}) at widths that give 2..63
+    workgroups per row group, power of two or not: every tree shape must return
+    the exact sum, bit for bit, and a second call the same bits."""
+    log("tree exact", M)
+    for C in (8, 12, 20, 28, 36, 60, 124, 252):
+        d_out, d_in = 130, 256 * C
+        mat = datagen.matrix(fg.NVFP4, d_out, d_in, datagen.tensor_seed("tree", C), device=DEV)
+        sc = torch.full_like(mat["scales"], 0x38)
+        W = fg.pack(fg.NVFP4, mat["codes"], sc)
+        g = torch.Generator(DEV).manual_seed(C * 10 + M)
+        X = torch.randint(-1, 2, (M, d_in), generator=g, device=DEV).to(torch.bfloat16)
+        Y, _ = oracle.gemv(fg.NVFP4, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
+        got = fg.fp4_skinny_gemm(W, X).clone()
+        assert np.array_equal(got.cpu().double().numpy(), Y), C
+        assert torch.equal(fg.fp4_skinny_gemm(W, X), got), C
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_grouped_matches_oracle(fmt, M):
+    """Ragged members (1, 70, 200 and 64 rows) of one input in one launch."""
+    log("grouped", fmt, M)
+    shapes = [(70, 1056), (1, 1056), (200, 1056), (64, 1056)]
+    mats = [make(fmt, o, i, seed=("grp", j)) for j, (o, i) in enumerate(shapes)]
+    X = datagen.bf16_normal((M, 1056), datagen.tensor_seed("grpX", M), device=DEV)
+    for n in (1, 2, 4):
+        G = fg.Group([W for W, _ in mats[:n]])
+        Ys = fg.fp4_gemv_grouped(G, X)
+        for (W, host), Y in zip(mats[:n], Ys):
+            check_product(Y, host, bits(X))
+
+
+def test_grouped_qkv_full_size():
+    """The three projections of the dense attention block that read the hidden
+    vector (12288, 12288 and 7680 rows of 5120), sampled rows, M = 1 and 4; the
+    grouped results agree with single-matrix calls and repeat bit for bit."""
+    log("grouped qkv")
+    shapes = [s for s in datagen.ATTN_SHAPES if s[1] == datagen.HIDDEN]
+    mats = [make(fg.NVFP4, o, i, seed=("qkv", j)) for j, (o, i) in enumerate(shapes)]
+    G = fg.Group([W for W, _ in mats])
+    for M in (1, 4):
+        X = datagen.bf16_normal((M, datagen.HIDDEN), datagen.tensor_seed("qkvX", M), device=DEV)
+        Ys = [y.clone() for y in fg.fp4_gemv_grouped(G, X)]
+        again = fg.fp4_gemv_grouped(G, X)
+        for (W, host), Y, Y2 in zip(mats, Ys, again):
+            assert torch.equal(Y, Y2)
+            check_product(Y, host, bits(X), rows=sample_rows(W.d_out, 128, seed=M))
+            single = fg.fp4_skinny_gemm(W, X)
+            scale = single.abs().max().item()
+            assert (single - Y).abs().max().item() <= 1e-5 * scale
+
+
 # ---- the workloads at full size (sampled rows where the oracle would be slow) -----------
 
 
