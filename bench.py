@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--cpu-sample-layers", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"],
+                    help="kernel path of the NVFP4/MXFP4 products (auto: MFMA from M = 3 on)")
     ap.add_argument("--engine", default="launches", choices=["stream", "launches"],
                     help="stream: one persistent launch per step (fp4_stream_run); launches: one launch per product")
     return ap.parse_args()
@@ -194,7 +196,7 @@ def copies_for(nbytes, min_total=1 << 30):
     return max(1, -(-min_total // nbytes))
 
 
-def build_other(name, M, fg, datagen, torch):
+def build_other(name, M, fg, datagen, torch, path=0):
     dev = "cuda"
     H, F = datagen.HIDDEN, datagen.FFN
     keep = []
@@ -226,12 +228,12 @@ def build_other(name, M, fg, datagen, torch):
                 ws.append(fg.pack(fg.NVFP4, m["codes"], m["scales"]))
             keep += ws
             Wg, Wu, Wd = ws
-            step.add("gate_up_silu", (lambda Wg=Wg, Wu=Wu: fg.fp4_gate_up_silu(Wg, Wu, X, h)),
+            step.add("gate_up_silu", (lambda Wg=Wg, Wu=Wu: fg.fp4_gate_up_silu(Wg, Wu, X, h, path=path)),
                      2 * fg.packed_bytes(fg.NVFP4, F, H) + M * H * 2 + M * F * 2)
-            if M == 1:
+            if M == 1 and path == fg.PATH_AUTO:
                 fn = (lambda Wd=Wd: fg.fp4_gemv(Wd, h.view(-1), y.view(-1)))
             else:
-                fn = (lambda Wd=Wd: fg.fp4_skinny_gemm(Wd, h, y))
+                fn = (lambda Wd=Wd: fg.fp4_skinny_gemm(Wd, h, y, path=path))
             step.add("down", fn, algorithmic_gemv_bytes(fg, fg.NVFP4, H, F, M))
         what = "dense MLP" if name == "c2" else "speculative-verify MLP"
         return step, keep, f"{what}, NVFP4 gate/up 17408x5120 + SiLU*mul, down 5120x17408, M={M} ({R} copies rotated)", \
@@ -378,7 +380,8 @@ def main():
             step = sstep
             dominant = "decode_stream"
     else:
-        step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch)
+        path = {"auto": fg.PATH_AUTO, "valu": fg.PATH_VALU, "mfma": fg.PATH_MFMA}[args.path]
+        step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch, path)
     bytes_per_step = step.bytes() / step.steps_per_replay
     engine = args.engine if args.workload == "c3" else "launches"
     # one eager pass allocates the workspace and checks every launch
@@ -431,7 +434,7 @@ def main():
         "vs_baseline": None,
         "dtype": "e2m1/e4m3 weights x bf16 -> f32",
         "data": "synthetic (seeded; weights and activations resident in HBM)",
-        "config": {"workload": workload, "M": M, "engine": engine, "bytes_per_step": bytes_per_step,
+        "config": {"workload": workload, "M": M, "engine": engine, "path": args.path, "bytes_per_step": bytes_per_step,
                    "launches_per_step": len(step.calls), "setup_s": round(setup_s, 1)},
         "roofline": {
             "bound": "hbm",

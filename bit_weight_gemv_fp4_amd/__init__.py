@@ -105,7 +105,7 @@ _SIGNATURES = {
     "fp4g_workspace_bytes": (_U64, [_I32, _VP, _I32]),
     "fp4_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP, _VP, _U64, _VP]),
     "fp4_skinny_gemm": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32, _VP, _U64, _VP]),
-    "fp4_gemv_grouped": (_I32, [ctypes.POINTER(GroupDesc), _VP, _I32, ctypes.POINTER(_VP), _VP, _U64, _VP]),
+    "fp4_gemv_grouped": (_I32, [ctypes.POINTER(GroupDesc), _VP, _I32, ctypes.POINTER(_VP), _I32, _VP, _U64, _VP]),
     "fp4_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32,
                                 _VP, _U64, _VP]),
     "moe_route_gemv": (_I32, [ctypes.POINTER(MoeDesc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _U64, _VP]),
@@ -314,7 +314,7 @@ class Group:
             self.desc.w[i] = W.desc
 
 
-def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, ws=None, stream=None):
+def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, path: int = PATH_AUTO, ws=None, stream=None):
     """Ys[i][m] = W_i X[m] for every member W_i of G, X bf16 [M, d_in] (or [d_in]);
     returns the list of float32 [M, d_out_i] outputs."""
     X2 = X if X.dim() == 2 else X.view(1, -1)
@@ -323,7 +323,7 @@ def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, ws=None, stream=None):
         Ys = [torch.empty((M, W.d_out), dtype=torch.float32, device=X.device) for W in G.members]
     ptrs = (_VP * len(Ys))(*[y.data_ptr() for y in Ys])
     wsb, need = _workspace(OP_GROUPED, G, M, X.device, ws)
-    _check(lib().fp4_gemv_grouped(ctypes.byref(G.desc), _bits(X2), M, ptrs, _ptr(wsb),
+    _check(lib().fp4_gemv_grouped(ctypes.byref(G.desc), _bits(X2), M, ptrs, path, _ptr(wsb),
                                   wsb.numel() if wsb is not None else 0, _stream(stream)), "fp4_gemv_grouped")
     return Ys
 

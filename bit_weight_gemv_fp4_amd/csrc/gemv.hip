@@ -1,7 +1,7 @@
 // gemv.hip -- launch planning, host-side validation and the product entry points
 // fp4_gemv, fp4_skinny_gemm, fp4_gemv_grouped, fp4_gate_up_silu and
 // fp8_lmhead_gemv.  The kernel itself is in gemv_kernel.hpp.
-#include "gemv_kernel.hpp"
+#include "gemv_mfma.hpp"
 
 namespace fp4g {
 
@@ -12,6 +12,28 @@ extern template hipError_t launch_m<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvPara
 extern template hipError_t launch_m<FP4G_MXFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, const GemvParams&, unsigned, hipStream_t);
+// Matrix-core launchers (gemv_mfma.hpp), in gemv_mfma_nvfp4.hip and gemv_mfma_mxfp4.hip.
+extern template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
+extern template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
+extern template hipError_t launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
+extern template hipError_t launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
+
+// AUTO takes the matrix cores from this many vectors on (below it the VALU
+// kernel's dot products keep up with HBM).
+constexpr int kMfmaMinM = 3;
+
+// The kernel path a call runs: FP8 rows always take the VALU kernel.
+static bool use_mfma(int32_t path, uint32_t format, int M) {
+  if (format == FP4G_FP8_ROW) return false;
+  if (path == FP4G_PATH_MFMA) return true;
+  if (path == FP4G_PATH_VALU) return false;
+  return M >= kMfmaMinM;
+}
+
+static bool valid_path(int32_t path, bool fp4) {
+  if (path == FP4G_PATH_AUTO || path == FP4G_PATH_VALU) return true;
+  return path == FP4G_PATH_MFMA && fp4;
+}
 
 // Workspace check shared by every entry point: NULL only when nothing is needed,
 // large enough, 256-B aligned.
@@ -25,7 +47,7 @@ static fp4g_status check_ws(const void* ws, uint64_t ws_bytes, uint64_t need) {
 // Validation + launch of n products of one input (n = 1: fp4_gemv,
 // fp4_skinny_gemm, fp8_lmhead_gemv).  Members share format and d_in.
 static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, const uint16_t* X, int32_t M,
-                         float* const* Y, void* ws, uint64_t ws_bytes, void* stream) {
+                         float* const* Y, int32_t path, void* ws, uint64_t ws_bytes, void* stream) {
   if (n < 1 || n > kMaxGroup) return FP4G_E_SHAPE;
   for (int i = 0; i < n; ++i) {
     const fp4g_status st = check_weight(W[i], want_fp4);
@@ -45,7 +67,9 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   int64_t R_total = 0;
   for (int i = 0; i < n; ++i) R_total += row_groups(W[i]->d_out);
   const int64_t C = chunks(W[0]->d_in);
-  const uint64_t need = gemv_ws_bytes(R_total, C, 1, M);
+  if (!valid_path(path, want_fp4)) return FP4G_E_PATH;
+  const bool mfma = use_mfma(path, W[0]->format, M);
+  const uint64_t need = gemv_ws_bytes_any(R_total, C, 1, M);
   const fp4g_status wst = check_ws(ws, ws_bytes, need);
   if (wst != FP4G_OK) return wst;
   const size_t xbytes = (size_t)M * W[0]->d_in * 2;
@@ -59,7 +83,7 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
       if (j > i && overlap(Y[i], yb, Y[j], (size_t)M * W[j]->d_out * 4)) return FP4G_E_ALIAS;
     }
   }
-  const Plan pl = plan_for(R_total, C, 1);
+  const Plan pl = mfma ? plan_mfma(R_total, C, 1, M) : plan_for(R_total, C, 1);
   GemvParams p{};
   p.n = n;
   int64_t gb = 0;
@@ -81,7 +105,10 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   const unsigned grid = (unsigned)(R_total * pl.S);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (W[0]->format == FP4G_NVFP4)
+  if (mfma)
+    e = W[0]->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, M), s)
+                                   : launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, M), s);
+  else if (W[0]->format == FP4G_NVFP4)
     e = launch_m<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, s);
   else if (W[0]->format == FP4G_MXFP4)
     e = launch_m<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, s);
@@ -90,10 +117,10 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 
-static int32_t run_gemv(const fp4g_weight* W, bool want_fp4, const uint16_t* X, int32_t M, float* Y, void* ws,
-                        uint64_t ws_bytes, void* stream) {
+static int32_t run_gemv(const fp4g_weight* W, bool want_fp4, const uint16_t* X, int32_t M, float* Y, int32_t path,
+                        void* ws, uint64_t ws_bytes, void* stream) {
   if (!W) return FP4G_E_NULL;
-  return run_group(&W, 1, want_fp4, X, M, &Y, ws, ws_bytes, stream);
+  return run_group(&W, 1, want_fp4, X, M, &Y, path, ws, ws_bytes, stream);
 }
 
 static fp4g_status check_group(const fp4g_group* G) {
@@ -109,28 +136,27 @@ using namespace fp4g;
 extern "C" {
 
 int32_t fp4_gemv(const fp4g_weight* W, const uint16_t* x, float* y, void* ws, uint64_t ws_bytes, void* stream) {
-  return run_gemv(W, true, x, 1, y, ws, ws_bytes, stream);
+  return run_gemv(W, true, x, 1, y, FP4G_PATH_AUTO, ws, ws_bytes, stream);
 }
 
 int32_t fp4_skinny_gemm(const fp4g_weight* W, const uint16_t* X, int32_t M, float* Y, int32_t path, void* ws,
                         uint64_t ws_bytes, void* stream) {
-  if (path != FP4G_PATH_AUTO && path != FP4G_PATH_VALU) return FP4G_E_PATH;
-  return run_gemv(W, true, X, M, Y, ws, ws_bytes, stream);
+  return run_gemv(W, true, X, M, Y, path, ws, ws_bytes, stream);
 }
 
-int32_t fp4_gemv_grouped(const fp4g_group* G, const uint16_t* X, int32_t M, float* const* Y, void* ws,
-                         uint64_t ws_bytes, void* stream) {
+int32_t fp4_gemv_grouped(const fp4g_group* G, const uint16_t* X, int32_t M, float* const* Y, int32_t path,
+                         void* ws, uint64_t ws_bytes, void* stream) {
   const fp4g_status st = check_group(G);
   if (st != FP4G_OK) return st;
   if (!Y) return FP4G_E_NULL;
   const fp4g_weight* W[kMaxGroup];
   for (int i = 0; i < G->n; ++i) W[i] = &G->w[i];
-  return run_group(W, G->n, true, X, M, Y, ws, ws_bytes, stream);
+  return run_group(W, G->n, true, X, M, Y, path, ws, ws_bytes, stream);
 }
 
 int32_t fp8_lmhead_gemv(const fp4g_weight* W, const uint16_t* X, int32_t M, float* logits, void* ws,
                         uint64_t ws_bytes, void* stream) {
-  return run_gemv(W, false, X, M, logits, ws, ws_bytes, stream);
+  return run_gemv(W, false, X, M, logits, FP4G_PATH_AUTO, ws, ws_bytes, stream);
 }
 
 int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uint16_t* X, int32_t M, uint16_t* H,
@@ -143,10 +169,11 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   if (Wg->d_out != Wu->d_out || Wg->d_in != Wu->d_in) return FP4G_E_SHAPE;
   if (!X || !H) return FP4G_E_NULL;
   if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
-  if (path != FP4G_PATH_AUTO && path != FP4G_PATH_VALU) return FP4G_E_PATH;
+  if (!valid_path(path, true)) return FP4G_E_PATH;
   if (!aligned(X, 16) || !aligned(H, 16)) return FP4G_E_ALIGN;
+  const bool mfma = use_mfma(path, Wg->format, M);
   const int64_t R = row_groups(Wg->d_out), C = chunks(Wg->d_in);
-  const uint64_t need = gemv_ws_bytes(R, C, 2, M);
+  const uint64_t need = gemv_ws_bytes_any(R, C, 2, M);
   st = check_ws(ws, ws_bytes, need);
   if (st != FP4G_OK) return st;
   const size_t hbytes = (size_t)M * Wg->d_out * 2, xbytes = (size_t)M * Wg->d_in * 2;
@@ -155,7 +182,7 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
       overlap(ws, need, X, xbytes) || overlap(ws, need, Wg->packed, Wg->packed_bytes) ||
       overlap(ws, need, Wu->packed, Wu->packed_bytes))
     return FP4G_E_ALIAS;
-  const Plan pl = plan_for(R, C, 2);
+  const Plan pl = mfma ? plan_mfma(R, C, 2, M) : plan_for(R, C, 2);
   GemvParams p{};
   p.n = 1;
   p.w[0] = (const uint8_t*)Wg->packed;
@@ -174,8 +201,13 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   p.wg_chunks = pl.wg_chunks;
   const unsigned grid = (unsigned)(R * pl.S);
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = Wg->format == FP4G_NVFP4 ? launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, s)
-                                          : launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, s);
+  hipError_t e;
+  if (mfma)
+    e = Wg->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, M), s)
+                                 : launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, M), s);
+  else
+    e = Wg->format == FP4G_NVFP4 ? launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, s)
+                                 : launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 
@@ -191,13 +223,13 @@ uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
       if (G->w[i].format != G->w[0].format || G->w[i].d_in != G->w[0].d_in) return 0;
       R += row_groups(G->w[i].d_out);
     }
-    return gemv_ws_bytes(R, chunks(G->w[0].d_in), 1, M);
+    return gemv_ws_bytes_any(R, chunks(G->w[0].d_in), 1, M);
   }
   const fp4g_weight* W = (const fp4g_weight*)desc;
   const bool fp4 = op != FP4G_OP_LMHEAD;
   if (op != FP4G_OP_GEMV && op != FP4G_OP_GATE_UP && op != FP4G_OP_LMHEAD) return 0;
   if (check_weight(W, fp4) != FP4G_OK) return 0;
-  return gemv_ws_bytes(row_groups(W->d_out), chunks(W->d_in), op == FP4G_OP_GATE_UP ? 2 : 1, M);
+  return gemv_ws_bytes_any(row_groups(W->d_out), chunks(W->d_in), op == FP4G_OP_GATE_UP ? 2 : 1, M);
 }
 
 }  // extern "C"

@@ -175,6 +175,57 @@ __device__ __forceinline__ void dec_unit(unsigned long long v, float& a, float& 
   b = __uint_as_float((uint32_t)(v >> 32));
 }
 
+// Split-K across workgroups: a binary tree of exchanges over the S workgroups
+// of a row group.  At each level the two subtrees of a node swap their sums into
+// the node's slot; the first to arrive deposits, the second receives the first's
+// sum in the same round trip, adds (a + b == b + a, so the result does not
+// depend on who is second) and carries on; an unpaired last node passes up.  One
+// device-scope atomic round trip per level; slots are left zero.  Units still
+// live afterwards hold the full sums.  Slot of (node, unit, lane_slot):
+// slots[(node * NU + unit) * unit_stride + lane_slot].
+template <int NU>
+__device__ __forceinline__ void exchange_tree(unsigned long long* __restrict__ slots, int64_t unit_stride,
+                                              int64_t lane_slot, int S, int s, float (&ua)[NU], float (&ub)[NU],
+                                              bool (&live)[NU]) {
+  int node_off = 0, n = S, idx = s;
+  while (n > 1) {
+    if ((idx ^ 1) < n) {
+      unsigned long long* base = slots + ((int64_t)(node_off + (idx >> 1)) * NU) * unit_stride + lane_slot;
+      unsigned long long old[NU];
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+        old[u] = live[u] ? __hip_atomic_exchange(base + u * unit_stride, enc_unit(ua[u], ub[u]), __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                         : 0ull;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (!live[u]) continue;
+        if (old[u] == 0ull) {
+          live[u] = false;  // deposited: the partner carries the pair sum on
+        } else {
+          float oa, ob;
+          dec_unit(old[u], oa, ob);
+          ua[u] = oa + ua[u];
+          ub[u] = ob + ub[u];
+          __hip_atomic_store(base + u * unit_stride, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    node_off += n >> 1;
+    n = (n + 1) >> 1;
+    idx >>= 1;
+  }
+}
+
+// Row group of a grouped launch: member index and its local row group.
+__device__ __forceinline__ int member_of(const GemvParams& p, int gt) {
+  int mem = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i)
+    if (i < p.n && gt >= p.gbase[i]) mem = i;
+  return mem;
+}
+
 // Epilogue for unit u of one row of member `mem` (row local to that member).
 template <uint32_t FMT, int M, int NMAT, int EPI>
 __device__ __forceinline__ void finish_unit(const GemvParams& p, int mem, int row, int u, float a, float b) {
@@ -206,12 +257,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
   const int wave = wave_id();
   const int gt = uniform(blockIdx.x / p.S);  // global row group
   const int s = uniform(blockIdx.x % p.S);
-  int mem = 0;
-  if constexpr (NMAT == 1) {
-#pragma unroll
-    for (int i = 1; i < kMaxGroup; ++i)
-      if (i < p.n && gt >= p.gbase[i]) mem = i;
-  }
+  const int mem = NMAT == 1 ? member_of(p, gt) : 0;
   const int g = gt - p.gbase[mem];
   const uint8_t* w0 = p.w[mem];
   const uint8_t* w1 = NMAT == 2 ? p.w[1] : w0;
@@ -302,45 +348,10 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
     }
   }
   const int row = g * 64 + lane;
-  // Split-K: a binary tree of exchanges.  At each level the two subtrees of a
-  // node swap their sums into the node's slot; the first to arrive deposits, the
-  // second receives the first's sum in the same round trip, adds (a + b == b + a,
-  // so the result does not depend on who is second) and carries on.  One
-  // device-scope atomic round trip per level; slots are left zero.
   bool live[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) live[u] = true;
-  const int64_t unit_stride = (int64_t)p.gbase[p.n] * 64;  // slots per (node, unit)
-  // level l has n nodes; node idx pairs with idx ^ 1, an unpaired last one passes up
-  int node_off = 0, n = p.S, idx = s;
-  while (n > 1) {
-    if ((idx ^ 1) < n) {
-      unsigned long long* base =
-          p.slots + ((int64_t)(node_off + (idx >> 1)) * NU) * unit_stride + (int64_t)gt * 64 + lane;
-      unsigned long long old[NU];
-#pragma unroll
-      for (int u = 0; u < NU; ++u)
-        old[u] = live[u] ? __hip_atomic_exchange(base + u * unit_stride, enc_unit(ua[u], ub[u]), __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                         : 0ull;
-#pragma unroll
-      for (int u = 0; u < NU; ++u) {
-        if (!live[u]) continue;
-        if (old[u] == 0ull) {
-          live[u] = false;  // deposited: the partner carries the pair sum on
-        } else {
-          float oa, ob;
-          dec_unit(old[u], oa, ob);
-          ua[u] = oa + ua[u];
-          ub[u] = ob + ub[u];
-          __hip_atomic_store(base + u * unit_stride, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-    node_off += n >> 1;
-    n = (n + 1) >> 1;
-    idx >>= 1;
-  }
+  exchange_tree<NU>(p.slots, (int64_t)p.gbase[p.n] * 64, (int64_t)gt * 64 + lane, p.S, s, ua, ub, live);
 #pragma unroll
   for (int u = 0; u < NU; ++u)
     if (live[u]) finish_unit<FMT, M, NMAT, EPI>(p, mem, row, u, ua[u], ub[u]);

@@ -79,9 +79,12 @@ typedef enum {
 
 typedef enum { FP4G_NVFP4 = 1, FP4G_MXFP4 = 2, FP4G_FP8_ROW = 3 } fp4g_format;
 
-/* Kernel path for the M = 2..8 verify products.  AUTO lets the library choose;
- * VALU forces the vector-ALU kernels; MFMA forces the matrix-core kernels and is
- * refused with FP4G_E_PATH where none exists. */
+/* Kernel path of the NVFP4/MXFP4 products.  VALU: one v_dot2 per weight pair and
+ * vector.  MFMA: the products on the matrix cores (bf16 MFMA on exact bf16
+ * weights; block scales applied per block in FP32).  AUTO takes MFMA from M = 3
+ * on and VALU below.  FP8 rows have only the VALU kernel: MFMA is refused there
+ * with FP4G_E_PATH.  Both paths give the same results up to the order of the
+ * FP32 additions. */
 typedef enum { FP4G_PATH_AUTO = 0, FP4G_PATH_VALU = 1, FP4G_PATH_MFMA = 2 } fp4g_path;
 
 /* Operation ids for fp4g_workspace_bytes. */
@@ -218,10 +221,10 @@ int32_t fp4_skinny_gemm(const fp4g_weight* W_host, const uint16_t* X_dev, int32_
 /* Several products of one input in one launch: Y_dev[i][m][r] = sum_k
  * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..8.  X_dev: bf16
  * [M][d_in]; Y_dev: host array of G->n device pointers, each f32 [M][w_i.d_out],
- * 16-B aligned and disjoint.  Each member's results are those of fp4_skinny_gemm
- * on it alone up to the order of the FP32 additions. */
+ * 16-B aligned and disjoint.  path: fp4g_path.  Each member's results are those
+ * of fp4_skinny_gemm on it alone up to the order of the FP32 additions. */
 int32_t fp4_gemv_grouped(const fp4g_group* G_host, const uint16_t* X_dev, int32_t M,
-                         float* const* Y_host, void* ws_dev, uint64_t ws_bytes, void* stream);
+                         float* const* Y_host, int32_t path, void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* Fused MLP front half: g = Wg X_m, u = Wu X_m, H_dev[m][r] = bf16_rne(SiLU(g[r]) *
  * u[r]) with SiLU(z) = z / (1 + e^-z), for m < M in 1..8.  Wg and Wu are NVFP4 or

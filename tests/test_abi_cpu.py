@@ -104,8 +104,8 @@ def test_skinny_and_lmhead_error_paths():
     X, Y = FAKE + (1 << 30), FAKE + (2 << 30)
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 0, Y, 0, None, 0, None) == E_SHAPE
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 9, Y, 0, None, 0, None) == E_SHAPE
-    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, fg.PATH_MFMA, None, 0, None) == E_PATH
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, 7, None, 0, None) == E_PATH
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, -1, None, 0, None) == E_PATH
     assert L.fp8_lmhead_gemv(ctypes.byref(d), X, 1, Y, None, 0, None) == E_FORMAT  # NVFP4 given
     f8 = good_desc(fmt=fg.FP8_ROW)
     assert L.fp8_lmhead_gemv(ctypes.byref(f8), X, 9, Y, None, 0, None) == E_SHAPE
@@ -120,17 +120,17 @@ def group_desc(*members):
     return G
 
 
-def call_grouped(G, M=1, x=FAKE + (1 << 30), ys=None, ws=None, wsb=0):
+def call_grouped(G, M=1, x=FAKE + (1 << 30), ys=None, ws=None, wsb=0, path=0):
     if ys is None:
         ys = [FAKE + ((2 + i) << 30) for i in range(max(G.n, 1))]
     arr = (ctypes.c_void_p * len(ys))(*ys)
-    return fg.lib().fp4_gemv_grouped(ctypes.byref(G), x, M, arr, ws, wsb, None)
+    return fg.lib().fp4_gemv_grouped(ctypes.byref(G), x, M, arr, path, ws, wsb, None)
 
 
 def test_grouped_error_paths():
     L = fg.lib()
     q = good_desc(d_out=128); k = good_desc(d_out=64); k.packed = FAKE + (8 << 30)
-    assert L.fp4_gemv_grouped(None, FAKE, 1, None, None, 0, None) == E_NULL
+    assert L.fp4_gemv_grouped(None, FAKE, 1, None, 0, None, 0, None) == E_NULL
     assert call_grouped(group_desc()) == E_SHAPE                       # n = 0
     G = group_desc(q, k); G.n = 5
     assert call_grouped(G) == E_SHAPE                                  # n > 4
@@ -145,7 +145,8 @@ def test_grouped_error_paths():
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (3 << 30) + 4]) == E_ALIGN
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (2 << 30) + 256]) == E_ALIAS
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (8 << 30) + 512]) == E_ALIAS  # into k's weights
-    assert fg.lib().fp4_gemv_grouped(ctypes.byref(group_desc(q, k)), FAKE, 1, None, None, 0, None) == E_NULL
+    assert fg.lib().fp4_gemv_grouped(ctypes.byref(group_desc(q, k)), FAKE, 1, None, 0, None, 0, None) == E_NULL
+    assert call_grouped(group_desc(q, k), path=7) == E_PATH
     # QKV-shaped group: more row groups than any member, so split-K workspace
     qq = good_desc(d_out=5120, d_in=5120); kk = good_desc(d_out=1024, d_in=5120); kk.packed = FAKE + (8 << 30)
     G = group_desc(qq, kk)
@@ -164,7 +165,7 @@ def test_gate_up_error_paths():
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u2), X, 1, H, 0, None, 0, None) == E_SHAPE
     u3 = good_desc(fmt=fg.MXFP4)
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u3), X, 1, H, 0, None, 0, None) == E_FORMAT
-    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, fg.PATH_MFMA, None, 0, None) == E_PATH
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, 3, None, 0, None) == E_PATH
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, None, 0, None, 0, None) == E_NULL
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, X, 0, None, 0, None) == E_ALIAS
 

@@ -132,14 +132,18 @@ def test_gemv_tensor_scale():
         check_product(fg.fp4_gemv(W, x), host, bits(x)[None, :])
 
 
-@pytest.mark.parametrize("M", [2, 3, 4, 8])
+PATHS = [fg.PATH_VALU, fg.PATH_MFMA]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
-def test_skinny_matches_oracle(fmt, M):
-    log("skinny", fmt, M)
+def test_skinny_matches_oracle(fmt, M, path):
+    log("skinny", fmt, M, path)
     for shape in ((200, 1056), (5120, 5120)):
         W, host = make(fmt, *shape, seed=3)
         X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("X", M, shape), device=DEV)
-        Y = fg.fp4_skinny_gemm(W, X)
+        Y = fg.fp4_skinny_gemm(W, X, path=path)
         check_product(Y, host, bits(X))
 
 
@@ -168,15 +172,16 @@ def check_h(H_gpu, gate, up, X_bits, rows=None):
     assert not bad.any(), f"{bad.sum()} h values out of bound"
 
 
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8])
 @pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
-def test_gate_up_silu_matches_oracle(fmt, M):
-    log("gate_up", fmt, M)
+def test_gate_up_silu_matches_oracle(fmt, M, path):
+    log("gate_up", fmt, M, path)
     for shape in ((200, 1056), (130, 544)):
         Wg, hg = make(fmt, *shape, seed=5)
         Wu, hu = make(fmt, *shape, seed=6)
         X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("Xg", M, shape), device=DEV)
-        H = fg.fp4_gate_up_silu(Wg, Wu, X)
+        H = fg.fp4_gate_up_silu(Wg, Wu, X, path=path)
         check_h(H, hg, hu, bits(X))
 
 
@@ -225,15 +230,46 @@ def test_sign_flip_and_determinism():
     assert torch.equal(fg.fp4_gemv(W, -x), -y1)
 
 
+def exact_scales(fmt, shape, gen):
+    """Power-of-two block scales (0.5, 1, 2 or 4): with x in {-1, 0, 1} every
+    partial sum is a multiple of 1/4 below 2^19, so any summation order is exact
+    and every path must return the oracle's value bit for bit -- also where a
+    scale is applied to the wrong row or block."""
+    n = shape[0] * (shape[1] // (16 if fmt == fg.NVFP4 else 32))
+    pick = torch.randint(0, 4, (n,), generator=gen, device=DEV)
+    if fmt == fg.NVFP4:  # E4M3 2^e: bits (e + 7) << 3
+        codes = ((pick + 6) << 3).to(torch.uint8)
+    else:  # E8M0 2^e: e + 127
+        codes = (pick + 126).to(torch.uint8)
+    return codes.view(shape[0], -1)
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_exact_sums_with_mixed_scales(fmt, path):
+    log("exact mixed scales", fmt, path)
+    for shape in ((130, 1056), (200, 5120), (64, 17408)):
+        gen = torch.Generator(DEV).manual_seed(shape[0] + shape[1])
+        mat = datagen.matrix(fmt, *shape, datagen.tensor_seed("exact", fmt, shape), device=DEV)
+        sc = exact_scales(fmt, shape, gen)
+        W = fg.pack(fmt, mat["codes"], sc)
+        for M in (1, 3, 4, 5, 8):
+            X = torch.randint(-1, 2, (M, shape[1]), generator=gen, device=DEV).to(torch.bfloat16)
+            Y, _ = oracle.gemv(fmt, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
+            got = fg.fp4_skinny_gemm(W, X, path=path)
+            assert np.array_equal(got.cpu().double().numpy(), Y), (shape, M)
+
+
 # ---- split-K exchange tree and grouped launches ----------------------------------------------
 
 
-@pytest.mark.parametrize("M", [1, 2, 3])
-def test_split_k_tree_exact_for_every_split_count(M):
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("M", [1, 2, 3, 8])
+def test_split_k_tree_exact_for_every_split_count(M, path):
     """Exact-sum inputs (scales 1.0, x in {-1,0,1}) at widths that give 2..63
     workgroups per row group, power of two or not: every tree shape must return
     the exact sum, bit for bit, and a second call the same bits."""
-    log("tree exact", M)
+    log("tree exact", M, path)
     for C in (8, 12, 20, 28, 36, 60, 124, 252):
         d_out, d_in = 130, 256 * C
         mat = datagen.matrix(fg.NVFP4, d_out, d_in, datagen.tensor_seed("tree", C), device=DEV)
@@ -242,22 +278,23 @@ def test_split_k_tree_exact_for_every_split_count(M):
         g = torch.Generator(DEV).manual_seed(C * 10 + M)
         X = torch.randint(-1, 2, (M, d_in), generator=g, device=DEV).to(torch.bfloat16)
         Y, _ = oracle.gemv(fg.NVFP4, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
-        got = fg.fp4_skinny_gemm(W, X).clone()
+        got = fg.fp4_skinny_gemm(W, X, path=path).clone()
         assert np.array_equal(got.cpu().double().numpy(), Y), C
-        assert torch.equal(fg.fp4_skinny_gemm(W, X), got), C
+        assert torch.equal(fg.fp4_skinny_gemm(W, X, path=path), got), C
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 3, 8])
 @pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
-def test_grouped_matches_oracle(fmt, M):
+def test_grouped_matches_oracle(fmt, M, path):
     """Ragged members (1, 70, 200 and 64 rows) of one input in one launch."""
-    log("grouped", fmt, M)
+    log("grouped", fmt, M, path)
     shapes = [(70, 1056), (1, 1056), (200, 1056), (64, 1056)]
     mats = [make(fmt, o, i, seed=("grp", j)) for j, (o, i) in enumerate(shapes)]
     X = datagen.bf16_normal((M, 1056), datagen.tensor_seed("grpX", M), device=DEV)
     for n in (1, 2, 4):
         G = fg.Group([W for W, _ in mats[:n]])
-        Ys = fg.fp4_gemv_grouped(G, X)
+        Ys = fg.fp4_gemv_grouped(G, X, path=path)
         for (W, host), Y in zip(mats[:n], Ys):
             check_product(Y, host, bits(X))
 
@@ -292,16 +329,17 @@ def test_config1_gemv_5120():
     check_product(fg.fp4_gemv(W, x), host, bits(x)[None, :])
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
-def test_config2_and_4_mlp(M):
+def test_config2_and_4_mlp(M, path):
     """Dense MLP: gate/up 17408x5120 fused with SiLU*mul, then down 5120x17408."""
-    log("C2/C4 MLP", M)
+    log("C2/C4 MLP", M, path)
     Wg, hg = make(fg.NVFP4, 17408, 5120, seed=200)
     Wu, hu = make(fg.NVFP4, 17408, 5120, seed=201)
     Wd, hd = make(fg.NVFP4, 5120, 17408, seed=202)
     X = datagen.bf16_normal((M, 5120), datagen.tensor_seed("C2x", M), device=DEV)
-    H = fg.fp4_gate_up_silu(Wg, Wu, X)
-    Y = fg.fp4_skinny_gemm(Wd, H) if M > 1 else fg.fp4_gemv(Wd, H.view(-1)).view(1, -1)
+    H = fg.fp4_gate_up_silu(Wg, Wu, X, path=path)
+    Y = fg.fp4_skinny_gemm(Wd, H, path=path)
     rows = sample_rows(17408, 160, seed=M)
     check_h(H, hg, hu, bits(X), rows=rows)
     drows = sample_rows(5120, 160, seed=M + 10)
