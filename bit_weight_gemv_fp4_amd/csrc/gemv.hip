@@ -7,11 +7,11 @@ namespace fp4g {
 
 // Per-format launchers (gemv_kernel.hpp), instantiated in gemv_nvfp4.hip,
 // gemv_mxfp4.hip and gemv_fp8.hip.
-extern template hipError_t launch_m<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, hipStream_t);
-extern template hipError_t launch_m<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, hipStream_t);
-extern template hipError_t launch_m<FP4G_MXFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, hipStream_t);
-extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, hipStream_t);
-extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_NVFP4, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_NVFP4, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_MXFP4, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 // Matrix-core launchers (gemv_mfma.hpp), in gemv_mfma_nvfp4.hip and gemv_mfma_mxfp4.hip.
 extern template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
 extern template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
@@ -83,7 +83,7 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
       if (j > i && overlap(Y[i], yb, Y[j], (size_t)M * W[j]->d_out * 4)) return FP4G_E_ALIAS;
     }
   }
-  const Plan pl = mfma ? plan_mfma(R_total, C, 1, M) : plan_for(R_total, C, 1);
+  const Plan pl = mfma ? plan_mfma(R_total, C, 1, M) : plan_for(R_total, C, 1, M);
   GemvParams p{};
   p.n = n;
   int64_t gb = 0;
@@ -109,11 +109,11 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
     e = W[0]->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, M), s)
                                    : launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, M), s);
   else if (W[0]->format == FP4G_NVFP4)
-    e = launch_m<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, s);
+    e = launch_m<FP4G_NVFP4, 1, EPI_STORE>(M, pl.nw, p, grid, s);
   else if (W[0]->format == FP4G_MXFP4)
-    e = launch_m<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, s);
+    e = launch_m<FP4G_MXFP4, 1, EPI_STORE>(M, pl.nw, p, grid, s);
   else
-    e = launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(M, p, grid, s);
+    e = launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(M, pl.nw, p, grid, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 
@@ -182,7 +182,7 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
       overlap(ws, need, X, xbytes) || overlap(ws, need, Wg->packed, Wg->packed_bytes) ||
       overlap(ws, need, Wu->packed, Wu->packed_bytes))
     return FP4G_E_ALIAS;
-  const Plan pl = mfma ? plan_mfma(R, C, 2, M) : plan_for(R, C, 2);
+  const Plan pl = mfma ? plan_mfma(R, C, 2, M) : plan_for(R, C, 2, M);
   GemvParams p{};
   p.n = 1;
   p.w[0] = (const uint8_t*)Wg->packed;
@@ -206,8 +206,8 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
     e = Wg->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, M), s)
                                  : launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, M), s);
   else
-    e = Wg->format == FP4G_NVFP4 ? launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, s)
-                                 : launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, s);
+    e = Wg->format == FP4G_NVFP4 ? launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s)
+                                 : launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 

@@ -247,11 +247,11 @@ __device__ __forceinline__ void finish_unit(const GemvParams& p, int mem, int ro
   }
 }
 
-template <uint32_t FMT, int M, int NMAT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
+template <uint32_t FMT, int M, int NMAT, int EPI, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
   constexpr int NA = NMAT * M;
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : FMT == FP4G_MXFP4 ? kTileMx : kTileF8;
-  __shared__ float red[kWavesPerWg][NA][64];
+  __shared__ float red[NW][NA][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -263,9 +263,9 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
   const uint8_t* w1 = NMAT == 2 ? p.w[1] : w0;
   const int wg_c0 = s * p.wg_chunks;
   const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
-  const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
-  const int c0 = min(wg_c1, wg_c0 + wave * per_wave);
-  const int c1 = min(wg_c1, c0 + per_wave);
+  // the workgroup's chunks split as evenly as possible over its NW waves
+  const int c0 = wg_c0 + (wave * (wg_c1 - wg_c0)) / NW;
+  const int c1 = wg_c0 + ((wave + 1) * (wg_c1 - wg_c0)) / NW;
 
   float acc[NMAT][M];
 #pragma unroll
@@ -332,7 +332,12 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
 
   float v[NA];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) v[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+  for (int i = 0; i < NA; ++i) {
+    float t = red[0][i][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += red[w][i][lane];
+    v[i] = t;
+  }
 
   // units: EPI_STORE (v[2u], v[2u+1]); EPI_SILU (gate v[u], up v[M+u])
   constexpr int NU = EPI == EPI_SILU ? M : (M + 1) / 2;
@@ -357,30 +362,40 @@ __global__ __launch_bounds__(kThreads) void k_gemv(GemvParams p) {
     if (live[u]) finish_unit<FMT, M, NMAT, EPI>(p, mem, row, u, ua[u], ub[u]);
 }
 
+template <uint32_t FMT, int M, int NMAT, int EPI>
+hipError_t launch_nw(int nw, const GemvParams& p, unsigned grid, hipStream_t s) {
+  switch (nw) {
+    case 4: k_gemv<FMT, M, NMAT, EPI, 4><<<grid, 256, 0, s>>>(p); break;
+    case 8: k_gemv<FMT, M, NMAT, EPI, 8><<<grid, 512, 0, s>>>(p); break;
+    case 16: k_gemv<FMT, M, NMAT, EPI, 16><<<grid, 1024, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <uint32_t FMT, int NMAT, int EPI>
-hipError_t launch_m(int M, const GemvParams& p, unsigned grid, hipStream_t s) {
+hipError_t launch_m(int M, int nw, const GemvParams& p, unsigned grid, hipStream_t s) {
   switch (M) {
 #define FP4G_CASE(MM) \
   case MM:            \
-    k_gemv<FMT, MM, NMAT, EPI><<<grid, kThreads, 0, s>>>(p); \
-    break;
+    return launch_nw<FMT, MM, NMAT, EPI>(nw, p, grid, s);
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
 #undef FP4G_CASE
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // ---- launch planning -----------------------------------------------------------
 struct Plan {
   int S;          // workgroups per row group
   int wg_chunks;  // chunks per workgroup
+  int nw;         // waves per workgroup
 };
 
-// Enough waves to cover HBM latency on all 256 CUs (about eight per CU), with at
-// least one chunk per wave; chunks are spread evenly over the S workgroups.
-inline Plan plan_for(int64_t R, int64_t C, int nmat) {
-  (void)nmat;
+// Four-wave workgroups: enough waves to cover HBM latency on all 256 CUs (about
+// eight per CU), with at least one chunk per wave; chunks spread evenly over the
+// S workgroups.  (The MoE and matrix-core kernels use this split.)
+inline Plan plan_nw4(int64_t R, int64_t C) {
   const int64_t target_waves = 2048;
   int64_t q = (R * C) / target_waves;  // chunks per wave
   if (q < 1) q = 1;
@@ -388,7 +403,49 @@ inline Plan plan_for(int64_t R, int64_t C, int nmat) {
   if (S < 1) S = 1;
   const int64_t wg_chunks = (C + S - 1) / S;
   S = (C + wg_chunks - 1) / wg_chunks;
-  return Plan{(int)S, (int)wg_chunks};
+  return Plan{(int)S, (int)wg_chunks, kWavesPerWg};
+}
+
+inline int tree_depth(int64_t S) {
+  int d = 0;
+  for (int64_t n = S; n > 1; n = (n + 1) / 2) ++d;
+  return d;
+}
+
+// VALU kernel: 4, 8 or 16 waves per workgroup and S workgroups per row group.
+// Workgroups go round-robin to the 256 CUs, so the busiest CU gets ceil(WGs /
+// 256) of them while the average CU needs WGs / 256: the plan minimises that
+// imbalance, times 1 + 3% per level of the split-K tree (one device-scope round
+// trip each), times 1 + 15% per extra round of waves beyond what the CUs hold at
+// once (16 waves per CU while the kernel needs at most 128 VGPRs: NMAT * M up to
+// 5 for plain products, M up to 3 fused; 12 above).  No more than a quarter of a
+// workgroup's waves may be left without a chunk; ties go to more waves.  (The
+// weights are fitted to timings of the dense-model shapes on MI355X.)
+constexpr int kCUs = 256;
+inline Plan plan_for(int64_t R, int64_t C, int nmat, int M) {
+  const int waves_per_cu = (nmat == 1 ? M <= 5 : M <= 3) ? 16 : 12;
+  Plan best = plan_nw4(R, C);
+  double best_cost = 1e30;
+  int64_t best_waves = 0;
+  for (int nw : {4, 8, 16}) {
+    if (nw > waves_per_cu) continue;
+    for (int64_t S0 = 1; S0 <= C; ++S0) {
+      const int64_t wg_chunks = (C + S0 - 1) / S0;
+      const int64_t S = (C + wg_chunks - 1) / wg_chunks;
+      if (S != S0) continue;              // each S once
+      if (4 * wg_chunks < 3 * nw) break;  // more than a quarter of the waves idle
+      const int64_t wgs = R * S, waves = wgs * nw;
+      const double imbalance = (double)((wgs + kCUs - 1) / kCUs) * kCUs / (double)wgs;
+      const double rounds = (double)waves / ((double)kCUs * waves_per_cu);
+      const double cost = imbalance * (1.0 + 0.03 * tree_depth(S)) * (1.0 + 0.15 * (rounds > 1.0 ? rounds - 1.0 : 0.0));
+      if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && waves > best_waves)) {
+        best = Plan{(int)S, (int)wg_chunks, nw};
+        best_cost = cost;
+        best_waves = waves;
+      }
+    }
+  }
+  return best;
 }
 
 inline uint64_t align256(uint64_t b) { return (b + 255) & ~uint64_t(255); }
@@ -406,7 +463,7 @@ inline int64_t exchange_units(int nmat, int M) { return nmat == 2 ? M : (M + 1) 
 
 // Exchange slots: tree nodes x units x all rows of all members, 8 bytes each.
 inline uint64_t gemv_ws_bytes(int64_t R_total, int64_t C, int nmat, int M) {
-  const Plan pl = plan_for(R_total, C, nmat);
+  const Plan pl = plan_for(R_total, C, nmat, M);
   if (pl.S == 1) return 0;
   return (uint64_t)tree_nodes(pl.S) * exchange_units(nmat, M) * R_total * 64 * 8;
 }

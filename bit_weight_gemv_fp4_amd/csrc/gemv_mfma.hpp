@@ -282,13 +282,14 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
 // The VALU plan, with S raised where needed so that a workgroup's staged input
 // (M rows of its chunk range) fits the LDS budget.
 inline Plan plan_mfma(int64_t R, int64_t C, int nmat, int M) {
-  Plan pl = plan_for(R, C, nmat);
+  (void)nmat;
+  Plan pl = plan_nw4(R, C);
   const int64_t max_chunks = kMfmaXBytes / (M * 512);
   if (pl.wg_chunks > max_chunks) {
     int64_t S = (C + max_chunks - 1) / max_chunks;
     const int64_t wg_chunks = (C + S - 1) / S;
     S = (C + wg_chunks - 1) / wg_chunks;
-    pl = Plan{(int)S, (int)wg_chunks};
+    pl = Plan{(int)S, (int)wg_chunks, kWavesPerWg};
   }
   return pl;
 }
@@ -305,7 +306,7 @@ inline int64_t exchange_units_any(int nmat, int M) {
 
 // Workspace for either kernel (the caller may choose the path per call).
 inline uint64_t gemv_ws_bytes_any(int64_t R_total, int64_t C, int nmat, int M) {
-  const Plan a = plan_for(R_total, C, nmat), b = plan_mfma(R_total, C, nmat, M);
+  const Plan a = plan_for(R_total, C, nmat, M), b = plan_mfma(R_total, C, nmat, M);
   const int64_t nodes = tree_nodes(a.S) > tree_nodes(b.S) ? tree_nodes(a.S) : tree_nodes(b.S);
   return (uint64_t)nodes * exchange_units_any(nmat, M) * R_total * 64 * 8;
 }

@@ -339,8 +339,8 @@ MoeLayout moe_layout(const fp4g_moe* mo, int M) {
   L.Cg = chunks(mo->hidden);
   L.Rd = row_groups(mo->hidden);
   L.Cd = chunks(mo->d_ff);
-  L.up = plan_for(L.Rg * L.n_slots_max, L.Cg, 2);
-  L.dn = plan_for(L.Rd * L.n_slots_max, L.Cd, 1);
+  L.up = plan_nw4(L.Rg * L.n_slots_max, L.Cg);
+  L.dn = plan_nw4(L.Rd * L.n_slots_max, L.Cd);
   // counters first (the fixed region), then tables and partial sums
   L.off_cnt_up = 0;
   L.off_cnt_dn = 4ull * L.n_slots_max * L.Rg;
