@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
-    ap.add_argument("--cpu-sample-layers", type=int, default=2)
+    ap.add_argument("--cpu-sample-layers", type=int, default=24,
+                    help="full layers the CPU oracle runs for cpu_baseline (about 0.45 s each on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"],

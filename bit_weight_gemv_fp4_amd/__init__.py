@@ -258,17 +258,24 @@ _ws_cache: dict = {}
 
 def _workspace(op, desc, M, device, ws):
     """A zero-filled workspace of the size the call needs.  The library leaves its
-    counters at zero after every call, so a per-device buffer is reused; calls that
-    share it must be ordered on one stream (pass `ws` otherwise)."""
+    exchange slots at zero after every call, so a per-device buffer is reused by
+    all products; MoE layers get one per layer shape (they keep tables there too).
+    Calls that share a workspace must be ordered on one stream (pass `ws`
+    otherwise)."""
     need = workspace_bytes(op, desc, M)
     if ws is not None:
         return ws, need
     if need == 0:
         return None, 0
-    key = torch.device(device)
+    dev = torch.device(device)
+    key = dev
+    if op == OP_MOE:
+        # MoE keeps tables after its slots: one workspace per layer shape
+        d = desc.desc
+        key = (dev, "moe", d.num_experts, d.top_k, d.hidden, d.d_ff, d.has_shared, d.gate.format)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < need:
-        buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=key)
+        buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = buf
     return buf, need
 

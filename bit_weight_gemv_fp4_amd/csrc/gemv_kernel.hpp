@@ -27,6 +27,8 @@
 //    and V projections of a layer) share one launch; each row group knows its
 //    member from the group's row-group offsets.
 #pragma once
+#include <initializer_list>
+
 #include "common.hpp"
 
 namespace fp4g {
@@ -162,6 +164,33 @@ __device__ __forceinline__ void tile_dot(const Frag<FMT>& f, const uint32_t* __r
   }
 }
 
+// Double-buffered stream over n_items tiles: the tile of item it+1 is in flight
+// while item it is consumed.  The loop body always has both fragments' loads in
+// flight, so the wait before each consume is a fixed "all but the newest
+// fragment" count (loads complete in order); the last one or two items are
+// peeled off so that no load is conditional.  tile_of(it) is the tile address of
+// item it, eat(fragment, it) consumes it.
+template <uint32_t FMT, class TileOf, class Eat>
+__device__ __forceinline__ void stream_items(int n_items, int lane, TileOf tile_of, Eat eat) {
+  if (n_items <= 0) return;
+  Frag<FMT> fa, fb;
+  load_frag<FMT>(fa, tile_of(0), lane);
+  int it = 0;
+  for (; it + 2 < n_items; it += 2) {
+    load_frag<FMT>(fb, tile_of(it + 1), lane);
+    eat(fa, it);
+    load_frag<FMT>(fa, tile_of(it + 2), lane);
+    eat(fb, it + 1);
+  }
+  if (it + 1 < n_items) {
+    load_frag<FMT>(fb, tile_of(it + 1), lane);
+    eat(fa, it);
+    eat(fb, it + 1);
+  } else {
+    eat(fa, it);
+  }
+}
+
 // Split-K results travel as 64-bit units: EPI_STORE packs the values of tokens
 // 2u and 2u+1, EPI_SILU the (gate, up) pair of token u.  Encoding: low word =
 // bits(a) + 1, high word = bits(b), so that 0 (a zero-filled slot) never
@@ -278,8 +307,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
   const int full_chunks = p.d_in / kChunkK;  // chunks with all 8 pieces present
   const int tail_pieces = (p.d_in % kChunkK) / kPieceK;
 
-  // Items are (chunk, matrix) pairs visited chunk-major.  Two register fragments
-  // alternate: the tile of item it+1 is in flight while item it is consumed.
+  // Items are (chunk, matrix) pairs visited chunk-major.
   const int n_items = (c1 - c0) * NMAT;
   const int64_t tile0 = (int64_t)g * p.C;
   auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE; };
@@ -301,27 +329,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
       for (int m = 0; m < M; ++m) acc[NMAT - 1][m] += part[m];
     }
   };
-  if (n_items > 0) {
-    // The loop body always has both fragments' loads in flight, so the wait before
-    // each consume is a fixed "all but the newest fragment" count; the last one
-    // or two items are peeled off.
-    Frag<FMT> fa, fb;
-    load_frag<FMT>(fa, item_tile(0), lane);
-    int it = 0;
-    for (; it + 2 < n_items; it += 2) {
-      load_frag<FMT>(fb, item_tile(it + 1), lane);
-      consume(fa, it);
-      load_frag<FMT>(fa, item_tile(it + 2), lane);
-      consume(fb, it + 1);
-    }
-    if (it + 1 < n_items) {
-      load_frag<FMT>(fb, item_tile(it + 1), lane);
-      consume(fa, it);
-      consume(fb, it + 1);
-    } else {
-      consume(fa, it);
-    }
-  }
+  stream_items<FMT>(n_items, lane, item_tile, consume);
 
 #pragma unroll
   for (int a = 0; a < NMAT; ++a)
@@ -367,7 +375,12 @@ hipError_t launch_nw(int nw, const GemvParams& p, unsigned grid, hipStream_t s) 
   switch (nw) {
     case 4: k_gemv<FMT, M, NMAT, EPI, 4><<<grid, 256, 0, s>>>(p); break;
     case 8: k_gemv<FMT, M, NMAT, EPI, 8><<<grid, 512, 0, s>>>(p); break;
-    case 16: k_gemv<FMT, M, NMAT, EPI, 16><<<grid, 1024, 0, s>>>(p); break;
+    case 16:
+      if constexpr (NMAT == 1 ? M <= 5 : M <= 3) {  // where plan_for offers 16 waves
+        k_gemv<FMT, M, NMAT, EPI, 16><<<grid, 1024, 0, s>>>(p);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -420,10 +433,11 @@ inline int tree_depth(int64_t S) {
 // once (16 waves per CU while the kernel needs at most 128 VGPRs: NMAT * M up to
 // 5 for plain products, M up to 3 fused; 12 above).  No more than a quarter of a
 // workgroup's waves may be left without a chunk; ties go to more waves.  (The
-// weights are fitted to timings of the dense-model shapes on MI355X.)
+// weights are fitted to timings of the dense-model shapes on MI355X.)  A kernel
+// with more registers passes its own waves_per_cu.
 constexpr int kCUs = 256;
-inline Plan plan_for(int64_t R, int64_t C, int nmat, int M) {
-  const int waves_per_cu = (nmat == 1 ? M <= 5 : M <= 3) ? 16 : 12;
+inline Plan plan_for(int64_t R, int64_t C, int nmat, int M, int waves_per_cu = 0) {
+  if (waves_per_cu == 0) waves_per_cu = (nmat == 1 ? M <= 5 : M <= 3) ? 16 : 12;
   Plan best = plan_nw4(R, C);
   double best_cost = 1e30;
   int64_t best_waves = 0;
@@ -439,6 +453,36 @@ inline Plan plan_for(int64_t R, int64_t C, int nmat, int M) {
       const double rounds = (double)waves / ((double)kCUs * waves_per_cu);
       const double cost = imbalance * (1.0 + 0.03 * tree_depth(S)) * (1.0 + 0.15 * (rounds > 1.0 ? rounds - 1.0 : 0.0));
       if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && waves > best_waves)) {
+        best = Plan{(int)S, (int)wg_chunks, nw};
+        best_cost = cost;
+        best_waves = waves;
+      }
+    }
+  }
+  return best;
+}
+
+// Small products (a few thousand tiles, such as the experts a token picked) are
+// bound by the chain of round trips in each wave, not by bandwidth: this plan
+// minimises the rounds of workgroups times the chunks each wave streams in
+// turn, plus half a chunk per level of the split-K tree; among equals the
+// fewest waves.  nws lists the workgroup sizes the kernel is built for.
+inline Plan plan_latency(int64_t R, int64_t C, int waves_per_cu, std::initializer_list<int> nws) {
+  Plan best = plan_nw4(R, C);
+  double best_cost = 1e30;
+  int64_t best_waves = 0;
+  for (int nw : nws) {
+    if (nw > waves_per_cu) continue;
+    for (int64_t S0 = 1; S0 <= C; ++S0) {
+      const int64_t wg_chunks = (C + S0 - 1) / S0;
+      const int64_t S = (C + wg_chunks - 1) / wg_chunks;
+      if (S != S0) continue;
+      const int64_t waves = R * S * nw;
+      const int64_t per_round = (int64_t)kCUs * (waves_per_cu / nw) * nw;
+      const int64_t rounds = (waves + per_round - 1) / per_round;
+      const int64_t per_wave = (wg_chunks + nw - 1) / nw;
+      const double cost = (double)(rounds * per_wave) + 0.5 * tree_depth(S);
+      if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && waves < best_waves)) {
         best = Plan{(int)S, (int)wg_chunks, nw};
         best_cost = cost;
         best_waves = waves;

@@ -13,15 +13,22 @@
 //             the (slot, 64-row group, K split) its block index names.  Slots are
 //             the union's experts in ascending id, then the shared expert.
 //             Workgroups past the realised union exit before reading a byte, so
-//             only the union's gate/up bytes stream.  The last workgroup of a
-//             (slot, row group) writes h = bf16(SiLU(gate x) * (up x)) for all M
-//             tokens to the workspace.  Workgroup 0 also writes the routing
-//             tables.
-//  k_moe_down Each (slot, 64-row group of the hidden size, K split) streams the
-//             expert's down projection against its h, multiplies by the token's
-//             gate weight (1 for the shared expert, 0 for tokens that did not pick
-//             it), and the last of all slots' workgroups of a row group sums the
-//             partial outputs in slot order into Y.
+//             only the union's gate/up bytes stream.  The K splits of a (slot,
+//             row group) meet in the split-K exchange tree, and the survivor
+//             writes h = bf16(SiLU(gate x) * (up x)) for all M tokens to the
+//             workspace.  Workgroup 0 also writes the routing tables: the slots'
+//             experts and, per (slot, token), the gate weight times the down
+//             matrix's tensor scale (0 for a token that did not pick the expert,
+//             1 x scale for the shared expert).
+//  k_moe_down Each workgroup owns one 64-row group of the hidden size and a
+//             share of the (slot, chunk) tiles of that row group over all the
+//             union's experts.  Each tile's dot products with the slot's h are
+//             weighted by the slot's coefficients and summed in registers, so the
+//             experts need no combine step; the K shares meet in the exchange
+//             tree, whose survivor writes Y.
+//
+// Both kernels use the tile loop, the split-K tree and the launch planner of the
+// dense product (gemv_kernel.hpp).  Results are deterministic.
 #include <algorithm>
 
 #include "gemv_kernel.hpp"
@@ -46,15 +53,13 @@ struct MoeParams {
   uint16_t* hdbg;        // optional bf16 [M][K + has_shared][dff]
   // workspace
   int* route;            // [0] = number of slots, [1 + i] = expert of slot i (-1 = shared)
-  float* coef;           // [n_slots_max][M] gate weight of token m for slot i
+  float* coef;           // [n_slots_max][M]: gate weight x down tensor scale
   uint16_t* hbuf;        // bf16 [n_slots_max][M][dff]
-  unsigned* cnt_up;      // [n_slots_max * Rg]
-  float* part_up;        // [S_up][n_slots_max][2][M][Rg * 64]
-  unsigned* cnt_dn;      // [Rd]
-  float* part_dn;        // [n_slots_max][S_dn][M][Rd * 64]
+  unsigned long long* x_up;  // exchange slots of the gate/up splits (zero between calls)
+  unsigned long long* x_dn;  // exchange slots of the down splits (zero between calls)
   int n_slots_max;
   int Rg, Cg, S_up, wg_up;  // gate/up: d_ff rows, hidden columns
-  int Rd, Cd, S_dn, wg_dn;  // down: hidden rows, d_ff columns
+  int Rd, Cd, S_dn;         // down: hidden rows, d_ff columns; S_dn shares of the tiles
 };
 
 // Shared routing state of one workgroup.
@@ -68,46 +73,79 @@ struct RouteLds {
   int n_slots;
 };
 
-// (v, i) beats (bv, bi): larger value, or equal value and lower index.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+// Pick order as one 64-bit key: the logit mapped to an unsigned integer of the
+// same order (sign bit flipped for positive values, all bits for negative ones)
+// in the high word, the complement of the expert index in the low word.  A
+// larger key is a larger logit, or an equal logit with a lower index (zeros of
+// either sign are equal).  Key 0 is below every logit's key and marks "none".
+__device__ __forceinline__ uint64_t pick_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);  // -0 ranks as +0
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
 
-// All 256 threads: route the M tokens into `r` (ids, weights, sorted union).
-template <int M>
+// One DPP step of the wave maximum: each lane takes the larger of its key and
+// the key `CTRL` names (key 0 where the source lane does not exist).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)k, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(k >> 32), CTRL, ROW_MASK, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+// Maximum key over the 64 lanes, uniform: row_shr 1, 2, 4, 8 leave each 16-lane
+// row's maximum in its lane 15; row_bcast 15 and 31 carry it up to lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max_step<0x111, 0xf>(k);  // row_shr:1
+  k = dpp_max_step<0x112, 0xf>(k);  // row_shr:2
+  k = dpp_max_step<0x114, 0xf>(k);  // row_shr:4
+  k = dpp_max_step<0x118, 0xf>(k);  // row_shr:8
+  k = dpp_max_step<0x142, 0xa>(k);  // row_bcast:15 into rows 1 and 3
+  k = dpp_max_step<0x143, 0xc>(k);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// All NW * 64 threads: route the M tokens into `r` (ids, weights, sorted union).
+template <int M, int NW>
 __device__ void route_tokens(const MoeParams& p, RouteLds<M>& r) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int words = (p.E + 31) / 32;
-  for (int i = threadIdx.x; i < words; i += kThreads) r.bits[i] = 0u;
+  for (int i = threadIdx.x; i < words; i += NW * 64) r.bits[i] = 0u;
   const int per_lane = (p.E + 63) / 64;  // <= 16
-  for (int m = wave; m < M; m += kWavesPerWg) {
+  for (int m = wave; m < M; m += NW) {
     const float* lg = p.logits + (int64_t)m * p.E;
-    unsigned left = 0;  // bit t set: element lane + 64 t still available
-    for (int t = 0; t < per_lane; ++t)
-      if (lane + 64 * t < p.E) left |= 1u << t;
-    for (int j = 0; j < p.K; ++j) {
-      float bv = -__builtin_inff();
-      int bi = 0x7fffffff;
-      for (int t = 0; t < per_lane; ++t) {
-        if (!((left >> t) & 1u)) continue;
-        const int e = lane + 64 * t;
-        const float v = lg[e];
-        if (better(v, e, bv, bi)) {
-          bv = v;
-          bi = e;
-        }
-      }
+    // the lane's pick keys (experts lane + 64 t) in registers, from one load
+    // round trip; a picked key becomes 0
+    constexpr int kPer = kMaxExperts / 64;
+    uint64_t key[kPer];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
+    for (int t = 0; t < kPer; ++t) {
+      const int e = lane + 64 * t;
+      key[t] = (t < per_lane && e < p.E) ? pick_key(lg[e], e) : 0ull;
+    }
+    const bool wide = per_lane > kPer / 2;  // uniform: more than 512 experts
+    for (int j = 0; j < p.K; ++j) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int t = 1; t < kPer / 2; ++t) best = key[t] > best ? key[t] : best;
+      if (wide) {
+#pragma unroll
+        for (int t = kPer / 2; t < kPer; ++t) best = key[t] > best ? key[t] : best;
       }
-      if (bi != 0x7fffffff && (bi & 63) == lane) left &= ~(1u << (bi >> 6));
+      best = wave_max_key(best);
+#pragma unroll
+      for (int t = 0; t < kPer; ++t) key[t] = key[t] == best ? 0ull : key[t];
       if (lane == 0) {
-        r.ids[m][j] = bi;
-        r.v[m][j] = bv;
+        r.ids[m][j] = key_index(best);
+        r.v[m][j] = key_value(best);
       }
     }
     if (lane == 0) {
@@ -163,24 +201,25 @@ __device__ __forceinline__ float coef_of(const RouteLds<M>& r, const MoeParams& 
   return c;
 }
 
-template <uint32_t FMT, int M>
-__global__ __launch_bounds__(kThreads) void k_moe_up(MoeParams p) {
+template <uint32_t FMT, int M, int NW>
+__global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : kTileMx;
   constexpr int NA = 2 * M;
   __shared__ RouteLds<M> r;
-  __shared__ float red[kWavesPerWg][NA][64];
-  route_tokens<M>(p, r);
+  __shared__ float red[NW][NA][64];
+  route_tokens<M, NW>(p, r);
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < M * p.K; i += kThreads) {
+    for (int i = threadIdx.x; i < M * p.K; i += NW * 64) {
       const int m = i / p.K, j = i % p.K;
       p.topk_ids[i] = r.ids[m][j];
       p.topk_w[i] = r.w[m][j];
     }
-    for (int i = threadIdx.x; i < r.n_slots; i += kThreads) {
+    for (int i = threadIdx.x; i < r.n_slots; i += NW * 64) {
       p.route[1 + i] = r.uni[i];
-      for (int m = 0; m < M; ++m) p.coef[i * M + m] = coef_of<M>(r, p, i, m);
+      const float tsd = r.uni[i] >= 0 ? p.ts_down : p.ts_sh_down;
+      for (int m = 0; m < M; ++m) p.coef[i * M + m] = coef_of<M>(r, p, i, m) * tsd;
     }
     if (threadIdx.x == 0) p.route[0] = r.n_slots;
   }
@@ -197,8 +236,8 @@ __global__ __launch_bounds__(kThreads) void k_moe_up(MoeParams p) {
   const float tsu = e >= 0 ? p.ts_up : p.ts_sh_up;
 
   const int wg_c0 = s * p.wg_up, wg_c1 = min(p.Cg, wg_c0 + p.wg_up);
-  const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
-  const int c0 = min(wg_c1, wg_c0 + wave * per_wave), c1 = min(wg_c1, c0 + per_wave);
+  const int c0 = wg_c0 + (wave * (wg_c1 - wg_c0)) / NW;
+  const int c1 = wg_c0 + ((wave + 1) * (wg_c1 - wg_c0)) / NW;
   const uint32_t* __restrict__ x32 = reinterpret_cast<const uint32_t*>(p.x);
   const int xstride = p.hidden / 2;
   const int full_chunks = p.hidden / kChunkK, tail_pieces = (p.hidden % kChunkK) / kPieceK;
@@ -209,50 +248,57 @@ __global__ __launch_bounds__(kThreads) void k_moe_up(MoeParams p) {
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[a][m] = 0.0f;
-  for (int c = c0; c < c1; ++c) {
-    Frag<FMT> fg, fu;
-    load_frag<FMT>(fg, wg_ + (tile0 + c) * TILE, lane);
-    load_frag<FMT>(fu, wu_ + (tile0 + c) * TILE, lane);
+  // items (chunk, matrix) chunk-major: even items gate, odd items up
+  auto tile_of = [&](int it) { return (it & 1 ? wu_ : wg_) + (tile0 + c0 + it / 2) * TILE; };
+  auto eat = [&](const Frag<FMT>& f, int it) {
+    const int c = c0 + it / 2;
     const uint32_t* xc = x32 + (int64_t)c * (kChunkK / 2);
-    if (c < full_chunks) {
-      tile_dot<FMT, M, true>(fg, xc, xstride, kPiecesNv, acc[0]);
-      tile_dot<FMT, M, true>(fu, xc, xstride, kPiecesNv, acc[1]);
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.0f;
+    if (c < full_chunks)
+      tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, part);
+    else
+      tile_dot<FMT, M, false>(f, xc, xstride, tail_pieces, part);
+    if ((it & 1) == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[0][m] += part[m];
     } else {
-      tile_dot<FMT, M, false>(fg, xc, xstride, tail_pieces, acc[0]);
-      tile_dot<FMT, M, false>(fu, xc, xstride, tail_pieces, acc[1]);
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[1][m] += part[m];
     }
-  }
+  };
+  stream_items<FMT>((c1 - c0) * 2, lane, tile_of, eat);
+
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int m = 0; m < M; ++m) red[wave][a * M + m][lane] = acc[a][m];
   __syncthreads();
   if (wave != 0) return;
-  float v[NA];
+  float ua[M], ub[M];
+  bool live[M];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) v[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
-  const int row = g * 64 + lane;
-  if (p.S_up > 1) {
-    const int64_t rpad = (int64_t)p.Rg * 64;
-    float* base = p.part_up + ((int64_t)s * p.n_slots_max + slot) * NA * rpad;
+  for (int m = 0; m < M; ++m) {
+    float tg = red[0][m][lane], tu = red[0][M + m][lane];
 #pragma unroll
-    for (int i = 0; i < NA; ++i) publish_partial(base + i * rpad + row, v[i]);
-    unsigned* cnt = p.cnt_up + slot * p.Rg + g;
-    if (!arrive_last(cnt, (unsigned)(p.S_up - 1))) return;
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      float t = 0.0f;
-      for (int q = 0; q < p.S_up; ++q)
-        t += collect_partial(p.part_up + (((int64_t)q * p.n_slots_max + slot) * NA + i) * rpad + row);
-      v[i] = t;
+    for (int w = 1; w < NW; ++w) {
+      tg += red[w][m][lane];
+      tu += red[w][M + m][lane];
     }
-    reset_counter(cnt);
+    ua[m] = tg;
+    ub[m] = tu;
+    live[m] = true;
   }
+  const int row = g * 64 + lane;
+  exchange_tree<M>(p.x_up, (int64_t)p.n_slots_max * p.Rg * 64, ((int64_t)slot * p.Rg + g) * 64 + lane, p.S_up, s,
+                   ua, ub, live);
   if (row >= p.dff) return;
   const int nh = p.K + p.has_shared;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const uint16_t h = f32_to_bf16_rne(silu_f32(v[m] * tsg) * (v[M + m] * tsu));
+    if (!live[m]) continue;
+    const uint16_t h = f32_to_bf16_rne(silu_f32(ua[m] * tsg) * (ub[m] * tsu));
     p.hbuf[((int64_t)slot * M + m) * p.dff + row] = h;
     if (p.hdbg) {
       if (e < 0) {
@@ -265,25 +311,17 @@ __global__ __launch_bounds__(kThreads) void k_moe_up(MoeParams p) {
   }
 }
 
-template <uint32_t FMT, int M>
-__global__ __launch_bounds__(kThreads) void k_moe_down(MoeParams p) {
+template <uint32_t FMT, int M, int NW>
+__global__ __launch_bounds__(NW * 64) void k_moe_down(MoeParams p) {
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : kTileMx;
-  __shared__ float red[kWavesPerWg][M][64];
+  __shared__ float red[NW][M][64];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int n_slots = uniform(p.route[0]);
-  const int per_slot = p.Rd * p.S_dn;
-  const int slot = uniform(blockIdx.x / per_slot);
-  if (slot >= n_slots) return;
-  const int rem = blockIdx.x % per_slot;
-  const int g = uniform(rem / p.S_dn), s = uniform(rem % p.S_dn);
-  const int e = uniform(p.route[1 + slot]);
-  const uint8_t* wd = e >= 0 ? p.down + (uint64_t)e * p.sd : p.sh_down;
-  const float tsd = e >= 0 ? p.ts_down : p.ts_sh_down;
-
-  const int wg_c0 = s * p.wg_dn, wg_c1 = min(p.Cd, wg_c0 + p.wg_dn);
-  const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
-  const int c0 = min(wg_c1, wg_c0 + wave * per_wave), c1 = min(wg_c1, c0 + per_wave);
-  const uint32_t* __restrict__ x32 = reinterpret_cast<const uint32_t*>(p.hbuf + (int64_t)slot * M * p.dff);
+  const int g = uniform(blockIdx.x / p.S_dn), s = uniform(blockIdx.x % p.S_dn);
+  // this workgroup's share of the row group's (slot, chunk) tiles, then the wave's
+  const int total = n_slots * p.Cd;
+  const int w0 = (int)(((int64_t)s * total) / p.S_dn), w1 = (int)(((int64_t)(s + 1) * total) / p.S_dn);
+  const int i0 = w0 + (wave * (w1 - w0)) / NW, i1 = w0 + ((wave + 1) * (w1 - w0)) / NW;
   const int xstride = p.dff / 2;
   const int full_chunks = p.dff / kChunkK, tail_pieces = (p.dff % kChunkK) / kPieceK;
   const int64_t tile0 = (int64_t)g * p.Cd;
@@ -291,37 +329,56 @@ __global__ __launch_bounds__(kThreads) void k_moe_down(MoeParams p) {
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
-  for (int c = c0; c < c1; ++c) {
-    Frag<FMT> f;
-    load_frag<FMT>(f, wd + (tile0 + c) * TILE, lane);
-    const uint32_t* xc = x32 + (int64_t)c * (kChunkK / 2);
+  auto tile_of = [&](int it) {
+    const int q = i0 + it, slot = q / p.Cd, c = q - slot * p.Cd;
+    const int e = p.route[1 + slot];
+    const uint8_t* wd = e >= 0 ? p.down + (uint64_t)e * p.sd : p.sh_down;
+    return wd + (tile0 + c) * TILE;
+  };
+  auto eat = [&](const Frag<FMT>& f, int it) {
+    const int q = i0 + it, slot = q / p.Cd, c = q - slot * p.Cd;
+    const uint32_t* xc =
+        reinterpret_cast<const uint32_t*>(p.hbuf + (int64_t)slot * M * p.dff) + (int64_t)c * (kChunkK / 2);
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.0f;
     if (c < full_chunks)
-      tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, acc);
+      tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, part);
     else
-      tile_dot<FMT, M, false>(f, xc, xstride, tail_pieces, acc);
-  }
+      tile_dot<FMT, M, false>(f, xc, xstride, tail_pieces, part);
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(part[m], p.coef[slot * M + m], acc[m]);
+  };
+  stream_items<FMT>(i1 - i0, lane, tile_of, eat);
+
 #pragma unroll
   for (int m = 0; m < M; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
   if (wave != 0) return;
-  const int row = g * 64 + lane;
-  const int64_t rpad = (int64_t)p.Rd * 64;
-  float* base = p.part_dn + ((int64_t)slot * p.S_dn + s) * M * rpad;
+  constexpr int NU = (M + 1) / 2;
+  float ua[NU], ub[NU];
+  bool live[NU];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const float v = ((red[0][m][lane] + red[1][m][lane]) + red[2][m][lane]) + red[3][m][lane];
-    publish_partial(base + m * rpad + row, v * tsd * p.coef[slot * M + m]);
-  }
-  if (!arrive_last(p.cnt_dn + g, (unsigned)(n_slots * p.S_dn - 1))) return;
-  if (row < p.hidden) {
+  for (int u = 0; u < NU; ++u) {
+    float ta = red[0][2 * u][lane], tb = 2 * u + 1 < M ? red[0][2 * u + 1][lane] : 0.0f;
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float t = 0.0f;
-      for (int q = 0; q < n_slots * p.S_dn; ++q) t += collect_partial(p.part_dn + ((int64_t)q * M + m) * rpad + row);
-      p.y[(int64_t)m * p.hidden + row] = t;
+    for (int w = 1; w < NW; ++w) {
+      ta += red[w][2 * u][lane];
+      if (2 * u + 1 < M) tb += red[w][2 * u + 1][lane];
     }
+    ua[u] = ta;
+    ub[u] = tb;
+    live[u] = true;
   }
-  reset_counter(p.cnt_dn + g);
+  exchange_tree<NU>(p.x_dn, (int64_t)p.Rd * 64, (int64_t)g * 64 + lane, p.S_dn, s, ua, ub, live);
+  const int row = g * 64 + lane;
+  if (row >= p.hidden) return;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (!live[u]) continue;
+    p.y[(int64_t)(2 * u) * p.hidden + row] = ua[u];
+    if (2 * u + 1 < M) p.y[(int64_t)(2 * u + 1) * p.hidden + row] = ub[u];
+  }
 }
 
 // ---- host side ------------------------------------------------------------------
@@ -329,39 +386,55 @@ struct MoeLayout {
   int n_slots_max;
   int64_t Rg, Cg, Rd, Cd;
   Plan up, dn;
-  uint64_t off_route, off_coef, off_hbuf, off_cnt_up, off_part_up, off_cnt_dn, off_part_dn, total;
+  uint64_t off_route, off_coef, off_hbuf, off_x_up, off_x_dn, total;
 };
+
+// Both kernels stream a few thousand tiles at most and are bound by each wave's
+// chain of round trips (routing, loads, tree): latency plans.  The routing code
+// takes k_moe_up past 128 VGPRs (12 waves per CU): workgroups of 4, 8 or 12
+// waves.  k_moe_down fits 16 waves per CU up to M = 5, like the dense kernel.
+constexpr int kUpWavesPerCu = 12;
+inline Plan plan_up(int64_t R, int64_t C) { return plan_latency(R, C, kUpWavesPerCu, {4, 8, 12}); }
+inline Plan plan_dn(int64_t R, int64_t C, int M) { return plan_latency(R, C, M <= 5 ? 16 : 12, {4, 8, 16}); }
+
+// Workspace: exchange slots first, sized for the largest need over M = 1..8
+// (they must start zero-filled and every call leaves them zero), then the
+// routing tables and h at an offset that does not depend on M: calls of any M on
+// one layer shape can share a workspace without their tables ever landing in
+// another call's slots.
+int n_slots_for(const fp4g_moe* mo, int M) {
+  return std::min(mo->num_experts, M * mo->top_k) + (mo->has_shared ? 1 : 0);
+}
 
 MoeLayout moe_layout(const fp4g_moe* mo, int M) {
   MoeLayout L{};
-  L.n_slots_max = std::min(mo->num_experts, M * mo->top_k) + (mo->has_shared ? 1 : 0);
+  L.n_slots_max = n_slots_for(mo, M);
   L.Rg = row_groups(mo->d_ff);
   L.Cg = chunks(mo->hidden);
   L.Rd = row_groups(mo->hidden);
   L.Cd = chunks(mo->d_ff);
-  L.up = plan_nw4(L.Rg * L.n_slots_max, L.Cg);
-  L.dn = plan_nw4(L.Rd * L.n_slots_max, L.Cd);
-  // counters first (the fixed region), then tables and partial sums
-  L.off_cnt_up = 0;
-  L.off_cnt_dn = 4ull * L.n_slots_max * L.Rg;
-  uint64_t o = kCounterBytes;
+  L.up = plan_up(L.Rg * L.n_slots_max, L.Cg);
+  L.dn = plan_dn(L.Rd, L.Cd * L.n_slots_max, M);
+  uint64_t slot_bytes = 0;
+  for (int m = 1; m <= kMaxM; ++m) {
+    const int ns = n_slots_for(mo, m);
+    const Plan up = plan_up(L.Rg * ns, L.Cg), dn = plan_dn(L.Rd, L.Cd * ns, m);
+    const uint64_t b = align256(8ull * tree_nodes(up.S) * m * ns * L.Rg * 64) +
+                       align256(8ull * tree_nodes(dn.S) * ((m + 1) / 2) * L.Rd * 64);
+    slot_bytes = std::max(slot_bytes, b);
+  }
+  L.off_x_up = 0;
+  L.off_x_dn = align256(8ull * tree_nodes(L.up.S) * M * L.n_slots_max * L.Rg * 64);
+  const int ns8 = n_slots_for(mo, kMaxM);
+  uint64_t o = slot_bytes;
   L.off_route = o;
-  o = align256(o + 4ull * (1 + L.n_slots_max));
+  o = align256(o + 4ull * (1 + ns8));
   L.off_coef = o;
-  o = align256(o + 4ull * L.n_slots_max * M);
+  o = align256(o + 4ull * ns8 * kMaxM);
   L.off_hbuf = o;
-  o = align256(o + 2ull * L.n_slots_max * M * mo->d_ff);
-  L.off_part_up = o;
-  o = align256(o + (L.up.S > 1 ? 4ull * L.up.S * L.n_slots_max * 2 * M * L.Rg * 64 : 0));
-  L.off_part_dn = o;
-  o = align256(o + 4ull * L.n_slots_max * L.dn.S * M * L.Rd * 64);
+  o = align256(o + 2ull * ns8 * kMaxM * mo->d_ff);
   L.total = o;
   return L;
-}
-
-fp4g_status check_moe_counters(const fp4g_moe* mo, int M) {
-  const int64_t slots = std::min(mo->num_experts, M * mo->top_k) + (mo->has_shared ? 1 : 0);
-  return slots * row_groups(mo->d_ff) + row_groups(mo->hidden) <= kMaxCounters ? FP4G_OK : FP4G_E_SHAPE;
 }
 
 fp4g_status check_moe(const fp4g_moe* mo) {
@@ -391,26 +464,48 @@ fp4g_status check_moe(const fp4g_moe* mo) {
   return FP4G_OK;
 }
 
-template <uint32_t FMT>
-hipError_t launch_moe(int M, const MoeParams& p, unsigned grid_up, unsigned grid_dn, hipStream_t s) {
-  switch (M) {
-#define FP4G_CASE(MM)                                           \
-  case MM:                                                      \
-    k_moe_up<FMT, MM><<<grid_up, kThreads, 0, s>>>(p);          \
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure; \
-    k_moe_down<FMT, MM><<<grid_dn, kThreads, 0, s>>>(p);        \
-    break;
-    FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
-#undef FP4G_CASE
+template <uint32_t FMT, int M>
+hipError_t launch_moe_m(const MoeParams& p, const Plan& up, const Plan& dn, unsigned grid_up, unsigned grid_dn,
+                        hipStream_t s) {
+  switch (up.nw) {
+    case 4: k_moe_up<FMT, M, 4><<<grid_up, 256, 0, s>>>(p); break;
+    case 8: k_moe_up<FMT, M, 8><<<grid_up, 512, 0, s>>>(p); break;
+    case 12: k_moe_up<FMT, M, 12><<<grid_up, 768, 0, s>>>(p); break;
+
+    default: return hipErrorInvalidValue;
+  }
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  switch (dn.nw) {
+    case 4: k_moe_down<FMT, M, 4><<<grid_dn, 256, 0, s>>>(p); break;
+    case 8: k_moe_down<FMT, M, 8><<<grid_dn, 512, 0, s>>>(p); break;
+    case 16:
+      if constexpr (M <= 5) {  // and for plain products up to M = 5
+        k_moe_down<FMT, M, 16><<<grid_dn, 1024, 0, s>>>(p);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <uint32_t FMT>
+hipError_t launch_moe(int M, const MoeParams& p, const Plan& up, const Plan& dn, unsigned grid_up, unsigned grid_dn,
+                      hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM) \
+  case MM:            \
+    return launch_moe_m<FMT, MM>(p, up, dn, grid_up, grid_dn, s);
+    FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 uint64_t moe_ws_bytes(const fp4g_moe* mo, int M) {
-  if (check_moe(mo) != FP4G_OK || M < 1 || M > kMaxM || check_moe_counters(mo, M) != FP4G_OK) return 0;
+  if (check_moe(mo) != FP4G_OK || M < 1 || M > kMaxM) return 0;
   return moe_layout(mo, M).total;
 }
 
@@ -425,7 +520,6 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   if (st != FP4G_OK) return st;
   if (!X || !logits || !Y || !topk_ids || !topk_w || !ws) return FP4G_E_NULL;
   if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
-  if (check_moe_counters(mo, M) != FP4G_OK) return FP4G_E_SHAPE;
   if (!aligned(X, 16) || !aligned(logits, 16) || !aligned(Y, 16) || !aligned(topk_ids, 16) ||
       !aligned(topk_w, 16) || (H && !aligned(H, 16)))
     return FP4G_E_ALIGN;
@@ -483,10 +577,8 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   p.route = (int*)(w + L.off_route);
   p.coef = (float*)(w + L.off_coef);
   p.hbuf = (uint16_t*)(w + L.off_hbuf);
-  p.cnt_up = (unsigned*)(w + L.off_cnt_up);
-  p.part_up = (float*)(w + L.off_part_up);
-  p.cnt_dn = (unsigned*)(w + L.off_cnt_dn);
-  p.part_dn = (float*)(w + L.off_part_dn);
+  p.x_up = (unsigned long long*)(w + L.off_x_up);
+  p.x_dn = (unsigned long long*)(w + L.off_x_dn);
   p.n_slots_max = L.n_slots_max;
   p.Rg = (int)L.Rg;
   p.Cg = (int)L.Cg;
@@ -495,11 +587,11 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   p.Rd = (int)L.Rd;
   p.Cd = (int)L.Cd;
   p.S_dn = L.dn.S;
-  p.wg_dn = L.dn.wg_chunks;
   const unsigned grid_up = (unsigned)(L.n_slots_max * L.Rg * L.up.S);
-  const unsigned grid_dn = (unsigned)(L.n_slots_max * L.Rd * L.dn.S);
+  const unsigned grid_dn = (unsigned)(L.Rd * L.dn.S);
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = mo->gate.format == FP4G_NVFP4 ? launch_moe<FP4G_NVFP4>(M, p, grid_up, grid_dn, s)
-                                                     : launch_moe<FP4G_MXFP4>(M, p, grid_up, grid_dn, s);
+  const hipError_t e = mo->gate.format == FP4G_NVFP4
+                           ? launch_moe<FP4G_NVFP4>(M, p, L.up, L.dn, grid_up, grid_dn, s)
+                           : launch_moe<FP4G_MXFP4>(M, p, L.up, L.dn, grid_up, grid_dn, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }

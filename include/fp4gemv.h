@@ -200,8 +200,11 @@ int32_t fp4g_validate(const fp4g_weight* W_host, int64_t* bad_dev, void* stream)
  * partial sums.  The caller zero-fills a workspace once, before its first use;
  * every call leaves the slots and counters at zero again when its kernels
  * complete, so one zero-filled workspace (of the largest size needed) serves
- * calls of any shape.  Calls that share a workspace must be ordered on one
- * stream.  Returns 0 also for invalid arguments. */
+ * calls of any shape.  moe_route_gemv is the exception: it also keeps its
+ * routing tables and intermediate vectors in the workspace, after the slots, so
+ * its workspace may be shared only by moe_route_gemv calls on layers of one
+ * shape (any M), and by nothing else.  Calls that share a workspace must be
+ * ordered on one stream.  Returns 0 also for invalid arguments. */
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc_host, int32_t M);
 
 /* --- products --------------------------------------------------------------- */

@@ -226,6 +226,14 @@ def test_moe_error_paths():
     assert call_moe(m, logits=FAKE + (7 << 32) + 4) == E_ALIGN
 
 
+def test_moe_workspace_does_not_depend_on_m():
+    """MoE tables sit after the exchange slots at an M-independent offset, so calls
+    of any M on one layer shape can share a workspace."""
+    m = moe_desc()
+    sizes = {fg.lib().fp4g_workspace_bytes(fg.OP_MOE, ctypes.byref(m), M) for M in range(1, 9)}
+    assert len(sizes) == 1 and sizes.pop() > 0
+
+
 def test_pack_error_paths():
     L = fg.lib()
     out = fg.WeightDesc()

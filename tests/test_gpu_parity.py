@@ -457,6 +457,7 @@ def test_moe_ties_and_repeat():
     logits = torch.zeros((3, 16), dtype=torch.float32, device=DEV)
     logits[1, 5] = 1.0
     logits[2] = torch.tensor([0.5, -1, 0.5, 0.25] * 4, device=DEV)
+    logits[0, 3] = -0.0  # a negative zero ties with the positive zeros
     ids = check_moe(layer, expert, sh, X, logits, 4)
     assert ids[0].tolist() == [0, 1, 2, 3]
     Y1, _, _ = fg.moe_route_gemv(layer, X, logits)
