@@ -1,560 +1,428 @@
-// stream.hip -- a whole decode step's chain of products in one persistent launch:
+// stream.hip -- a whole decode step's chain of products in one launch:
 // fp4g_stream_workspace_bytes, fp4g_stream_build, fp4_stream_run,
 // fp4g_stream_error.
 //
 // Decoding one token reads every matrix of the model once, one after another
 // (mdjawad.com DGX Spark feed, "Decode speed is bytes divided by bandwidth"), so
 // a decode step is a chain of GEMVs whose only dependence is on activations,
-// never on weights.  Launching each product separately leaves HBM idle at every
-// boundary (kernel ramp-up, the split-K tail and the next kernel's first-byte
-// latency: about 5 us per matrix here).  This kernel keeps HBM busy across the
-// boundaries:
+// never on weights.  Launched one by one, every product pays a kernel boundary
+// (ramp-up, the split-K tail, the compute of the last tiles, the next kernel's
+// first-byte latency).  Here the whole chain is one launch:
 //
-//  * Work items are (op, 64-row group, K range) in op order; wave w of a grid of
-//    G takes items w, w+G, w+2G, ...  An item only waits for items of earlier
-//    ops, which every wave reaches first, so the chain progresses as long as the
-//    grid is resident at once; the grid is sized from the kernel's occupancy.
-//    (A global ticket would serialise: same-address device atomics cost about
-//    11 ns each on this GPU.)
-//  * Every wave streams a flat sequence of weight tiles across its items and
-//    always has the next tile in flight, including the first tile of its next
-//    item before that item's input vector is ready (weights do not depend on
-//    activations).
-//  * An op's input is read only after every row group of the op it waits on has
-//    been finalised (device-scope done counters, eight per op on separate cache
-//    lines so that finalisers do not queue on one address); outputs and partials
-//    are written with device-scope stores.  Each buffer is written once per
-//    launch and first read after it was written, so no cache holds a stale copy.
-//  * Every wait is bounded: on time-out a sticky error flag is set and all waves
-//    drain out; nothing can spin forever.
+//  * One workgroup per work unit (op, 64-row group, K split), units in op order:
+//    the same units, tile loop, split-K exchange tree and epilogues as the
+//    separate launches.
+//  * A unit first puts its first weight tiles in flight, then waits until the
+//    ops it depends on are complete, then stages its input range in LDS and
+//    streams on.  Workgroups are dispatched in index order (per XCD), so the
+//    units of the next op load their weights while the current op finishes --
+//    HBM stays busy across the boundary -- and every wait is for ops whose
+//    units were all dispatched earlier.
+//  * Completion: the split-K survivor of each (lane, unit) reports it on one of
+//    eight 64-bit sub-counters of the op (on separate cache lines) once its
+//    output stores are complete; an op is complete when the reports reach
+//    epoch x (its lane-units), epoch being the number of runs so far (a
+//    one-thread kernel bumps it before each run, so counters never need a reset
+//    and graph replays stay correct).
+//  * Outputs and inputs that cross workgroups use device-scope stores and loads.
+//  * Every wait is bounded: on time-out a sticky error flag is set and the unit
+//    carries on (every unit still runs and reports); nothing spins forever.
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "gemv_kernel.hpp"
 
 namespace fp4g {
 namespace {
 
-constexpr uint32_t kStreamMagic = 0x53344731u;
-constexpr int kSpinLimit = 1 << 20;  // polls of about 1 us each before giving up
-constexpr int kDoneLanes = 8;        // sub-counters per op
-constexpr int kDoneStride = 32;      // u32 between sub-counters (128 B)
+constexpr uint32_t kStreamMagic = 0x53344732u;
+constexpr int kSpinLimit = 1 << 15;   // polls (about 1-2 us each) before giving up
+constexpr int kDoneLanes = 8;         // sub-counters per op
+constexpr int kDoneStride = 16;       // u64 between sub-counters (128 B)
+constexpr int kStreamXBytes = 32768;  // LDS for a unit's staged input
+constexpr int kStreamNW = 4;          // waves per workgroup
 
 enum { SK_GEMV = 0, SK_GATE_UP = 1 };
 
 // One op as the kernel sees it (128 bytes, in the workspace).
 struct StreamOp {
-  const uint8_t* w0;    // packed matrix (gate for GATE_UP)
-  const uint8_t* w1;    // packed up matrix (GATE_UP), else = w0
-  const uint16_t* x;    // bf16 [M][d_in]
-  void* out;            // f32 [M][d_out] or bf16 [M][d_out]
-  const float* rs;      // FP8 row scales, else null
-  float ts0, ts1;       // tensor scales
+  const uint8_t* w0;  // packed matrix (gate for GATE_UP)
+  const uint8_t* w1;  // packed up matrix (GATE_UP), else = w0
+  const uint16_t* x;  // bf16 [M][d_in]
+  void* out;          // f32 [M][d_out] or bf16 [M][d_out]
+  const float* rs;    // FP8 row scales, else null
+  float ts0, ts1;     // tensor scales
   int32_t fmt, kind, d_out, d_in;
-  int32_t R, C, S, Q;   // row groups, chunks, splits, chunks per item
-  int32_t wait_op;      // -1 or an earlier op
-  int32_t item_begin, n_items, nmat;
-  int32_t cnt_base;     // first arrival counter of this op
-  int32_t halves;       // steps per chunk and matrix: 2 for FP8 (8 KiB halves), else 1
-  int64_t part_off;     // float offset of this op's partial sums [S][nmat][M][R*64]
-  int32_t wait_first;   // first op waited for (wait_first .. wait_op)
+  int32_t R, C, S, wg_chunks;
+  int32_t wait_first, wait_op, unit_begin, nu;
+  int64_t slot_off;   // exchange-slot words before this op's slots
+  int64_t expect;     // lane-units this op's survivors report per run (R * 64 * nu)
+  int32_t done_base;  // first of this op's sub-counters
   int32_t pad[3];
 };
 static_assert(sizeof(StreamOp) == 128, "StreamOp is 128 bytes");
 
 struct StreamHdr {
   uint32_t magic;
-  int32_t n_ops, n_items, M, grid, total_cnt;
-  int64_t off_ops, off_done, off_cnt, off_part;
-  int32_t pad0[18];
-  uint32_t unused;      // offset 128
-  int32_t pad1[31];
-  uint32_t exit_count;  // offset 256: waves that finished
-  int32_t pad2[31];
-  int32_t err;          // offset 384: sticky error flag
-  int32_t pad3[31];
+  int32_t n_ops, n_units, M;
+  int64_t off_ops, off_unit_op, off_done, off_slots;
+  int32_t lds_bytes;
+  int32_t pad0[19];
+  uint64_t epoch;  // offset 128: runs so far
+  int32_t pad1[30];
+  int32_t err;     // offset 256: sticky error flag
+  int32_t pad2[63];
 };
 static_assert(sizeof(StreamHdr) == 512, "StreamHdr is 512 bytes");
 
-typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
-
-// Scalar loads of read-only-after-ready data (the op table, an op's input once its
-// producer is done).  Issued in program order with respect to every other
-// memory access of the wave.
-__device__ __forceinline__ const void* uptr(const void* p) {
-  const uint64_t u = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-  return (const void*)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ u32x8 sload8(const void* p) {
-  u32x8 v;
-  const void* q = uptr(p);
-  asm volatile("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q) : "memory");
-  return v;
-}
-
 // Pointers read from the op table are generic; accesses through them are cast to
 // the global address space so that they are issued as global (not FLAT)
-// instructions, which count only in vmcnt and leave scalar-load waits alone.
+// instructions, which count only in vmcnt.
 #define FP4G_GLOBAL __attribute__((address_space(1)))
 __device__ __forceinline__ u32x4 ld_stream_g(const void* p) {
   return __builtin_nontemporal_load((const FP4G_GLOBAL u32x4*)p);
 }
+__device__ __forceinline__ u32x2 ld_stream2_g(const void* p) {
+  return __builtin_nontemporal_load((const FP4G_GLOBAL u32x2*)p);
+}
+__device__ __forceinline__ uint64_t load_dev_u64(const void* p) {
+  return __hip_atomic_load((const FP4G_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_dev_i32(const int* p) {
+  return __hip_atomic_load((const FP4G_GLOBAL int*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void store_dev_f32(void* p, float v) {
   __hip_atomic_store((FP4G_GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_dev_u32(void* p, uint32_t v) {
-  __hip_atomic_store((FP4G_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_dev_u16(void* p, uint16_t v) {
+  __hip_atomic_store((FP4G_GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_f32_g(const float* p) { return *(const FP4G_GLOBAL float*)p; }
-
-__device__ __forceinline__ unsigned atomic_load_dev(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int atomic_load_dev(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  return ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+         __builtin_amdgcn_readfirstlane((uint32_t)v);
 }
 
-// A step: one 8 KiB slab of codes (a whole NVFP4/MXFP4 tile, or half an FP8
-// tile) plus its scales.  Always nine 16-byte loads per lane, whatever the
-// format, so that the wait counts of the pipeline are the same on every path.
-struct StepFrag {
-  u32x4 q[8];
-  u32x4 s;
-};
-
-struct StepDesc {
-  int op;        // -1: no step (end of the stream)
-  int fmt;
-  int g, s;      // row group, split
-  int c;         // chunk
-  int mat;       // 0 or 1 (up)
-  int half;      // FP8 half tile
-  int first, last;
-  const uint8_t* slab;  // 8 KiB of codes for this step (tile + half * 8192)
-  const uint8_t* tile;  // the tile (scales live at tile + 8192)
-};
-
-__device__ __forceinline__ void load_step(StepFrag& f, const StepDesc& d, int lane) {
-  const int fmt = d.fmt;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f.q[j] = ld_stream_g(d.slab + j * 1024 + lane * 16);
-  // ninth load: NVFP4 16 B of E4M3 scales; MXFP4 the 16-byte pair holding this
-  // lane's 8 E8M0 scales; FP8 a repeat of the first slice (no scales in tiles)
-  const uint8_t* sp = fmt == FP4G_NVFP4 ? d.tile + kCodeBytes + lane * 16
-                      : fmt == FP4G_MXFP4 ? d.tile + kCodeBytes + (lane & ~1) * 8
-                                          : d.slab + lane * 16;
-  f.s = ld_stream_g(sp);
-}
-
-// acc[m] += the step's dot products, for one format known at compile time.
-// xb: the bf16 pairs of column 256c of token 0 in LDS (the same address in every
-// lane: broadcast reads); token stride xs u32.
-template <uint32_t FMT, int M>
-__device__ __forceinline__ void step_dot_fmt(const StepFrag& f, int half, int lane, const uint32_t* xb, int xs,
-                                             float (&acc)[M]) {
+template <uint32_t FMT>
+__device__ __forceinline__ void load_frag_g(Frag<FMT>& f, const uint8_t* tile, int lane) {
   if constexpr (FMT == FP4G_FP8_ROW) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16x2 w[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        w[2 * d] = e4m3x2_bf16<false>(f.q[j][d]);
-        w[2 * d + 1] = e4m3x2_bf16<true>(f.q[j][d]);
-      }
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const u32x8 xv = *reinterpret_cast<const u32x8*>(xb + m * xs + half * 64 + j * 8);
-        float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          p0 = dot2(w[i], xv[i], p0);
-          p1 = dot2(w[i + 1], xv[i + 1], p1);
-        }
-        acc[m] += p0 + p1;
-      }
-    }
+    for (int j = 0; j < kSlotsFp8; ++j) f.q[j] = ld_stream_g(tile + j * 1024 + lane * 16);
   } else {
-    // MXFP4: this lane's 8 scale bytes are the low or high half of the 16 loaded
-    const uint32_t mx_lo = (lane & 1) ? f.s[2] : f.s[0];
-    const uint32_t mx_hi = (lane & 1) ? f.s[3] : f.s[1];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      bf16x2 w[16];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        w[4 * d + 0] = e2m1x2_bf16<0>(f.q[j][d]);
-        w[4 * d + 1] = e2m1x2_bf16<1>(f.q[j][d]);
-        w[4 * d + 2] = e2m1x2_bf16<2>(f.q[j][d]);
-        w[4 * d + 3] = e2m1x2_bf16<3>(f.q[j][d]);
-      }
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const u32x8 xa = *reinterpret_cast<const u32x8*>(xb + m * xs + j * 16);
-        const u32x8 xc = *reinterpret_cast<const u32x8*>(xb + m * xs + j * 16 + 8);
-        float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p0 = dot2(w[i], xa[i], p0);
-          p1 = dot2(w[8 + i], xc[i], p1);
-        }
-        if constexpr (FMT == FP4G_NVFP4) {
-          const uint32_t sdw = f.s[j >> 1];
-          const float s0 = (j & 1) ? e4m3_f32<2>(sdw) : e4m3_f32<0>(sdw);
-          const float s1 = (j & 1) ? e4m3_f32<3>(sdw) : e4m3_f32<1>(sdw);
-          acc[m] = __builtin_fmaf(p0, s0, acc[m]);
-          acc[m] = __builtin_fmaf(p1, s1, acc[m]);
-        } else {
-          const uint32_t sdw = (j < 4) ? mx_lo : mx_hi;
-          const int e = (int)((sdw >> (8 * (j & 3))) & 0xffu);
-          acc[m] += __builtin_amdgcn_ldexpf(p0 + p1, e - 127);
-        }
-      }
-    }
+    for (int j = 0; j < kPiecesNv; ++j) f.q[j] = ld_stream_g(tile + j * 1024 + lane * 16);
+    if constexpr (FMT == FP4G_NVFP4)
+      f.s = ld_stream_g(tile + kCodeBytes + lane * 16);
+    else
+      f.s = ld_stream2_g(tile + kCodeBytes + lane * 8);
   }
 }
 
-template <int M>
-__device__ __forceinline__ void step_dot(const StepFrag& f, int fmt, int half, int lane, const uint32_t* xb, int xs,
-                                         float (&acc)[M]) {
-  if (fmt == FP4G_NVFP4)
-    step_dot_fmt<FP4G_NVFP4, M>(f, half, lane, xb, xs, acc);
-  else if (fmt == FP4G_MXFP4)
-    step_dot_fmt<FP4G_MXFP4, M>(f, half, lane, xb, xs, acc);
-  else
-    step_dot_fmt<FP4G_FP8_ROW, M>(f, half, lane, xb, xs, acc);
-}
-
-// The fields of one op, loaded with scalar loads (never vector loads: those
-// would wait behind the prefetched weight tile).
-struct OpView {
-  const uint8_t *w0, *w1;
-  const uint16_t* x;
-  void* out;
-  const float* rs;
-  float ts0, ts1;
-  int fmt, kind, d_out, d_in, R, C, S, Q, wait_op, item_begin, n_items, nmat, cnt_base, halves;
-  int64_t part_off;
-  int wait_first;
+// FP8 tiles stream as two 8 KiB halves (slots 0-7, 8-15) so that a fragment
+// takes as many registers as an NVFP4 one.
+struct FragH {
+  u32x4 q[8];
 };
-
-__device__ __forceinline__ OpView load_op(const StreamOp* ops, int i) {
-  const uint8_t* o = reinterpret_cast<const uint8_t*>(uptr(ops + i));
-  const u32x8 a = sload8(o);
-  const u32x8 b = sload8(o + 32);
-  const u32x8 c = sload8(o + 64);
-  const u32x8 d = sload8(o + 96);
-  OpView v;
-  v.w0 = (const uint8_t*)(((uint64_t)a[1] << 32) | a[0]);
-  v.w1 = (const uint8_t*)(((uint64_t)a[3] << 32) | a[2]);
-  v.x = (const uint16_t*)(((uint64_t)a[5] << 32) | a[4]);
-  v.out = (void*)(((uint64_t)a[7] << 32) | a[6]);
-  v.rs = (const float*)(((uint64_t)b[1] << 32) | b[0]);
-  v.ts0 = __uint_as_float(b[2]);
-  v.ts1 = __uint_as_float(b[3]);
-  v.fmt = (int)b[4];
-  v.kind = (int)b[5];
-  v.d_out = (int)b[6];
-  v.d_in = (int)b[7];
-  v.R = (int)c[0];
-  v.C = (int)c[1];
-  v.S = (int)c[2];
-  v.Q = (int)c[3];
-  v.wait_op = (int)c[4];
-  v.item_begin = (int)c[5];
-  v.n_items = (int)c[6];
-  v.nmat = (int)c[7];
-  v.cnt_base = (int)d[0];
-  v.halves = (int)d[1];
-  v.part_off = (int64_t)(((uint64_t)d[3] << 32) | d[2]);
-  v.wait_first = (int)d[4];
-  return v;
+__device__ __forceinline__ void load_half_g(FragH& f, const uint8_t* half, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.q[j] = ld_stream_g(half + j * 1024 + lane * 16);
 }
-
-// Walks the wave's flat sequence of steps across its items (w, w+G, ...).
-struct Cursor {
-  const StreamOp* ops;
-  int n_items, stride;
-  int opi;               // op of the current item
-  int item;              // current item (>= n_items: end)
-  int t, n_steps;        // step within the current item
-  int g, s, c0;
-  int fmt, nmat, halves, C;
-  const uint8_t *w0, *w1;
-
-  __device__ void decode() {
-    if (item >= n_items) return;
-    for (;;) {
-      const uint8_t* o = reinterpret_cast<const uint8_t*>(uptr(ops + opi));
-      const u32x8 c = sload8(o + 64);
-      const int item_begin = (int)c[5], n = (int)c[6];
-      if (item < item_begin + n) {
-        const u32x8 a = sload8(o);
-        const u32x8 b = sload8(o + 32);
-        const u32x8 d = sload8(o + 96);
-        const int S = (int)c[2], Q = (int)c[3];
-        const int li = item - item_begin;
-        g = li / S;
-        s = li - g * S;
-        c0 = s * Q;
-        C = (int)c[1];
-        const int c1 = min(C, c0 + Q);
-        fmt = (int)b[4];
-        nmat = (int)c[7];
-        halves = (int)d[1];
-        n_steps = (c1 - c0) * nmat * halves;
-        w0 = (const uint8_t*)(((uint64_t)a[1] << 32) | a[0]);
-        w1 = (const uint8_t*)(((uint64_t)a[3] << 32) | a[2]);
-        t = 0;
-        return;
-      }
-      ++opi;
-    }
-  }
-  __device__ void init(const StreamOp* o, int n, int first, int grid) {
-    ops = o;
-    n_items = n;
-    stride = grid;
-    opi = 0;
-    item = first;
-    decode();
-  }
-  __device__ void stop() { item = n_items; }
-  // Describe the current step (op = -1 past the end) and move to the next one.
-  __device__ StepDesc step_and_advance(const uint8_t* fallback) {
-    StepDesc d;
-    if (item >= n_items) {
-      d.op = -1;
-      d.fmt = FP4G_FP8_ROW;
-      d.slab = d.tile = fallback;
-      d.g = d.s = d.c = d.mat = d.half = d.first = d.last = 0;
-      return d;
-    }
-    const int per_chunk = nmat * halves;
-    d.op = opi;
-    d.fmt = fmt;
-    d.g = g;
-    d.s = s;
-    d.c = c0 + t / per_chunk;
-    const int r = t % per_chunk;
-    d.mat = halves == 2 ? 0 : r;
-    d.half = halves == 2 ? r : 0;
-    d.first = t == 0;
-    d.last = t == n_steps - 1;
-    const int T = fmt == FP4G_NVFP4 ? kTileNv : fmt == FP4G_MXFP4 ? kTileMx : kTileF8;
-    d.tile = (d.mat ? w1 : w0) + ((int64_t)g * C + d.c) * T;
-    d.slab = d.tile + d.half * 8192;
-    if (++t == n_steps) {
-      item += stride;
-      decode();
-    }
-    return d;
-  }
-};
-
+// Half a tile of E4M3 rows (128 columns) against xc (bf16 pairs of its first
+// column for token 0; token m at + m * xstride).
 template <int M>
-__device__ __forceinline__ void finalize_row(const OpView& op, unsigned* done, int opi, int row, const float (&v)[2][M],
-                                             int lane) {
-  if (op.kind == SK_GATE_UP) {
-    uint32_t* out = reinterpret_cast<uint32_t*>(op.out);
+__device__ __forceinline__ void half_dot_fp8(const FragH& f, const uint32_t* xc, int xstride, float (&acc)[M]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bf16x2 w[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      w[2 * d] = e4m3x2_bf16<false>(f.q[j][d]);
+      w[2 * d + 1] = e4m3x2_bf16<true>(f.q[j][d]);
+    }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const uint32_t h = f32_to_bf16_rne(silu_f32(v[0][m] * op.ts0) * (v[1][m] * op.ts1));
-      const uint32_t hn = __shfl_down(h, 1, 64);
-      if ((lane & 1) == 0) store_dev_u32(out + ((int64_t)m * op.d_out + row) / 2, h | (hn << 16));
-    }
-  } else {
-    float* out = reinterpret_cast<float*>(op.out);
-    const float sc = op.rs ? load_f32_g(op.rs + row) : op.ts0;
+      const uint32_t* xm = xc + m * xstride + j * 8;
+      float p0 = 0.0f, p1 = 0.0f;
 #pragma unroll
-    for (int m = 0; m < M; ++m) store_dev_f32(out + (int64_t)m * op.d_out + row, v[0][m] * sc);
+      for (int i = 0; i < 8; i += 2) {
+        p0 = dot2(w[i], xm[i], p0);
+        p1 = dot2(w[i + 1], xm[i + 1], p1);
+      }
+      acc[m] += p0 + p1;
+    }
   }
-  // the outputs are complete before the op's done counter moves
+}
+
+// Wave 0: wait until ops first..last are complete in this run (bounded).
+__device__ void wait_ops(StreamHdr* hdr, const StreamOp* ops, int first, int last, uint64_t epoch, int lane) {
+  const uint8_t* done = reinterpret_cast<const uint8_t*>(hdr) + hdr->off_done;
+  for (int j = first; j <= last; ++j) {
+    const uint64_t target = epoch * (uint64_t)ops[j].expect;
+    const int base = ops[j].done_base;
+    for (int spins = 0;; ++spins) {
+      uint64_t v = lane < kDoneLanes ? load_dev_u64(done + (int64_t)(base + lane) * kDoneStride * 8) : 0ull;
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      if (uniform64(v) >= target) break;
+      if (spins >= kSpinLimit || load_dev_i32(&hdr->err) != 0) {
+        if (lane == 0) __hip_atomic_store(&hdr->err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+}
+
+// One work unit of an op of format FMT (NMAT = 2: the fused gate/up pair).
+template <uint32_t FMT, int M, int NMAT>
+__device__ __forceinline__ void run_unit(StreamHdr* hdr, const StreamOp* ops, const StreamOp& op, uint64_t epoch,
+                                         float (*red)[2 * M][64], uint8_t* xs) {
+  constexpr int NA = NMAT * M;
+  constexpr int EPI = NMAT == 2 ? EPI_SILU : EPI_STORE;
+  constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : FMT == FP4G_MXFP4 ? kTileMx : kTileF8;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int local = uniform((int)blockIdx.x - op.unit_begin);
+  const int g = local / op.S, s = local % op.S;
+  const int wg_c0 = s * op.wg_chunks, wg_c1 = min(op.C, wg_c0 + op.wg_chunks);
+  const int c0 = wg_c0 + (wave * (wg_c1 - wg_c0)) / kStreamNW;
+  const int c1 = wg_c0 + ((wave + 1) * (wg_c1 - wg_c0)) / kStreamNW;
+  const int64_t tile0 = (int64_t)g * op.C;
+  const uint8_t* w0 = op.w0;
+  const uint8_t* w1 = op.w1;
+  // items: NVFP4/MXFP4 (chunk, matrix) chunk-major; FP8 (chunk, half)
+  constexpr bool F8 = FMT == FP4G_FP8_ROW;
+  constexpr int PER = F8 ? 2 : NMAT;  // items per chunk
+  using FragT = typename std::conditional<F8, FragH, Frag<FMT>>::type;
+  const int n_items = (c1 - c0) * PER;
+  auto tile_of = [&](int it) {
+    if constexpr (F8)
+      return w0 + (tile0 + c0 + it / 2) * TILE + (it & 1) * 8192;
+    else
+      return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE;
+  };
+  auto load = [&](FragT& f, int it) {
+    if constexpr (F8)
+      load_half_g(f, tile_of(it), lane);
+    else
+      load_frag_g<FMT>(f, tile_of(it), lane);
+  };
+
+  // weights first: they do not depend on the ops this one waits for
+  FragT fa, fb;
+  if (n_items > 0) load(fa, 0);
+  if (op.wait_op >= 0) {
+    if (wave == 0) wait_ops(hdr, ops, op.wait_first, op.wait_op, epoch, lane);
+    __syncthreads();
+  }
+  asm volatile("" ::: "memory");
+
+  // the unit's input columns of all M vectors into LDS (device-scope loads, all
+  // issued before the first LDS store)
+  const int nck = wg_c1 - wg_c0;
+  const int tstride = op.wg_chunks * 512;  // bytes per vector in LDS
+  {
+    constexpr int kMaxPieces = kStreamXBytes / 8 / (kStreamNW * 64);
+    const int per_tok = nck * 64;  // 8-byte pieces per vector
+    const int pieces = M * per_tok;
+    uint64_t v[kMaxPieces];
+#pragma unroll
+    for (int k = 0; k < kMaxPieces; ++k) {
+      const int idx = threadIdx.x + k * kStreamNW * 64;
+      const int m = idx / per_tok, r = idx - m * per_tok;
+      v[k] = idx < pieces ? load_dev_u64(op.x + (int64_t)m * op.d_in + wg_c0 * kChunkK + r * 4) : 0ull;
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxPieces; ++k) {
+      const int idx = threadIdx.x + k * kStreamNW * 64;
+      if (idx < pieces) {
+        const int m = idx / per_tok, r = idx - m * per_tok;
+        *reinterpret_cast<uint64_t*>(xs + m * tstride + r * 8) = v[k];
+      }
+    }
+  }
+  __syncthreads();
+
+  float acc[NMAT][M];
+#pragma unroll
+  for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[a][m] = 0.0f;
+  const uint32_t* xl = reinterpret_cast<const uint32_t*>(xs);
+  const int xstride = tstride / 4;
+  auto eat = [&](const FragT& f, int it) {
+    // re-read x from LDS for every item: kept live across the gate and up items
+    // of one chunk it would take 128 more VGPRs
+    asm volatile("" ::: "memory");
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = 0.0f;
+    if constexpr (F8) {
+      const uint32_t* xc = xl + (c0 + it / 2 - wg_c0) * (kChunkK / 2) + (it & 1) * 64;
+      half_dot_fp8<M>(f, xc, xstride, part);
+    } else {
+      const uint32_t* xc = xl + (c0 + it / NMAT - wg_c0) * (kChunkK / 2);
+      tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, part);
+    }
+    if (NMAT == 1 || it % NMAT == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[0][m] += part[m];
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[NMAT - 1][m] += part[m];
+    }
+  };
+  // fa is already in flight; the rest as in the separate kernel
+  if (n_items > 0) {
+    int it = 0;
+    for (; it + 2 < n_items; it += 2) {
+      load(fb, it + 1);
+      eat(fa, it);
+      load(fa, it + 2);
+      eat(fb, it + 1);
+    }
+    if (it + 1 < n_items) {
+      load(fb, it + 1);
+      eat(fa, it);
+      eat(fb, it + 1);
+    } else {
+      eat(fa, it);
+    }
+  }
+
+#pragma unroll
+  for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+    for (int m = 0; m < M; ++m) red[wave][a * M + m][lane] = acc[a][m];
+  __syncthreads();
+  if (wave != 0) return;
+  float v[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    float t = red[0][i][lane];
+#pragma unroll
+    for (int w = 1; w < kStreamNW; ++w) t += red[w][i][lane];
+    v[i] = t;
+  }
+  constexpr int NU = EPI == EPI_SILU ? M : (M + 1) / 2;
+  float ua[NU], ub[NU];
+  bool live[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if constexpr (EPI == EPI_SILU) {
+      ua[u] = v[u];
+      ub[u] = v[M + u];
+    } else {
+      ua[u] = v[2 * u];
+      ub[u] = 2 * u + 1 < M ? v[2 * u + 1] : 0.0f;
+    }
+    live[u] = true;
+  }
+  unsigned long long* slots =
+      reinterpret_cast<unsigned long long*>(reinterpret_cast<uint8_t*>(hdr) + hdr->off_slots) + op.slot_off;
+  exchange_tree<NU>(slots, (int64_t)op.R * 64, (int64_t)g * 64 + lane, op.S, s, ua, ub, live);
+
+  const int row = g * 64 + lane;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (!live[u]) continue;
+    if constexpr (EPI == EPI_SILU) {
+      const float gv = ua[u] * op.ts0, uv = ub[u] * op.ts1;
+      store_dev_u16(reinterpret_cast<uint16_t*>(op.out) + (int64_t)u * op.d_out + row,
+                    f32_to_bf16_rne(silu_f32(gv) * uv));
+    } else {
+      const float sc = FMT == FP4G_FP8_ROW ? *(const FP4G_GLOBAL float*)(op.rs + row) : op.ts0;
+      float* y = reinterpret_cast<float*>(op.out);
+      store_dev_f32(y + (int64_t)(2 * u) * op.d_out + row, ua[u] * sc);
+      if (2 * u + 1 < M) store_dev_f32(y + (int64_t)(2 * u + 1) * op.d_out + row, ub[u] * sc);
+    }
+  }
+  // each (lane, unit) survives in exactly one workgroup: report the ones that
+  // survived here once the stores above are complete
+  int reports = 0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) reports += __builtin_popcountll(__ballot(live[u]));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (lane == 0)
-    __hip_atomic_fetch_add(done + ((int64_t)opi * kDoneLanes + (row >> 6) % kDoneLanes) * kDoneStride, 1u,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0 && reports > 0) {
+    uint8_t* done = reinterpret_cast<uint8_t*>(hdr) + hdr->off_done;
+    uint64_t* c = reinterpret_cast<uint64_t*>(done) + (int64_t)(op.done_base + blockIdx.x % kDoneLanes) * kDoneStride;
+    __hip_atomic_fetch_add(c, (uint64_t)reports, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int M>
-__global__ __launch_bounds__(64) void k_stream(StreamHdr* hdr) {
-  const int lane = threadIdx.x;
-  const int n_items = hdr->n_items;
-  const StreamOp* ops = reinterpret_cast<const StreamOp*>(reinterpret_cast<uint8_t*>(hdr) + hdr->off_ops);
-  unsigned* done = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(hdr) + hdr->off_done);
-  unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(hdr) + hdr->off_cnt);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(hdr) + hdr->off_part);
-  const int grid = hdr->grid;
-  const int n_ops = hdr->n_ops;
-  const int total_cnt = hdr->total_cnt;
-  const uint8_t* fallback = reinterpret_cast<const uint8_t*>(hdr);  // >= 16 KiB of workspace, read harmlessly
-
-  // the x columns of the current item, M tokens x (Q chunks x 128 bf16 pairs)
-  constexpr int kQ = M <= 2 ? 4 : M <= 4 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint32_t xs_lds[M * kQ * 128];
-  Cursor cu;
-  cu.init(ops, n_items, blockIdx.x, grid);
-  int waited = -1;     // last op whose completion this wave has observed
-  int item_c0 = 0;     // first chunk of the current item (x columns in LDS)
-  int cached = -1;     // op whose fields are in `op`
-  bool abort = false;
-  float acc[2][M];
-  OpView op;
-
-  StepFrag fa, fb;
-  StepDesc da = cu.step_and_advance(fallback);
-  load_step(fa, da, lane);
-  StepDesc db = cu.step_and_advance(da.slab);
-  load_step(fb, db, lane);
-
-  auto consume = [&](const StepFrag& f, const StepDesc& d) {
-    if (d.op != cached) {
-      op = load_op(ops, d.op);
-      cached = d.op;
-    }
-    if (d.first) {
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int m = 0; m < M; ++m) acc[a][m] = 0.0f;
-      const int w = op.wait_op;
-      if (w >= 0 && w != waited && !abort) {
-        for (int wi = op.wait_first; wi <= w && !abort; ++wi) {
-          const uint8_t* wo = reinterpret_cast<const uint8_t*>(uptr(ops + wi));
-          const unsigned need = (unsigned)sload8(wo + 64)[0];  // R of the awaited op
-          int spins = 0;
-          for (;;) {
-            unsigned sum = 0;
-            if (lane < kDoneLanes) sum = atomic_load_dev(done + ((int64_t)wi * kDoneLanes + lane) * kDoneStride);
-#pragma unroll
-            for (int off = 4; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-            if (__builtin_amdgcn_readfirstlane(sum) >= need) break;
-            if (atomic_load_dev(&hdr->err) != 0 || ++spins > kSpinLimit) {
-              abort = true;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(2);
-          }
-        }
-        if (abort) {
-          if (lane == 0) __hip_atomic_store(&hdr->err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          cu.stop();
-        }
-        waited = w;
-      }
-    }
-    if (abort) return;
-    if (d.first) {
-      // stage this item's x columns (chunks c0 .. c0+nc-1 of every token) in LDS;
-      // device-scope loads, issued once the producer of x is known to be done
-      const int c0 = d.c;
-      const int nc = min(op.Q, op.C - c0);
-      const int per_tok = nc * 64;  // u64 per token
-      const uint64_t* xg = reinterpret_cast<const uint64_t*>(op.x);
-      uint64_t* xl = reinterpret_cast<uint64_t*>(xs_lds);
-      for (int i = lane; i < M * per_tok; i += 64) {
-        const int m = i / per_tok, k = i - m * per_tok;
-        xl[m * (kQ * 64) + k] = __hip_atomic_load(
-            (const FP4G_GLOBAL uint64_t*)(xg + (int64_t)m * (op.d_in / 4) + (int64_t)c0 * 64 + k), __ATOMIC_RELAXED,
-            __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the LDS writes are done
-      item_c0 = c0;
-    }
-    const uint32_t* xb = xs_lds + (d.c - item_c0) * 128;
-    float pa[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) pa[m] = 0.0f;
-    step_dot<M>(f, op.fmt, d.half, lane, xb, kQ * 128, pa);
-    if (d.mat == 0) {
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[0][m] += pa[m];
-    } else {
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[1][m] += pa[m];
-    }
-    if (!d.last) return;
-    const int row = d.g * 64 + lane;
-    const int64_t rpad = (int64_t)op.R * 64;
-    if (op.S == 1) {
-      finalize_row<M>(op, done, d.op, row, acc, lane);
-      return;
-    }
-    float* base = part + op.part_off + (int64_t)d.s * op.nmat * M * rpad;
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-      if (a < op.nmat)
-#pragma unroll
-        for (int m = 0; m < M; ++m) publish_partial(base + (a * M + m) * rpad + row, acc[a][m]);
-    unsigned* c = cnt + op.cnt_base + d.g;
-    if (!arrive_last(c, (unsigned)(op.S - 1))) return;
-    float v[2][M];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float tsum = 0.0f;
-        if (a < op.nmat)
-          for (int q = 0; q < op.S; ++q)
-            tsum += collect_partial(part + op.part_off + (((int64_t)q * op.nmat + a) * M + m) * rpad + row);
-        v[a][m] = tsum;
-      }
-    reset_counter(c);
-    finalize_row<M>(op, done, d.op, row, v, lane);
-  };
-
-  // Two fragments alternate.  The loads are unconditional (past the end a wave
-  // re-reads its last slab) so that the wait counts are the same on every path.
-  while (da.op >= 0) {
-    consume(fa, da);
-    const StepDesc dn = cu.step_and_advance(db.slab);
-    if (db.op < 0) break;
-    da = dn;
-    load_step(fa, da, lane);
-    consume(fb, db);
-    db = cu.step_and_advance(da.slab);
-    load_step(fb, db, lane);
+__global__ __launch_bounds__(kStreamNW * 64) void k_stream(StreamHdr* hdr) {
+  __shared__ float red[kStreamNW][2 * M][64];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  const uint16_t* unit_op =
+      reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(hdr) + hdr->off_unit_op);
+  const StreamOp* ops = reinterpret_cast<const StreamOp*>(reinterpret_cast<const uint8_t*>(hdr) + hdr->off_ops);
+  const int oi = uniform((int)unit_op[blockIdx.x]);
+  const StreamOp& op = ops[oi];
+  const uint64_t epoch = op.wait_op >= 0 ? uniform64(load_dev_u64(&hdr->epoch)) : 0ull;
+  if (op.fmt == FP4G_NVFP4) {
+    if (op.kind == SK_GATE_UP)
+      run_unit<FP4G_NVFP4, M, 2>(hdr, ops, op, epoch, red, xs);
+    else
+      run_unit<FP4G_NVFP4, M, 1>(hdr, ops, op, epoch, red, xs);
+  } else if (op.fmt == FP4G_MXFP4) {
+    if (op.kind == SK_GATE_UP)
+      run_unit<FP4G_MXFP4, M, 2>(hdr, ops, op, epoch, red, xs);
+    else
+      run_unit<FP4G_MXFP4, M, 1>(hdr, ops, op, epoch, red, xs);
+  } else {
+    run_unit<FP4G_FP8_ROW, M, 1>(hdr, ops, op, epoch, red, xs);
   }
+}
 
-  // the last wave to leave resets the counters for the next launch
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  unsigned prev = 0;
-  if (lane == 0) prev = __hip_atomic_fetch_add(&hdr->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0, 64);
-  if (prev != (unsigned)(grid - 1)) return;
-  for (int i = lane; i < n_ops * kDoneLanes; i += 64)
-    __hip_atomic_store(done + (int64_t)i * kDoneStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (atomic_load_dev(&hdr->err) != 0)
-    for (int i = lane; i < total_cnt; i += 64)
-      __hip_atomic_store(cnt + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane == 0) __hip_atomic_store(&hdr->exit_count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Runs so far: bumped once before each run (the same stream orders it).
+__global__ void k_stream_epoch(StreamHdr* hdr) {
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&hdr->epoch, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- host side ----------------------------------------------------------------------
-// Chunks per item: enough items per op to give every wave of a full grid
-// (256 CUs x 8 waves) about one, so that each op spreads over the whole GPU;
-// never more chunks than the LDS staging of x holds at this M.
-constexpr int64_t kTargetItems = 2048;
-int max_chunks_per_item(int M) { return M <= 2 ? 4 : M <= 4 ? 2 : 1; }
-int64_t chunks_per_item(int M, int64_t R, int64_t C) {
-  int64_t S = (kTargetItems + R - 1) / R;
-  if (S > C) S = C;
-  int64_t Q = (C + S - 1) / S;
-  const int64_t qmax = max_chunks_per_item(M);
-  return Q < qmax ? Q : qmax;
+// Splits of an op: the dense planner's cost for four-wave workgroups (a launch
+// has one workgroup size), never more chunks per unit than the LDS staging of x
+// holds at this M.
+Plan plan_stream(int64_t R, int64_t C, int nmat, int M) {
+  const int waves_per_cu = (nmat == 1 ? M <= 5 : M <= 3) ? 16 : 12;
+  const int64_t max_chunks = kStreamXBytes / (M * 512);
+  Plan best{(int)C, 1, kStreamNW};
+  double best_cost = 1e30;
+  for (int64_t S0 = 1; S0 <= C; ++S0) {
+    const int64_t wg_chunks = (C + S0 - 1) / S0;
+    const int64_t S = (C + wg_chunks - 1) / wg_chunks;
+    if (S != S0 || wg_chunks > max_chunks) continue;
+    if (4 * wg_chunks < 3 * kStreamNW) break;  // more than a quarter of the waves idle
+    const int64_t wgs = R * S, waves = wgs * kStreamNW;
+    const double imbalance = (double)((wgs + kCUs - 1) / kCUs) * kCUs / (double)wgs;
+    const double rounds = (double)waves / ((double)kCUs * waves_per_cu);
+    const double cost =
+        imbalance * (1.0 + 0.03 * tree_depth(S)) * (1.0 + 0.15 * (rounds > 1.0 ? rounds - 1.0 : 0.0));
+    if (cost < best_cost - 1e-9) {
+      best = Plan{(int)S, (int)wg_chunks, kStreamNW};
+      best_cost = cost;
+    }
+  }
+  if (best_cost > 1e29) {  // short rows: as few splits as the LDS allows
+    const int64_t wg_chunks = std::min<int64_t>(C, max_chunks);
+    best = Plan{(int)((C + wg_chunks - 1) / wg_chunks), (int)wg_chunks, kStreamNW};
+  }
+  return best;
 }
 
 struct StreamLayout {
-  uint64_t off_ops, off_done, off_cnt, off_part, total;
-  int64_t total_cnt, total_part, n_items;
+  uint64_t off_ops, off_unit_op, off_done, off_slots, total;
+  int64_t n_units, slot_words;
+  int lds_bytes;
 };
 
 fp4g_status layout_stream(const fp4g_stream_op* ops, int n, int M, StreamLayout& L, StreamOp* table) {
   if (!ops) return FP4G_E_NULL;
-  if (n < 1 || n > (1 << 20) || M < 1 || M > kMaxM) return FP4G_E_SHAPE;
-  int64_t cnt = 0, partf = 0, items = 0;
+  if (n < 1 || n > 65535 || M < 1 || M > kMaxM) return FP4G_E_SHAPE;
+  int64_t units = 0, slot_words = 0;
+  int lds = 0;
   for (int i = 0; i < n; ++i) {
     const fp4g_stream_op& o = ops[i];
     if (!o.w || !o.x_dev || !o.out_dev) return FP4G_E_NULL;
@@ -575,9 +443,10 @@ fp4g_status layout_stream(const fp4g_stream_op* ops, int n, int M, StreamLayout&
     if (o.wait_op >= 0 && o.wait_op - wcount + 1 < 0) return FP4G_E_SHAPE;
     if (!aligned(o.x_dev, 16) || !aligned(o.out_dev, 256)) return FP4G_E_ALIGN;
     const int64_t R = row_groups(o.w->d_out), C = chunks(o.w->d_in);
-    const int64_t Q = chunks_per_item(M, R, C);
-    const int64_t S = (C + Q - 1) / Q;
     const int nmat = gu ? 2 : 1;
+    const Plan pl = plan_stream(R, C, nmat, M);
+    const int nu = gu ? M : (M + 1) / 2;
+    lds = std::max(lds, M * pl.wg_chunks * 512);
     if (table) {
       StreamOp& t = table[i];
       memset(&t, 0, sizeof t);
@@ -594,40 +463,38 @@ fp4g_status layout_stream(const fp4g_stream_op* ops, int n, int M, StreamLayout&
       t.d_in = o.w->d_in;
       t.R = (int32_t)R;
       t.C = (int32_t)C;
-      t.S = (int32_t)S;
-      t.Q = (int32_t)Q;
+      t.S = pl.S;
+      t.wg_chunks = pl.wg_chunks;
       t.wait_op = o.wait_op;
       t.wait_first = o.wait_op >= 0 ? o.wait_op - wcount + 1 : -1;
-      t.item_begin = (int32_t)items;
-      t.n_items = (int32_t)(R * S);
-      t.nmat = nmat;
-      t.cnt_base = (int32_t)cnt;
-      t.halves = o.w->format == FP4G_FP8_ROW ? 2 : 1;
-      t.part_off = S > 1 ? partf : 0;
+      t.unit_begin = (int32_t)units;
+      t.nu = nu;
+      t.slot_off = slot_words;
+      t.expect = R * 64 * nu;
+      t.done_base = i * kDoneLanes;
     }
-    items += R * S;
-    cnt += R;
-    if (S > 1) partf += S * nmat * M * R * 64;
-    if (items > (int64_t)1 << 30) return FP4G_E_SHAPE;
+    units += R * pl.S;
+    slot_words += tree_nodes(pl.S) * nu * R * 64;
+    if (units > (int64_t)1 << 30) return FP4G_E_SHAPE;
   }
-  L.total_cnt = cnt;
-  L.total_part = partf;
-  L.n_items = items;
+  L.n_units = units;
+  L.slot_words = slot_words;
+  L.lds_bytes = lds;
   uint64_t o = sizeof(StreamHdr);
   L.off_ops = o;
   o = align256(o + (uint64_t)n * sizeof(StreamOp));
+  L.off_unit_op = o;
+  o = align256(o + 2ull * units);
   L.off_done = o;
-  o = align256(o + 4ull * n * kDoneLanes * kDoneStride);
-  L.off_cnt = o;
-  o = align256(o + 4ull * cnt);
-  L.off_part = o;
-  o = align256(o + 4ull * partf);
-  L.total = o < 16384 ? 16384 : o;  // the fallback slab of finished waves must be readable
+  o = align256(o + 8ull * n * kDoneLanes * kDoneStride);
+  L.off_slots = o;
+  o = align256(o + 8ull * slot_words);
+  L.total = o;
   return FP4G_OK;
 }
 
 // Aliasing rules of a stream: outputs are disjoint from each other and from all
-// weights; an op's input overlaps no output except that of the op it waits for.
+// weights; an op's input overlaps no output except those of the ops it waits for.
 fp4g_status check_stream_aliases(const fp4g_stream_op* ops, int n, int M) {
   auto out_bytes = [&](const fp4g_stream_op& o) {
     return (size_t)M * o.w->d_out * (o.kind == FP4G_OP_GATE_UP ? 2 : 4);
@@ -646,19 +513,6 @@ fp4g_status check_stream_aliases(const fp4g_stream_op* ops, int n, int M) {
     }
   }
   return FP4G_OK;
-}
-
-const void* stream_kernel(int M) {
-  switch (M) {
-    case 1: return (const void*)&k_stream<1>;
-    case 2: return (const void*)&k_stream<2>;
-    case 3: return (const void*)&k_stream<3>;
-    case 4: return (const void*)&k_stream<4>;
-    case 5: return (const void*)&k_stream<5>;
-    case 6: return (const void*)&k_stream<6>;
-    case 7: return (const void*)&k_stream<7>;
-    default: return (const void*)&k_stream<8>;
-  }
 }
 
 }  // namespace
@@ -686,51 +540,42 @@ int32_t fp4g_stream_build(const fp4g_stream_op* ops, int32_t n_ops, int32_t M, v
   if (st != FP4G_OK) return st;
   for (int i = 0; i < n_ops; ++i) {
     const size_t ob = (size_t)M * ops[i].w->d_out * (ops[i].kind == FP4G_OP_GATE_UP ? 2 : 4);
-    if (overlap(ws, L.total, ops[i].out_dev, ob) || overlap(ws, L.total, ops[i].x_dev, (size_t)M * ops[i].w->d_in * 2) ||
+    if (overlap(ws, L.total, ops[i].out_dev, ob) ||
+        overlap(ws, L.total, ops[i].x_dev, (size_t)M * ops[i].w->d_in * 2) ||
         overlap(ws, L.total, ops[i].w->packed, ops[i].w->packed_bytes))
       return FP4G_E_ALIAS;
   }
-  // host image of header + op table, then one synchronous copy; counters zeroed
+  // host image of header, op table and unit table; counters and slots zeroed
   const size_t img = L.off_done;
   uint8_t* h = (uint8_t*)calloc(1, img);
   if (!h) return FP4G_E_HIP;
   StreamHdr* hdr = (StreamHdr*)h;
   hdr->magic = kStreamMagic;
   hdr->n_ops = n_ops;
-  hdr->n_items = (int32_t)L.n_items;
+  hdr->n_units = (int32_t)L.n_units;
   hdr->M = M;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-    free(h);
-    return FP4G_E_HIP;
-  }
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)stream_kernel(M), 64, 0) != hipSuccess ||
-      per_cu < 1) {
-    free(h);
-    return FP4G_E_HIP;
-  }
-  // every workgroup must be resident at once (waits go to other workgroups)
-  const int grid = cus * std::min(per_cu, 8);
-  hdr->grid = grid;
-  hdr->total_cnt = (int32_t)L.total_cnt;
   hdr->off_ops = (int64_t)L.off_ops;
+  hdr->off_unit_op = (int64_t)L.off_unit_op;
   hdr->off_done = (int64_t)L.off_done;
-  hdr->off_cnt = (int64_t)L.off_cnt;
-  hdr->off_part = (int64_t)L.off_part;
-  layout_stream(ops, n_ops, M, L, (StreamOp*)(h + L.off_ops));
+  hdr->off_slots = (int64_t)L.off_slots;
+  hdr->lds_bytes = L.lds_bytes;
+  StreamOp* table = (StreamOp*)(h + L.off_ops);
+  layout_stream(ops, n_ops, M, L, table);
+  uint16_t* uop = (uint16_t*)(h + L.off_unit_op);
+  for (int i = 0; i < n_ops; ++i)
+    for (int64_t u = 0; u < (int64_t)table[i].R * table[i].S; ++u) uop[table[i].unit_begin + u] = (uint16_t)i;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemcpyAsync(ws, h, img, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipMemsetAsync((uint8_t*)ws + L.off_done, 0, L.off_part - L.off_done, s);
+  if (e == hipSuccess) e = hipMemsetAsync((uint8_t*)ws + L.off_done, 0, L.total - L.off_done, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   free(h);
   if (e != hipSuccess) return FP4G_E_HIP;
   plan->magic = kStreamMagic;
   plan->M = M;
   plan->n_ops = n_ops;
-  plan->n_items = (int32_t)L.n_items;
-  plan->grid = grid;
-  plan->reserved = 0;
+  plan->n_items = (int32_t)L.n_units;
+  plan->grid = (int32_t)L.n_units;
+  plan->reserved = L.lds_bytes;
   plan->ws = ws;
   plan->ws_bytes = L.total;
   return FP4G_OK;
@@ -739,13 +584,17 @@ int32_t fp4g_stream_build(const fp4g_stream_op* ops, int32_t n_ops, int32_t M, v
 int32_t fp4_stream_run(const fp4g_stream_plan* plan, void* stream) {
   if (!plan || !plan->ws) return FP4G_E_NULL;
   if (plan->magic != kStreamMagic) return FP4G_E_FORMAT;
-  if (plan->M < 1 || plan->M > kMaxM || plan->grid < 1) return FP4G_E_SHAPE;
+  if (plan->M < 1 || plan->M > kMaxM || plan->grid < 1 || plan->reserved < 0 || plan->reserved > kStreamXBytes)
+    return FP4G_E_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   StreamHdr* hdr = (StreamHdr*)plan->ws;
+  k_stream_epoch<<<1, 64, 0, s>>>(hdr);
+  if (hipGetLastError() != hipSuccess) return FP4G_E_HIP;
+  const size_t lds = (size_t)plan->reserved;
   switch (plan->M) {
 #define FP4G_CASE(MM) \
   case MM:            \
-    k_stream<MM><<<plan->grid, 64, 0, s>>>(hdr); \
+    k_stream<MM><<<plan->grid, kStreamNW * 64, lds, s>>>(hdr); \
     break;
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
 #undef FP4G_CASE

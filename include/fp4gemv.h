@@ -269,8 +269,9 @@ int32_t fp8_lmhead_gemv(const fp4g_weight* W_host, const uint16_t* X_dev, int32_
 
 /* One product of a decode step.  Decoding a token runs every matrix of the model
  * once, each on the previous one's output (feed, section "Decode speed is bytes
- * divided by bandwidth"); a stream is that chain, executed by one persistent
- * launch that keeps HBM busy across the boundaries between products.
+ * divided by bandwidth"); a stream is that chain, executed by one launch in
+ * which each unit of work (op, 64-row group, K split) puts its weight loads in
+ * flight before it waits for the ops it depends on.
  *   kind     FP4G_OP_GEMV: NVFP4/MXFP4 matrix, out = f32 [M][d_out];
  *            FP4G_OP_GATE_UP: gate (w) and up (w_up) of one shape, out = bf16
  *            [M][d_out] = bf16(SiLU(gate x) * (up x)) as fp4_gate_up_silu;
@@ -301,9 +302,9 @@ typedef struct {
   uint32_t magic;
   int32_t M;        /* vectors per product, 1..8 */
   int32_t n_ops;
-  int32_t n_items;  /* work items (op, 64-row group, column range) */
-  int32_t grid;     /* workgroups per launch */
-  int32_t reserved;
+  int32_t n_items;  /* work units (op, 64-row group, K split) */
+  int32_t grid;     /* workgroups per launch (one per unit) */
+  int32_t reserved; /* set by fp4g_stream_build (LDS bytes per workgroup); do not edit */
   void* ws;         /* the stream's workspace (device) */
   uint64_t ws_bytes;
 } fp4g_stream_plan;
@@ -318,8 +319,8 @@ uint64_t fp4g_stream_workspace_bytes(const fp4g_stream_op* ops_host, int32_t n_o
 int32_t fp4g_stream_build(const fp4g_stream_op* ops_host, int32_t n_ops, int32_t M, void* ws_dev, uint64_t ws_bytes,
                           fp4g_stream_plan* plan_host, void* stream);
 
-/* Run every op of the stream once, in one asynchronous launch (capturable in a
- * HIP graph).  Runs of one plan must be ordered on one stream.  A run that hits
+/* Run every op of the stream once, asynchronously (a one-thread launch that
+ * counts the run, then the stream's launch; capturable in a HIP graph).  Runs of one plan must be ordered on one stream.  A run that hits
  * an internal time-out sets a sticky error flag (see fp4g_stream_error) instead
  * of hanging; its outputs are then unspecified. */
 int32_t fp4_stream_run(const fp4g_stream_plan* plan_host, void* stream);

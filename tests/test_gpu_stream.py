@@ -93,6 +93,26 @@ def test_small_chain_matches_oracle(M):
             assert torch.equal(a, b), "repeated runs differ"
 
 
+def test_new_inputs_each_run():
+    """Inputs change between runs (as activations do between decode steps): every
+    run must read this run's inputs and intermediates, never a copy cached by the
+    previous run."""
+    log("stream new inputs")
+    M = 2
+    ops, (hg, hu, hd, hm, hh), x, (h0, y1, y2, y3) = small_chain(M)
+    st = fg.Stream(ops, M)
+    for rep in range(4):
+        x.copy_(datagen.bf16_normal((M, 512), datagen.tensor_seed("sx-rep", rep), device=DEV))
+        st.run()
+        torch.cuda.synchronize()
+        assert st.error() == 0
+        xb = bits(x)
+        check_h(h0, hg, hu, xb)
+        check_y(y1, hd, bits(h0))
+        check_y(y2, hm, xb)
+        check_y(y3, hh, xb)
+
+
 def test_graph_replays_match_eager():
     log("stream graph")
     M = 2
