@@ -320,9 +320,10 @@ int32_t fp4g_stream_build(const fp4g_stream_op* ops_host, int32_t n_ops, int32_t
                           fp4g_stream_plan* plan_host, void* stream);
 
 /* Run every op of the stream once, asynchronously (a one-thread launch that
- * counts the run, then the stream's launch; capturable in a HIP graph).  Runs of one plan must be ordered on one stream.  A run that hits
- * an internal time-out sets a sticky error flag (see fp4g_stream_error) instead
- * of hanging; its outputs are then unspecified. */
+ * counts the run, then the stream's launch; capturable in a HIP graph).  Runs of
+ * one plan must be ordered on one stream.  A run that hits an internal time-out
+ * sets a sticky error flag (see fp4g_stream_error) instead of hanging; its
+ * outputs are then unspecified. */
 int32_t fp4_stream_run(const fp4g_stream_plan* plan_host, void* stream);
 
 /* Read (into *err_host: 0 = every run since the last check was complete) and
