@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "copy"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "head", "copy"])
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
     ap.add_argument("--cpu-sample-layers", type=int, default=24,
                     help="full layers the CPU oracle runs for cpu_baseline (about 0.45 s each on 16 threads)")
@@ -239,6 +239,24 @@ def build_other(name, M, fg, datagen, torch, path=0):
         what = "dense MLP" if name == "c2" else "speculative-verify MLP"
         return step, keep, f"{what}, NVFP4 gate/up 17408x5120 + SiLU*mul, down 5120x17408, M={M} ({R} copies rotated)", \
             "gate_up_silu"
+    if name == "head":
+        # the dense model's FP8 head: plain logits, fused greedy pick, and a draft
+        # head over the leading 100032 rows (the reduced vocabulary)
+        V, DV = datagen.VOCAB, 100032
+        m = datagen.matrix(fg.FP8_ROW, V, H, datagen.tensor_seed("c3", "head"), device=dev)
+        Wh = fg.pack(fg.FP8_ROW, m["codes"], m["scales"])
+        del m
+        X = datagen.bf16_normal((M, H), datagen.tensor_seed("head", "x", M), device=dev)
+        logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+        keep += [Wh, X, logits]
+        step = Step()
+        step.add("lm_head", (lambda: fg.fp8_lmhead_gemv(Wh, X, logits)), algorithmic_gemv_bytes(fg, fg.FP8_ROW, V, H, M))
+        step.add("lm_head_argmax", (lambda: fg.fp8_lmhead_argmax(Wh, X)),
+                 algorithmic_gemv_bytes(fg, fg.FP8_ROW, V, H, M, out_bytes=0) + 8 * M)
+        step.add("draft_head_argmax", (lambda: fg.fp8_lmhead_argmax(Wh, X, 0, DV)),
+                 DV * H + 4 * DV + 2 * M * H + 8 * M)
+        return step, keep, f"FP8 LM head 248320x5120, M={M}: logits; fused greedy pick; pick over the first 100032 rows", \
+            "lm_head_argmax"
     if name == "c5":
         E, K, Hm, Fm = datagen.MOE_EXPERTS, datagen.MOE_TOPK, datagen.MOE_HIDDEN, datagen.MOE_FF
         pg = fg.packed_bytes(fg.MXFP4, Fm, Hm)

@@ -16,15 +16,15 @@ import torch
 
 __all__ = [
     "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
-    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "MAX_GROUP", "Fp4gError", "PackedWeight", "MoeLayer",
+    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
     "validate", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
-    "fp8_lmhead_gemv", "LIB_PATH", "Stream",
+    "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH", "Stream",
 ]
 
 NVFP4, MXFP4, FP8_ROW = 1, 2, 3
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
-OP_GEMV, OP_GATE_UP, OP_MOE, OP_LMHEAD, OP_GROUPED = 1, 2, 3, 4, 5
+OP_GEMV, OP_GATE_UP, OP_MOE, OP_LMHEAD, OP_GROUPED, OP_LMHEAD_ARGMAX = 1, 2, 3, 4, 5, 6
 MAX_GROUP = 4
 LAYOUT_TILE64x256 = 0x46344731
 
@@ -110,6 +110,7 @@ _SIGNATURES = {
                                 _VP, _U64, _VP]),
     "moe_route_gemv": (_I32, [ctypes.POINTER(MoeDesc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _U64, _VP]),
     "fp8_lmhead_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _VP, _U64, _VP]),
+    "fp8_lmhead_argmax": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _U64, _VP]),
     "fp4g_stream_workspace_bytes": (_U64, [ctypes.POINTER(StreamOpDesc), _I32, _I32]),
     "fp4g_stream_build": (_I32, [ctypes.POINTER(StreamOpDesc), _I32, _I32, _VP, _U64, ctypes.POINTER(StreamPlan), _VP]),
     "fp4_stream_run": (_I32, [ctypes.POINTER(StreamPlan), _VP]),
@@ -360,6 +361,24 @@ def fp8_lmhead_gemv(W: PackedWeight, X: torch.Tensor, logits: torch.Tensor | Non
     _check(lib().fp8_lmhead_gemv(ctypes.byref(W.desc), _bits(X2), M, logits.data_ptr(), _ptr(wsb),
                                  wsb.numel() if wsb is not None else 0, _stream(stream)), "fp8_lmhead_gemv")
     return logits if X.dim() == 2 else logits.view(-1)
+
+
+def fp8_lmhead_argmax(W: PackedWeight, X: torch.Tensor, row_begin: int = 0, n_rows: int | None = None,
+                      logits: bool = False, ws=None, stream=None):
+    """Greedy pick over rows [row_begin, row_begin + n_rows) of an FP8 head for X
+    bf16 [M, d_in] (or [d_in]): returns (row int32 [M], logit float32 [M],
+    logits float32 [M, n_rows] or None)."""
+    X2 = X if X.dim() == 2 else X.view(1, -1)
+    M = X2.shape[0]
+    n = W.d_out - row_begin if n_rows is None else n_rows
+    L = torch.empty((M, n), dtype=torch.float32, device=X.device) if logits else None
+    idx = torch.empty(M, dtype=torch.int32, device=X.device)
+    val = torch.empty(M, dtype=torch.float32, device=X.device)
+    wsb, need = _workspace(OP_LMHEAD_ARGMAX, W, M, X.device, ws)
+    _check(lib().fp8_lmhead_argmax(ctypes.byref(W.desc), _bits(X2), M, row_begin, n, _ptr(L), idx.data_ptr(),
+                                   val.data_ptr(), _ptr(wsb), wsb.numel() if wsb is not None else 0,
+                                   _stream(stream)), "fp8_lmhead_argmax")
+    return idx, val, L
 
 
 @dataclass

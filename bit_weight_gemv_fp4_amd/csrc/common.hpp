@@ -21,6 +21,7 @@ constexpr int kChunkK = 256;        // columns per tile
 constexpr int kPieceK = 32;         // columns per 16-byte code load of one lane
 constexpr int kPiecesNv = 8;        // NVFP4/MXFP4: 8 x 16 B code loads per tile and lane
 constexpr int kSlotsFp8 = 16;       // FP8: 16 x 16 B code loads per tile and lane
+constexpr int kHalfFp8 = 8;         // kernels stream an FP8 tile as two 8 KiB halves
 constexpr int kTileNv = 9216;       // 8 KiB codes + 64 x 16 B E4M3 scales
 constexpr int kTileMx = 8704;       // 8 KiB codes + 64 x 8 B E8M0 scales
 constexpr int kTileF8 = 16384;      // 16 KiB codes (row scales follow all tiles)
@@ -115,6 +116,47 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---- arg-max keys (MoE routing, LM-head greedy pick) -------------------------------
+// Pick order of (value, index) as one 64-bit key: the logit mapped to an unsigned integer of the
+// same order (sign bit flipped for positive values, all bits for negative ones)
+// in the high word, the complement of the expert index in the low word.  A
+// larger key is a larger logit, or an equal logit with a lower index (zeros of
+// either sign are equal).  Key 0 is below every logit's key and marks "none".
+__device__ __forceinline__ uint64_t pick_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);  // -0 ranks as +0
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)(0xffffffffu - (uint32_t)e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)(0xffffffffu - (uint32_t)k); }
+
+// One DPP step of the wave maximum: each lane takes the larger of its key and
+// the key `CTRL` names (key 0 where the source lane does not exist).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)k, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(k >> 32), CTRL, ROW_MASK, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+// Maximum key over the 64 lanes, uniform: row_shr 1, 2, 4, 8 leave each 16-lane
+// row's maximum in its lane 15; row_bcast 15 and 31 carry it up to lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max_step<0x111, 0xf>(k);  // row_shr:1
+  k = dpp_max_step<0x112, 0xf>(k);  // row_shr:2
+  k = dpp_max_step<0x114, 0xf>(k);  // row_shr:4
+  k = dpp_max_step<0x118, 0xf>(k);  // row_shr:8
+  k = dpp_max_step<0x142, 0xa>(k);  // row_bcast:15 into rows 1 and 3
+  k = dpp_max_step<0x143, 0xc>(k);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
 
 // ---- host-side validation helpers -----------------------------------------------
 inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }

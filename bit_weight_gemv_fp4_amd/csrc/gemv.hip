@@ -12,6 +12,7 @@ extern template hipError_t launch_m<FP4G_NVFP4, 2, EPI_SILU>(int, int, const Gem
 extern template hipError_t launch_m<FP4G_MXFP4, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_ARGMAX>(int, int, const GemvParams&, unsigned, hipStream_t);
 // Matrix-core launchers (gemv_mfma.hpp), in gemv_mfma_nvfp4.hip and gemv_mfma_mxfp4.hip.
 extern template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
 extern template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
@@ -96,6 +97,8 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
     gb += row_groups(W[i]->d_out);
   }
   p.gbase[n] = (int)gb;
+  if (W[0]->format == FP4G_FP8_ROW)  // row scales follow the tiles
+    p.rs = (const float*)((const uint8_t*)W[0]->packed + row_groups(W[0]->d_out) * C * kTileF8);
   p.x = X;
   p.slots = need ? (unsigned long long*)ws : nullptr;
   p.d_in = W[0]->d_in;
@@ -122,6 +125,25 @@ static int32_t run_gemv(const fp4g_weight* W, bool want_fp4, const uint16_t* X, 
   if (!W) return FP4G_E_NULL;
   return run_group(&W, 1, want_fp4, X, M, &Y, path, ws, ws_bytes, stream);
 }
+
+// One wave: the pick of every vector from the slots, which it leaves at zero.
+__global__ void k_argmax_finish(unsigned long long* amax, int M, int32_t* top_idx, float* top_val) {
+  const int lane = threadIdx.x & 63;
+  if (lane < M) {
+    uint64_t best = 0;
+    for (int j = 0; j < kArgSlots; ++j) {
+      const uint64_t k = amax[(int64_t)j * kMaxM + lane];
+      best = k > best ? k : best;
+    }
+    top_idx[lane] = key_index(best);
+    top_val[lane] = key_value(best);
+  }
+  __syncthreads();
+  for (int i = lane; i < kArgSlots * kMaxM; i += 64) amax[i] = 0ull;
+}
+
+// The greedy pick's slots (zero between calls).
+static uint64_t argmax_ws_bytes() { return align256((uint64_t)kArgSlots * kMaxM * 8); }
 
 static fp4g_status check_group(const fp4g_group* G) {
   if (!G) return FP4G_E_NULL;
@@ -157,6 +179,59 @@ int32_t fp4_gemv_grouped(const fp4g_group* G, const uint16_t* X, int32_t M, floa
 int32_t fp8_lmhead_gemv(const fp4g_weight* W, const uint16_t* X, int32_t M, float* logits, void* ws,
                         uint64_t ws_bytes, void* stream) {
   return run_gemv(W, false, X, M, logits, FP4G_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+int32_t fp8_lmhead_argmax(const fp4g_weight* W, const uint16_t* X, int32_t M, int32_t row_begin, int32_t n_rows,
+                          float* logits, int32_t* top_idx, float* top_val, void* ws, uint64_t ws_bytes,
+                          void* stream) {
+  fp4g_status st = check_weight(W, false);
+  if (st != FP4G_OK) return st;
+  if (!X || !top_idx || !top_val) return FP4G_E_NULL;
+  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
+  if (row_begin < 0 || row_begin % kRowsPerGroup || n_rows < 1 || (int64_t)row_begin + n_rows > W->d_out)
+    return FP4G_E_SHAPE;
+  if (!aligned(X, 16) || (logits && !aligned(logits, 16)) || !aligned(top_idx, 4) || !aligned(top_val, 4))
+    return FP4G_E_ALIGN;
+  const uint64_t need = argmax_ws_bytes();
+  st = check_ws(ws, ws_bytes, need);
+  if (st != FP4G_OK) return st;
+  const int64_t R_all = row_groups(W->d_out), C = chunks(W->d_in), R = row_groups(n_rows);
+  const size_t xbytes = (size_t)M * W->d_in * 2, lbytes = logits ? (size_t)M * n_rows * 4 : 0;
+  const void* outs[4] = {logits, top_idx, top_val, ws};
+  const size_t outb[4] = {lbytes, (size_t)M * 4, (size_t)M * 4, need};
+  for (int i = 0; i < 4; ++i) {
+    if (overlap(outs[i], outb[i], X, xbytes) || overlap(outs[i], outb[i], W->packed, W->packed_bytes))
+      return FP4G_E_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outb[i], outs[j], outb[j])) return FP4G_E_ALIAS;
+  }
+  GemvParams p{};
+  p.n = 1;
+  // the rows [row_begin, row_begin + n_rows) as a matrix of their own: their
+  // tiles are contiguous, their row scales sit after all the matrix's tiles
+  const uint8_t* base = (const uint8_t*)W->packed;
+  p.w[0] = base + (int64_t)(row_begin / kRowsPerGroup) * C * kTileF8;
+  p.rs = (const float*)(base + R_all * C * kTileF8) + row_begin;
+  p.tscale[0] = 1.0f;
+  p.y[0] = logits;
+  p.d_out[0] = n_rows;
+  p.gbase[0] = 0;
+  p.gbase[1] = (int)R;
+  p.x = X;
+  p.slots = nullptr;
+  p.amax = (unsigned long long*)ws;
+  p.top_idx = top_idx;
+  p.top_val = top_val;
+  p.row_base = row_begin;
+  p.d_in = W->d_in;
+  p.C = (int)C;
+  p.S = 1;  // whole rows per workgroup: no split-K tree
+  p.wg_chunks = (int)C;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_m<FP4G_FP8_ROW, 1, EPI_ARGMAX>(M, 4, p, (unsigned)R, s);
+  if (e != hipSuccess) return FP4G_E_HIP;
+  k_argmax_finish<<<1, 64, 0, s>>>(p.amax, M, top_idx, top_val);
+  return hipGetLastError() == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 
 int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uint16_t* X, int32_t M, uint16_t* H,
@@ -214,6 +289,7 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
   if (!desc || M < 1 || M > kMaxM) return 0;
   if (op == FP4G_OP_MOE) return moe_ws_bytes((const fp4g_moe*)desc, M);
+  if (op == FP4G_OP_LMHEAD_ARGMAX) return check_weight((const fp4g_weight*)desc, false) == FP4G_OK ? argmax_ws_bytes() : 0;
   if (op == FP4G_OP_GROUPED) {
     const fp4g_group* G = (const fp4g_group*)desc;
     if (check_group(G) != FP4G_OK) return 0;

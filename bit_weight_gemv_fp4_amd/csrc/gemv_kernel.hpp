@@ -34,7 +34,10 @@
 namespace fp4g {
 
 
-enum { EPI_STORE = 0, EPI_SILU = 1 };
+// EPI_ARGMAX: products as EPI_STORE (logits written only when y[0] is set), plus
+// each vector's largest logit and its row (ties to the lower row) over the launch.
+enum { EPI_STORE = 0, EPI_SILU = 1, EPI_ARGMAX = 2 };
+constexpr int kArgSlots = 64;  // spread slots of the launch-wide maximum
 
 constexpr int kMaxGroup = 4;  // matrices sharing one input in one launch
 
@@ -50,6 +53,11 @@ struct GemvParams {
   const uint16_t* x;          // bf16 [M][d_in]
   uint16_t* h;                // EPI_SILU: bf16 [M][d_out[0]]
   unsigned long long* slots;  // split-K exchange slots, zero between calls
+  const float* rs;            // FP8 rows: the row scales of rows 0.. of this launch
+  unsigned long long* amax;   // EPI_ARGMAX: [kArgSlots][kMaxM] keys, zero between calls
+  int32_t* top_idx;           // EPI_ARGMAX: [M] row of the largest logit (+ row_base)
+  float* top_val;             // EPI_ARGMAX: [M] the largest logit
+  int row_base;               // EPI_ARGMAX: added to the reported row
   int d_in, C;
   int S;                      // workgroups per row group
   int wg_chunks;              // chunks per workgroup (the last ones may get fewer)
@@ -68,15 +76,15 @@ struct Frag<FP4G_MXFP4> {
   u32x2 s;
 };
 template <>
-struct Frag<FP4G_FP8_ROW> {
-  u32x4 q[kSlotsFp8];
+struct Frag<FP4G_FP8_ROW> {  // half a tile: slots 0-7 or 8-15
+  u32x4 q[kHalfFp8];
 };
 
 template <uint32_t FMT>
 __device__ __forceinline__ void load_frag(Frag<FMT>& f, const uint8_t* tile, int lane) {
-  if constexpr (FMT == FP4G_FP8_ROW) {
+  if constexpr (FMT == FP4G_FP8_ROW) {  // `tile` is the half's first byte
 #pragma unroll
-    for (int j = 0; j < kSlotsFp8; ++j) f.q[j] = ld_stream(tile + j * 1024 + lane * 16);
+    for (int j = 0; j < kHalfFp8; ++j) f.q[j] = ld_stream(tile + j * 1024 + lane * 16);
   } else {
 #pragma unroll
     for (int j = 0; j < kPiecesNv; ++j) f.q[j] = ld_stream(tile + j * 1024 + lane * 16);
@@ -90,13 +98,15 @@ __device__ __forceinline__ void load_frag(Frag<FMT>& f, const uint8_t* tile, int
 // Accumulate one tile (columns 256c .. 256c+255, or its first `npieces` 32-column
 // pieces when FULL is false) of one matrix into acc[0..M).  xc points at the bf16
 // pairs of column 256c of token 0; token m is xc + m * xstride (in u32 units).
+// FP8: one half tile (128 columns; its first `npieces` 16-column slots when FULL
+// is false), xc at the half's first column.
 template <uint32_t FMT, int M, bool FULL>
 __device__ __forceinline__ void tile_dot(const Frag<FMT>& f, const uint32_t* __restrict__ xc, int xstride,
                                          int npieces, float (&acc)[M]) {
   if constexpr (FMT == FP4G_FP8_ROW) {
 #pragma unroll
-    for (int j = 0; j < kSlotsFp8; ++j) {
-      if (!FULL && j >= 2 * npieces) continue;
+    for (int j = 0; j < kHalfFp8; ++j) {
+      if (!FULL && j >= npieces) continue;
       bf16x2 w[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -259,20 +269,45 @@ __device__ __forceinline__ int member_of(const GemvParams& p, int gt) {
 template <uint32_t FMT, int M, int NMAT, int EPI>
 __device__ __forceinline__ void finish_unit(const GemvParams& p, int mem, int row, int u, float a, float b) {
   if (row >= p.d_out[mem]) return;
-  if constexpr (EPI == EPI_STORE) {
-    float sc = p.tscale[mem];
-    if constexpr (FMT == FP4G_FP8_ROW) {
-      const int64_t R = p.gbase[1] - p.gbase[0];
-      const int64_t C = p.C;
-      sc = reinterpret_cast<const float*>(p.w[0] + R * C * kTileF8)[row];
-    }
+  if constexpr (EPI == EPI_STORE || EPI == EPI_ARGMAX) {
+    const float sc = FMT == FP4G_FP8_ROW ? p.rs[row] : p.tscale[mem];
     const int m0 = 2 * u;
-    p.y[mem][(int64_t)m0 * p.d_out[mem] + row] = a * sc;
-    if (m0 + 1 < M) p.y[mem][(int64_t)(m0 + 1) * p.d_out[mem] + row] = b * sc;
+    if (EPI == EPI_STORE || p.y[0]) {
+      p.y[mem][(int64_t)m0 * p.d_out[mem] + row] = a * sc;
+      if (m0 + 1 < M) p.y[mem][(int64_t)(m0 + 1) * p.d_out[mem] + row] = b * sc;
+    }
   } else {
     const float g = a * p.tscale[0];
     const float v = b * p.tscale[1];
     p.h[(int64_t)u * p.d_out[0] + row] = f32_to_bf16_rne(silu_f32(g) * v);
+  }
+}
+
+// Greedy pick over the launch (wave 0 of every workgroup, after the split-K
+// tree).  The surviving lanes' logits become pick keys (the same float as the
+// logit written, ties to the lower row); each vector's wave maximum goes into one
+// of kArgSlots slots with a device-scope atomic max that nobody waits for.
+// k_argmax_finish, launched next on the same stream, reads the slots, writes
+// (row, value) per vector and leaves the slots at zero.
+template <uint32_t FMT, int M, int NU>
+__device__ __forceinline__ void argmax_epilogue(const GemvParams& p, int row, int lane, const float (&ua)[NU],
+                                                const float (&ub)[NU], const bool (&live)[NU]) {
+  const bool valid = row < p.d_out[0];
+  const float sc = valid ? (FMT == FP4G_FP8_ROW ? p.rs[row] : p.tscale[0]) : 0.0f;
+  uint64_t key[M];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const bool ok = live[u] && valid;
+    key[2 * u] = ok ? pick_key(ua[u] * sc, p.row_base + row) : 0ull;
+    if (2 * u + 1 < M) key[2 * u + 1] = ok ? pick_key(ub[u] * sc, p.row_base + row) : 0ull;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) key[m] = wave_max_key(key[m]);
+  unsigned long long* slot = p.amax + (int64_t)(blockIdx.x % kArgSlots) * kMaxM;
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      if (key[m]) __hip_atomic_fetch_max(slot + m, (unsigned long long)key[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -307,20 +342,32 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
   const int full_chunks = p.d_in / kChunkK;  // chunks with all 8 pieces present
   const int tail_pieces = (p.d_in % kChunkK) / kPieceK;
 
-  // Items are (chunk, matrix) pairs visited chunk-major.
-  const int n_items = (c1 - c0) * NMAT;
+  // Items are (chunk, matrix) pairs visited chunk-major; FP8 (chunk, half).
+  constexpr bool F8 = FMT == FP4G_FP8_ROW;
+  constexpr int PER = F8 ? 2 : NMAT;  // items per chunk
+  const int n_items = (c1 - c0) * PER;
   const int64_t tile0 = (int64_t)g * p.C;
-  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE; };
+  auto item_tile = [&](int it) {
+    if constexpr (F8)
+      return w0 + (tile0 + c0 + it / 2) * TILE + (it & 1) * (kHalfFp8 * 1024);
+    else
+      return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE;
+  };
   auto consume = [&](const Frag<FMT>& f, int it) {
-    const int c = c0 + it / NMAT;
-    const uint32_t* xc = x32 + (int64_t)c * (kChunkK / 2);
+    const int c = c0 + it / PER;
+    const int half = F8 ? (it & 1) : 0;
+    const uint32_t* xc = x32 + (int64_t)c * (kChunkK / 2) + half * (kHalfFp8 * 8);
     float part[M];
 #pragma unroll
     for (int m = 0; m < M; ++m) part[m] = 0.0f;
-    if (c < full_chunks)
+    if (c < full_chunks) {
       tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, part);
-    else
+    } else if constexpr (F8) {
+      const int slots = min(max(2 * tail_pieces - kHalfFp8 * half, 0), kHalfFp8);
+      tile_dot<FMT, M, false>(f, xc, xstride, slots, part);
+    } else {
       tile_dot<FMT, M, false>(f, xc, xstride, tail_pieces, part);
+    }
     if (NMAT == 1 || it % NMAT == 0) {
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[0][m] += part[m];
@@ -368,6 +415,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
 #pragma unroll
   for (int u = 0; u < NU; ++u)
     if (live[u]) finish_unit<FMT, M, NMAT, EPI>(p, mem, row, u, ua[u], ub[u]);
+  if constexpr (EPI == EPI_ARGMAX) argmax_epilogue<FMT, M, NU>(p, row, lane, ua, ub, live);
 }
 
 template <uint32_t FMT, int M, int NMAT, int EPI>

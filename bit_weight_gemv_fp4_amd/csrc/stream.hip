@@ -30,7 +30,6 @@
 #include <algorithm>
 #include <cstdlib>
 #include <cstring>
-#include <type_traits>
 
 #include "gemv_kernel.hpp"
 
@@ -106,9 +105,9 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
 
 template <uint32_t FMT>
 __device__ __forceinline__ void load_frag_g(Frag<FMT>& f, const uint8_t* tile, int lane) {
-  if constexpr (FMT == FP4G_FP8_ROW) {
+  if constexpr (FMT == FP4G_FP8_ROW) {  // a half tile
 #pragma unroll
-    for (int j = 0; j < kSlotsFp8; ++j) f.q[j] = ld_stream_g(tile + j * 1024 + lane * 16);
+    for (int j = 0; j < kHalfFp8; ++j) f.q[j] = ld_stream_g(tile + j * 1024 + lane * 16);
   } else {
 #pragma unroll
     for (int j = 0; j < kPiecesNv; ++j) f.q[j] = ld_stream_g(tile + j * 1024 + lane * 16);
@@ -116,41 +115,6 @@ __device__ __forceinline__ void load_frag_g(Frag<FMT>& f, const uint8_t* tile, i
       f.s = ld_stream_g(tile + kCodeBytes + lane * 16);
     else
       f.s = ld_stream2_g(tile + kCodeBytes + lane * 8);
-  }
-}
-
-// FP8 tiles stream as two 8 KiB halves (slots 0-7, 8-15) so that a fragment
-// takes as many registers as an NVFP4 one.
-struct FragH {
-  u32x4 q[8];
-};
-__device__ __forceinline__ void load_half_g(FragH& f, const uint8_t* half, int lane) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f.q[j] = ld_stream_g(half + j * 1024 + lane * 16);
-}
-// Half a tile of E4M3 rows (128 columns) against xc (bf16 pairs of its first
-// column for token 0; token m at + m * xstride).
-template <int M>
-__device__ __forceinline__ void half_dot_fp8(const FragH& f, const uint32_t* xc, int xstride, float (&acc)[M]) {
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bf16x2 w[8];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      w[2 * d] = e4m3x2_bf16<false>(f.q[j][d]);
-      w[2 * d + 1] = e4m3x2_bf16<true>(f.q[j][d]);
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint32_t* xm = xc + m * xstride + j * 8;
-      float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        p0 = dot2(w[i], xm[i], p0);
-        p1 = dot2(w[i + 1], xm[i + 1], p1);
-      }
-      acc[m] += p0 + p1;
-    }
   }
 }
 
@@ -175,7 +139,8 @@ __device__ void wait_ops(StreamHdr* hdr, const StreamOp* ops, int first, int las
   }
 }
 
-// One work unit of an op of format FMT (NMAT = 2: the fused gate/up pair).
+// One work unit of an op of format FMT (NMAT = 2: the fused gate/up pair).  FP8
+// tiles stream as two 8 KiB halves, like in the separate kernel.
 template <uint32_t FMT, int M, int NMAT>
 __device__ __forceinline__ void run_unit(StreamHdr* hdr, const StreamOp* ops, const StreamOp& op, uint64_t epoch,
                                          float (*red)[2 * M][64], uint8_t* xs) {
@@ -194,20 +159,15 @@ __device__ __forceinline__ void run_unit(StreamHdr* hdr, const StreamOp* ops, co
   // items: NVFP4/MXFP4 (chunk, matrix) chunk-major; FP8 (chunk, half)
   constexpr bool F8 = FMT == FP4G_FP8_ROW;
   constexpr int PER = F8 ? 2 : NMAT;  // items per chunk
-  using FragT = typename std::conditional<F8, FragH, Frag<FMT>>::type;
+  using FragT = Frag<FMT>;
   const int n_items = (c1 - c0) * PER;
   auto tile_of = [&](int it) {
     if constexpr (F8)
-      return w0 + (tile0 + c0 + it / 2) * TILE + (it & 1) * 8192;
+      return w0 + (tile0 + c0 + it / 2) * TILE + (it & 1) * (kHalfFp8 * 1024);
     else
       return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE;
   };
-  auto load = [&](FragT& f, int it) {
-    if constexpr (F8)
-      load_half_g(f, tile_of(it), lane);
-    else
-      load_frag_g<FMT>(f, tile_of(it), lane);
-  };
+  auto load = [&](FragT& f, int it) { load_frag_g<FMT>(f, tile_of(it), lane); };
 
   // weights first: they do not depend on the ops this one waits for
   FragT fa, fb;
@@ -259,8 +219,8 @@ __device__ __forceinline__ void run_unit(StreamHdr* hdr, const StreamOp* ops, co
 #pragma unroll
     for (int m = 0; m < M; ++m) part[m] = 0.0f;
     if constexpr (F8) {
-      const uint32_t* xc = xl + (c0 + it / 2 - wg_c0) * (kChunkK / 2) + (it & 1) * 64;
-      half_dot_fp8<M>(f, xc, xstride, part);
+      const uint32_t* xc = xl + (c0 + it / 2 - wg_c0) * (kChunkK / 2) + (it & 1) * (kHalfFp8 * 8);
+      tile_dot<FMT, M, true>(f, xc, xstride, kHalfFp8, part);
     } else {
       const uint32_t* xc = xl + (c0 + it / NMAT - wg_c0) * (kChunkK / 2);
       tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, part);

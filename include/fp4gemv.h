@@ -93,7 +93,8 @@ typedef enum {
   FP4G_OP_GATE_UP = 2,  /* fp4_gate_up_silu; desc = fp4g_weight (gate) */
   FP4G_OP_MOE = 3,      /* moe_route_gemv; desc = fp4g_moe */
   FP4G_OP_LMHEAD = 4,   /* fp8_lmhead_gemv; desc = fp4g_weight */
-  FP4G_OP_GROUPED = 5   /* fp4_gemv_grouped; desc = fp4g_group */
+  FP4G_OP_GROUPED = 5,  /* fp4_gemv_grouped; desc = fp4g_group */
+  FP4G_OP_LMHEAD_ARGMAX = 6  /* fp8_lmhead_argmax; desc = fp4g_weight */
 } fp4g_op;
 
 /* Most matrices one fp4_gemv_grouped call takes. */
@@ -264,6 +265,24 @@ int32_t moe_route_gemv(const fp4g_moe* moe_host, const uint16_t* X_dev, const fl
  * X_dev: bf16 [M][d_in]; logits_dev: f32 [M][d_out]. */
 int32_t fp8_lmhead_gemv(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M,
                         float* logits_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
+/* Greedy pick from the FP8 output layer in the same launch (the layer scores
+ * the vocabulary and decoding keeps its best token: feed, sections "MTP: the
+ * drafter inside the checkpoint" and "Shaving the step"), over the rows
+ * [row_begin, row_begin + n_rows) -- the whole vocabulary, or a draft head that
+ * scores a leading part of it.  For m < M in 1..8:
+ *   logit[m][r] = s_row[r] * sum_k e4m3(c[r][k]) * X_dev[m][k] as fp8_lmhead_gemv,
+ *   top_idx_dev[m] = the row r (absolute, row_begin <= r < row_begin + n_rows)
+ *     with the largest FP32 logit, the lower row on equal logits (-0 == +0),
+ *   top_val_dev[m] = that logit.
+ * row_begin % 64 == 0.  logits_dev: NULL, or f32 [M][n_rows] (logit of row
+ * row_begin + j at j).  top_idx_dev i32 [M], top_val_dev f32 [M].  The workspace
+ * (fp4g_workspace_bytes(FP4G_OP_LMHEAD_ARGMAX, ...), a few KiB) must be
+ * zero-filled once; every call leaves it at zero.  One workgroup per 64 rows (no
+ * split-K), then a one-wave launch that collects the pick. */
+int32_t fp8_lmhead_argmax(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M, int32_t row_begin,
+                          int32_t n_rows, float* logits_dev, int32_t* top_idx_dev, float* top_val_dev,
+                          void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* --- a whole decode step in one launch --------------------------------------- */
 

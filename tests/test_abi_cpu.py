@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     L = fg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -155,6 +155,32 @@ def test_grouped_error_paths():
     assert call_grouped(G) == E_NULL
     assert call_grouped(G, ws=FAKE + (12 << 30), wsb=need - 8) == E_WORKSPACE
     assert L.fp4g_workspace_bytes(fg.OP_GROUPED, ctypes.byref(group_desc(q, k2)), 1) == 0
+
+
+def test_lmhead_argmax_error_paths():
+    L = fg.lib()
+    f8 = good_desc(fmt=fg.FP8_ROW, d_out=300, d_in=512)
+    X, I, V, LG = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
+    need = L.fp4g_workspace_bytes(fg.OP_LMHEAD_ARGMAX, ctypes.byref(f8), 1)
+    assert 0 < need <= 8192
+    WS = FAKE + (5 << 30)
+
+    def call(d=f8, M=1, rb=0, n=300, lg=LG, i=I, v=V, ws=WS, wsb=need):
+        return L.fp8_lmhead_argmax(ctypes.byref(d), X, M, rb, n, lg, i, v, ws, wsb, None)
+
+    assert call(d=good_desc()) == E_FORMAT        # NVFP4 is not a head format here
+    assert call(M=9) == E_SHAPE
+    assert call(rb=32) == E_SHAPE                 # row_begin not a multiple of 64
+    assert call(n=0) == E_SHAPE
+    assert call(rb=64, n=237) == E_SHAPE          # past d_out
+    assert call(i=None) == E_NULL
+    assert call(v=None) == E_NULL
+    assert call(ws=None) == E_NULL
+    assert call(wsb=need - 1) == E_WORKSPACE
+    assert call(lg=LG + 4) == E_ALIGN
+    assert call(lg=FAKE + 1024) == E_ALIAS        # logits over the weights
+    assert call(i=V) == E_ALIAS                   # the two outputs overlap
+    assert L.fp4g_workspace_bytes(fg.OP_LMHEAD_ARGMAX, ctypes.byref(good_desc()), 1) == 0
 
 
 def test_gate_up_error_paths():

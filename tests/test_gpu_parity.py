@@ -156,6 +156,65 @@ def test_lmhead_matches_oracle(M):
         check_product(fg.fp8_lmhead_gemv(W, X), host, bits(X))
 
 
+def f32_argmax(L):
+    """Per row of L (float32), the column of the largest value, the lower column
+    on ties (-0 == +0): the pick the kernel must make from its own FP32 logits."""
+    L = np.where(L == 0, np.float32(0), L)
+    return np.argmax(L, axis=1)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_lmhead_argmax(M):
+    """Fused greedy pick: logits within the bound, the pick is the FP32 arg-max of
+    those very logits, its value is that logit, and the oracle's best row is
+    within the bound of it; also on a row range (a draft head's rows)."""
+    log("lmhead argmax", M)
+    W, host = make(fg.FP8_ROW, 1000, 544, seed=40)
+    X = datagen.bf16_normal((M, 544), datagen.tensor_seed("am", M), device=DEV)
+    Y, A = oracle.gemv(fg.FP8_ROW, host["codes"], host["scales"], 1.0, bits(X))
+    for rb, n in ((0, 1000), (128, 300), (960, 40), (0, 64)):
+        idx, val, L = fg.fp8_lmhead_argmax(W, X, rb, n, logits=True)
+        Lh = L.cpu().numpy()
+        check_product(L, {**host, "codes": host["codes"][rb:rb + n], "scales": host["scales"][rb:rb + n]}, bits(X))
+        pick = f32_argmax(Lh) + rb
+        assert np.array_equal(idx.cpu().numpy(), pick), (rb, n)
+        assert np.array_equal(val.cpu().numpy(), Lh[np.arange(M), pick - rb]), (rb, n)
+        best = np.argmax(Y[:, rb:rb + n], axis=1)
+        assert np.all(Y[np.arange(M), idx.cpu().numpy()] >= Y[np.arange(M), best + rb] - 2 * TOL * A.max()), (rb, n)
+        # no logits requested: the same pick
+        idx2, val2, _ = fg.fp8_lmhead_argmax(W, X, rb, n)
+        assert torch.equal(idx2, idx) and torch.equal(val2, val)
+
+
+def test_lmhead_argmax_ties_pick_the_lower_row():
+    log("lmhead argmax ties")
+    mat = datagen.matrix(fg.FP8_ROW, 320, 256, 41, device=DEV)
+    codes = mat["codes"][:1].repeat(320, 1).contiguous()       # every row the same
+    scales = torch.full((320,), 0.01, dtype=torch.float32, device=DEV)
+    W = fg.pack(fg.FP8_ROW, codes, scales)
+    X = datagen.bf16_normal((3, 256), 42, device=DEV)
+    for rb in (0, 64, 192):
+        idx, val, _ = fg.fp8_lmhead_argmax(W, X, rb, 320 - rb)
+        assert idx.tolist() == [rb] * 3
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_lmhead_argmax_full_vocabulary(M):
+    """The dense model's 248320-row head (M = 1) and the MoE model's 157184-row head
+    (M = 4) against the full FP64 oracle."""
+    log("lmhead argmax full", M)
+    V, d = (datagen.VOCAB, datagen.HIDDEN) if M == 1 else (datagen.MOE_VOCAB, datagen.MOE_HIDDEN)
+    W, host = make(fg.FP8_ROW, V, d, seed=43)
+    X = datagen.bf16_normal((M, d), datagen.tensor_seed("amf", M), device=DEV)
+    idx, val, L = fg.fp8_lmhead_argmax(W, X, logits=True)
+    Lh = L.cpu().numpy()
+    assert np.array_equal(idx.cpu().numpy(), f32_argmax(Lh))
+    Y, A = oracle.gemv(fg.FP8_ROW, host["codes"], host["scales"], 1.0, bits(X))
+    assert np.all(np.abs(Lh.astype(np.float64) - Y) <= TOL * A)
+    i = idx.cpu().numpy().astype(np.int64)
+    assert np.all(Y[np.arange(M), i] >= Y.max(axis=1) - 2 * TOL * A.max(axis=1))
+
+
 def h_bound(r, h_ref):
     tg, tu = TOL * r["Ag"], TOL * r["Au"]
     silu_g = r["g"] / (1.0 + np.exp(-r["g"]))
