@@ -20,7 +20,8 @@
 //    FP32.  One block (16 columns NVFP4, 32 MXFP4) is summed by chained MFMAs into
 //    a fresh accumulator, then scaled once per row on the VALU: lane i's outputs
 //    are rows 16 (i % 4) + 4 (i / 16) + 0..3 of token (i / 4) % 4, so it loads
-//    those four rows' block scales (64 or 32 contiguous bytes of the tile).
+//    those four rows' block scales.  Tiles stream as two halves (4 code slots
+//    and their scales) to keep the double-buffered fragments in 48 VGPRs.
 //  * The input columns of a workgroup's chunk range are staged in LDS (zero past
 //    d_in), with a 512-byte zero area that the off-diagonal lanes read.
 #pragma once
@@ -35,29 +36,35 @@ constexpr int kMfmaXBytes = 40960;  // LDS for the staged input of one workgroup
                                     // 16 KiB reduction buffer: under 64 KiB)
 constexpr int kZeroBytes = 512;     // one chunk row of zeros
 
+// A fragment is half a tile: code slots 4h .. 4h+3 of lane i's row, and the
+// block scales of those slots for the lane's four output rows srow .. srow+3.
 template <uint32_t FMT>
 struct MFrag;
 template <>
 struct MFrag<FP4G_NVFP4> {
-  u32x4 q[kPiecesNv];
-  u32x4 s[4];  // rows srow + v, 16 E4M3 block scales each
+  u32x4 q[4];
+  u32x2 s[4];  // row srow + v: E4M3 scales of blocks 8h .. 8h+7
 };
 template <>
 struct MFrag<FP4G_MXFP4> {
-  u32x4 q[kPiecesNv];
-  u32x4 s[2];  // rows srow + 2h, srow + 2h + 1: 8 E8M0 block scales each
+  u32x4 q[4];
+  uint32_t s[4];  // row srow + v: E8M0 scales of blocks 4h .. 4h+3
 };
 
+__device__ __forceinline__ uint32_t ld_stream1(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
 template <uint32_t FMT>
-__device__ __forceinline__ void load_mfrag(MFrag<FMT>& f, const uint8_t* tile, int lane, int srow) {
+__device__ __forceinline__ void load_mfrag(MFrag<FMT>& f, const uint8_t* tile, int half, int lane, int srow) {
 #pragma unroll
-  for (int j = 0; j < kPiecesNv; ++j) f.q[j] = ld_stream(tile + j * 1024 + lane * 16);
+  for (int j = 0; j < 4; ++j) f.q[j] = ld_stream(tile + (4 * half + j) * 1024 + lane * 16);
   if constexpr (FMT == FP4G_NVFP4) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) f.s[v] = ld_stream(tile + kCodeBytes + (srow + v) * 16);
+    for (int v = 0; v < 4; ++v) f.s[v] = ld_stream2(tile + kCodeBytes + (srow + v) * 16 + half * 8);
   } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) f.s[h] = ld_stream(tile + kCodeBytes + srow * 8 + h * 16);
+    for (int v = 0; v < 4; ++v) f.s[v] = ld_stream1(tile + kCodeBytes + (srow + v) * 8 + half * 4);
   }
 }
 
@@ -96,12 +103,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   const int srow = 16 * (lane & 3) + 4 * (lane >> 4);  // first of the lane's four output rows
   const int tok = (lane >> 2) & 3;                     // the lane's token within a set
   const int64_t tile0 = (int64_t)g * p.C;
-  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE; };
+  // items (chunk, half, matrix), matrix fastest: with NMAT = 2 the even items
+  // are gate, the odd ones up
+  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / (2 * NMAT)) * TILE; };
+  auto item_half = [&](int it) { return (it / NMAT) & 1; };
 
   // first fragment in flight before the input is staged
-  const int n_items = (c1 - c0) * NMAT;
+  const int n_items = (c1 - c0) * 2 * NMAT;
   MFrag<FMT> fa, fb;
-  if (n_items > 0) load_mfrag<FMT>(fa, item_tile(0), lane, srow);
+  if (n_items > 0) load_mfrag<FMT>(fa, item_tile(0), item_half(0), lane, srow);
 
   // stage x[m][256 wg_c0 ..) for m < M (zero past d_in), then the zero area; all
   // loads are issued before the first LDS store
@@ -152,24 +162,26 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   // items alternate matrices (NMAT = 2), so fragment fa always holds matrix 0
   // and fb the last one: each call names its accumulators statically
   auto consume = [&](const MFrag<FMT>& f, int it, f32x4(&ac)[NSET]) {
-    const int cc = c0 + it / NMAT - wg_c0;  // chunk within the staged range
+    const int cc = c0 + it / (2 * NMAT) - wg_c0;  // chunk within the staged range
+    const int half = item_half(it);
     int bb[NSET];
 #pragma unroll
     for (int q = 0; q < NSET; ++q) bb[q] = boff[q] + (bval[q] ? cc * 512 : 0);
 #pragma unroll
-    for (int j = 0; j < kPiecesNv; ++j) {
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * half + jj;  // slot within the chunk
       if constexpr (FMT == FP4G_NVFP4) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {  // 16-column blocks 2j, 2j+1 = dwords 2h, 2h+1
-          const bf16x8 a0 = e2m1x8_bf16(f.q[j][2 * h]);
-          const bf16x8 a1 = e2m1x8_bf16(f.q[j][2 * h + 1]);
-          const int b = 2 * j + h;  // block within the chunk: dword b/4, byte b%4 of a row's 16 scales
+          const bf16x8 a0 = e2m1x8_bf16(f.q[jj][2 * h]);
+          const bf16x8 a1 = e2m1x8_bf16(f.q[jj][2 * h + 1]);
+          const int lb = 2 * jj + h;  // block within the half: dword lb/4, byte lb%4 of s[v]
           float sc[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const uint32_t sdw = f.s[v][b >> 2];
-            sc[v] = (b & 3) == 0 ? e4m3_f32<0>(sdw) : (b & 3) == 1 ? e4m3_f32<1>(sdw)
-                  : (b & 3) == 2 ? e4m3_f32<2>(sdw) : e4m3_f32<3>(sdw);
+            const uint32_t sdw = f.s[v][lb >> 2];
+            sc[v] = (lb & 3) == 0 ? e4m3_f32<0>(sdw) : (lb & 3) == 1 ? e4m3_f32<1>(sdw)
+                  : (lb & 3) == 2 ? e4m3_f32<2>(sdw) : e4m3_f32<3>(sdw);
           }
 #pragma unroll
           for (int q = 0; q < NSET; ++q) {
@@ -182,13 +194,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
           }
         }
       } else {
-        // one 32-column block per slot: byte j%4 of dword j/4 of a row's 8 scales
+        // one 32-column block per slot: byte jj of s[v]
         int e[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) e[v] = (int)((f.s[v >> 1][(v & 1) * 2 + (j >> 2)] >> (8 * (j & 3))) & 0xffu) - 127;
+        for (int v = 0; v < 4; ++v) e[v] = (int)((f.s[v] >> (8 * jj)) & 0xffu) - 127;
         bf16x8 av[4];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) av[d] = e2m1x8_bf16(f.q[j][d]);
+        for (int d = 0; d < 4; ++d) av[d] = e2m1x8_bf16(f.q[jj][d]);
 #pragma unroll
         for (int q = 0; q < NSET; ++q) {
           const int off = bb[q] + 32 * j * 2;
@@ -210,13 +222,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   if (n_items > 0) {
     int it = 0;
     for (; it + 2 < n_items; it += 2) {
-      load_mfrag<FMT>(fb, item_tile(it + 1), lane, srow);
+      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane, srow);
       consume(fa, it, acc[0]);
-      load_mfrag<FMT>(fa, item_tile(it + 2), lane, srow);
+      load_mfrag<FMT>(fa, item_tile(it + 2), item_half(it + 2), lane, srow);
       consume(fb, it + 1, acc[NMAT - 1]);
     }
     if (it + 1 < n_items) {
-      load_mfrag<FMT>(fb, item_tile(it + 1), lane, srow);
+      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane, srow);
       consume(fa, it, acc[0]);
       consume(fb, it + 1, acc[NMAT - 1]);
     } else {
