@@ -18,7 +18,7 @@ __all__ = [
     "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
     "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
-    "validate", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
+    "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
     "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH", "Stream",
 ]
 
@@ -101,6 +101,7 @@ _SIGNATURES = {
     "fp4g_packed_bytes": (_U64, [_U32, _I32, _I32]),
     "fp4g_pack": (_I32, [_U32, _I32, _I32, _VP, _VP, _F, _VP, _U64, ctypes.POINTER(WeightDesc), _VP]),
     "fp4g_unpack": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP, _VP]),
+    "fp4g_quantize": (_I32, [_U32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _U64, _VP]),
     "fp4g_validate": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP]),
     "fp4g_workspace_bytes": (_U64, [_I32, _VP, _I32]),
     "fp4_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP, _VP, _U64, _VP]),
@@ -225,6 +226,25 @@ def pack(fmt: int, codes: torch.Tensor, scales: torch.Tensor, tensor_scale: floa
                            out.data_ptr() + offset, out.numel() - offset, ctypes.byref(desc), _stream(stream)),
            "fp4g_pack")
     return PackedWeight(desc, out)
+
+
+def quantize(fmt: int, w: torch.Tensor, stream=None):
+    """Quantise a bf16 matrix [d_out, d_in] on the device: returns (codes, scales,
+    tensor_scale) in the logical layout `pack` takes."""
+    assert w.dtype == torch.bfloat16 and w.dim() == 2 and w.is_contiguous()
+    d_out, d_in = w.shape
+    dev = w.device
+    if fmt == FP8_ROW:
+        codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+        scales = torch.empty(d_out, dtype=torch.float32, device=dev)
+    else:
+        codes = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((d_out, d_in // (16 if fmt == NVFP4 else 32)), dtype=torch.uint8, device=dev)
+    ts = torch.empty(1, dtype=torch.float32, device=dev)
+    scratch = torch.empty(256, dtype=torch.uint8, device=dev)
+    _check(lib().fp4g_quantize(fmt, d_out, d_in, w.data_ptr(), codes.data_ptr(), scales.data_ptr(), ts.data_ptr(),
+                               scratch.data_ptr(), 256, _stream(stream)), "fp4g_quantize")
+    return codes, scales, float(ts.item())
 
 
 def unpack(W: PackedWeight, stream=None):

@@ -184,6 +184,28 @@ int32_t fp4g_pack(uint32_t format, int32_t d_out, int32_t d_in, const void* code
                   const void* scales_dev, float tensor_scale, void* packed_dev,
                   uint64_t packed_bytes, fp4g_weight* out_host, void* stream);
 
+/* Quantise a bf16 matrix w_dev [d_out][d_in] (d_in % 32 == 0; finite values) into
+ * the logical codes and scales fp4g_pack takes (feed, section "Fewer bytes per
+ * weight: NVFP4": each block's largest magnitude maps to 6, the E2M1 maximum;
+ * E4M3 block scales; one FP32 tensor scale bringing them into E4M3's range):
+ *   NVFP4:   s_T = amax(w) / (6 * 448) (1 if all zero); block scale code =
+ *            E4M3(amax_block / (6 s_T)); element = E2M1(w / (s_block * s_T)),
+ *            0 where the block scale is 0.
+ *   MXFP4:   per 32 weights the smallest power of two 2^e with amax/2^e <= 6,
+ *            E8M0 code e + 127 (clamped to 0..254; 127 for an all-zero block);
+ *            element = E2M1(w / 2^e).
+ *   FP8_ROW: per row s = amax_row / 448 (1 if all zero) as the FP32 row scale;
+ *            element = E4M3(w / s).
+ * Rounding: nearest, ties to the even code, saturating (E2M1 at 6, E4M3 at 448);
+ * a value that rounds to zero gets the +0 code.  Scale arithmetic in FP32, one
+ * rounding per operation in the order written.
+ *   codes_dev   NVFP4/MXFP4: u8[d_out][d_in/2]; FP8_ROW: u8[d_out][d_in].
+ *   scales_dev  u8[d_out][d_in/16] (NVFP4), u8[d_out][d_in/32] (MXFP4), f32[d_out].
+ *   tensor_scale_dev  NULL or one f32: s_T (NVFP4), 1.0 otherwise.
+ *   ws_dev      NVFP4 only: >= 256 bytes of scratch (any contents); else unused. */
+int32_t fp4g_quantize(uint32_t format, int32_t d_out, int32_t d_in, const uint16_t* w_dev, void* codes_dev,
+                      void* scales_dev, float* tensor_scale_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
+
 /* Inverse of fp4g_pack: write the logical codes and scales of W. */
 int32_t fp4g_unpack(const fp4g_weight* W_host, void* codes_dev, void* scales_dev, void* stream);
 

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     L = fg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -181,6 +181,25 @@ def test_lmhead_argmax_error_paths():
     assert call(lg=FAKE + 1024) == E_ALIAS        # logits over the weights
     assert call(i=V) == E_ALIAS                   # the two outputs overlap
     assert L.fp4g_workspace_bytes(fg.OP_LMHEAD_ARGMAX, ctypes.byref(good_desc()), 1) == 0
+
+
+def test_quantize_error_paths():
+    L = fg.lib()
+    W, C, S, T, WS = FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
+
+    def q(fmt=fg.NVFP4, d_out=64, d_in=256, w=W, c=C, s=S, t=T, ws=WS, wsb=256):
+        return L.fp4g_quantize(fmt, d_out, d_in, w, c, s, t, ws, wsb, None)
+
+    assert q(fmt=4) == E_FORMAT
+    assert q(w=None) == E_NULL
+    assert q(c=None) == E_NULL
+    assert q(d_in=48) == E_SHAPE
+    assert q(d_out=0) == E_SHAPE
+    assert q(w=W + 2) == E_ALIGN
+    assert q(ws=None) == E_NULL                   # NVFP4 needs the scratch
+    assert q(wsb=255) == E_WORKSPACE
+    assert q(c=W + 1024) == E_ALIAS               # codes over the input
+    assert q(s=C) == E_ALIAS                      # scales over the codes
 
 
 def test_gate_up_error_paths():

@@ -244,6 +244,56 @@ def test_gate_up_silu_matches_oracle(fmt, M, path):
         check_h(H, hg, hu, bits(X))
 
 
+# ---- load-time quantisers ------------------------------------------------------------------------
+from oracle import quant as oq  # noqa: E402
+
+
+def quant_inputs(d_out, d_in, seed):
+    """Normal weights with outliers, an all-zero block, tiny values (E4M3/E8M0
+    subnormal range) and mixed signs, as bf16."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    w = torch.randn((d_out, d_in), generator=g)
+    w[0, :32] = 0.0
+    w[1, 5] = 300.0
+    w[2, :64] *= 1e-5
+    w[3] = torch.randn(d_in, generator=g) * 1e-30
+    return w.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4, fg.FP8_ROW])
+@pytest.mark.parametrize("shape", [(130, 544), (256, 2048)])
+def test_quantize_matches_oracle_bit_exact(fmt, shape):
+    log("quantize", fmt, shape)
+    w = quant_inputs(*shape, seed=shape[0] + fmt)
+    codes, scales, ts = fg.quantize(fmt, w.to(DEV))
+    rc, rs, rts = oq.quantize(fmt, w.view(torch.int16).numpy().view(np.uint16))
+    assert ts == rts
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_quantize_then_product():
+    """Quantise -> pack -> product: equals the oracle's product of the quantised
+    matrix, and stays near the bf16 matrix's product."""
+    log("quantize -> gemv")
+    w = quant_inputs(192, 1024, 7).to(DEV)
+    x = datagen.bf16_normal((1024,), 8, device=DEV)
+    exact = (w.double() @ x.double()).cpu().numpy()
+    for fmt in (fg.NVFP4, fg.MXFP4):
+        codes, scales, ts = fg.quantize(fmt, w)
+        W = fg.pack(fmt, codes, scales, ts)
+        y = fg.fp4_gemv(W, x)
+        host = {"format": fmt, "codes": codes.cpu(), "scales": scales.cpu(), "tensor_scale": ts}
+        check_product(y, host, bits(x)[None, :])
+        rel = np.linalg.norm(y.cpu().double().numpy() - exact) / np.linalg.norm(exact)
+        assert rel < 0.2, (fmt, rel)
+    codes, scales, _ = fg.quantize(fg.FP8_ROW, w)
+    W = fg.pack(fg.FP8_ROW, codes, scales)
+    y = fg.fp8_lmhead_gemv(W, x)
+    rel = np.linalg.norm(y.cpu().double().numpy().ravel() - exact) / np.linalg.norm(exact)
+    assert rel < 0.05, rel
+
+
 # ---- special cases: bit-exact ------------------------------------------------------------------
 
 

@@ -384,3 +384,89 @@ def test_layout_reference_places_each_element(fmt):
     if fmt == oracle.FP8_ROW:
         rs = img[R * C * tile:].view(np.float32)
         assert np.array_equal(rs[:d_out], scales) and not rs[d_out:].any()
+
+
+# ---- load-time quantisers (oracle/quant.py) ---------------------------------------------------
+from oracle import quant as Q  # noqa: E402
+
+
+def test_quant_e2m1_rounding_ties_and_saturation():
+    # midpoints of the pages' grid 0, .5, 1, 1.5, 2, 3, 4, 6 go to the even code
+    cases = {0.0: 0, 0.2: 0, 0.25: 0, 0.26: 1, 0.75: 2, 1.25: 2, 1.3: 3, 1.75: 4, 2.5: 4, 2.6: 5,
+             3.5: 6, 5.0: 6, 5.1: 7, 6.0: 7, 7.0: 7, 100.0: 7, -0.75: 10, -6.5: 15, -0.1: 0}
+    for q, code in cases.items():
+        assert Q.e2m1_rne(q) == code, q
+
+
+def test_quant_e4m3_rounding_matches_torch():
+    import torch
+    vals = Q._E4M3
+    mids = (vals[:-1] + vals[1:]) / 2          # every tie
+    rng = np.random.default_rng(3)
+    ts = np.concatenate([vals, mids, rng.uniform(0, 448, 2000), rng.uniform(0, 0.02, 500)]).astype(np.float32)
+    ref = torch.from_numpy(ts).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([vals[Q.e4m3_rne(float(t))] for t in ts])
+    assert np.array_equal(got, ref)
+    assert Q.e4m3_rne(448.0) == 126 and Q.e4m3_rne(470.0) == 126 and Q.e4m3_rne(1e6) == 126
+
+
+def _bf16_bits(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_quant_exactly_representable_inputs_round_trip():
+    """Weights built from codes and scales with every block's largest magnitude at
+    6 (and, for NVFP4, one block scale at 448 with a power-of-two tensor scale)
+    come back with the same codes and scales."""
+    rng = np.random.default_rng(5)
+    d_out, d_in = 6, 96
+    for fmt, blk in ((Q.NVFP4, 16), (Q.MXFP4, 32)):
+        el = rng.integers(0, 16, (d_out, d_in))
+        el[:, ::blk] = rng.choice([7, 15], (d_out, d_in // blk))    # a +-6 in every block
+        if fmt == Q.NVFP4:
+            sc = rng.integers(1, 127, (d_out, d_in // blk))
+            sc[0, 0] = 126                                            # 448: sets the tensor scale
+            s_t = 2.0 ** -7
+            sv = Q._E4M3[sc] * s_t
+        else:
+            sc = rng.integers(120, 135, (d_out, d_in // blk))
+            s_t = 1.0
+            sv = 2.0 ** (sc - 127.0)
+        mag = Q._E2M1[el & 7] * np.where(el & 8, -1.0, 1.0)
+        w = mag * np.repeat(sv, blk, axis=1)
+        codes, scales, ts = Q.quantize(fmt, _bf16_bits(w))
+        el_ref = np.where((el & 7) == 0, 0, el)                     # -0 comes back as +0
+        assert ts == s_t
+        assert np.array_equal(scales, sc.astype(np.uint8))
+        assert np.array_equal(codes, (el_ref[:, 0::2] | (el_ref[:, 1::2] << 4)).astype(np.uint8))
+    # FP8 rows: one element at 448 per row, power-of-two row scales
+    c = rng.integers(0, 127, (d_out, d_in))
+    c[:, 0] = 126
+    sgn = rng.integers(0, 2, (d_out, d_in))
+    s_row = 2.0 ** rng.integers(-12, 0, d_out)
+    w = Q._E4M3[c] * np.where(sgn, -1.0, 1.0) * s_row[:, None]
+    codes, scales, _ = Q.quantize(Q.FP8_ROW, _bf16_bits(w))
+    ref = np.where(sgn & (c != 0), 0x80 | c, c).astype(np.uint8)
+    assert np.array_equal(scales, s_row.astype(np.float32)) and np.array_equal(codes, ref)
+
+
+def test_quant_nvfp4_error_within_a_grid_step():
+    """Reconstruction error of random weights is at most one E2M1 step (the
+    largest step, 2, is between 4 and 6) times the block's scale, and every
+    block's largest magnitude decodes to 4 or 6 (the pages: it maps to 6, up to
+    the E4M3 rounding of the scale)."""
+    rng = np.random.default_rng(6)
+    w = rng.standard_normal((8, 128)).astype(np.float32)
+    w[3, 20] = 40.0                                                  # an outlier
+    bits = _bf16_bits(w)
+    wb = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, scales, ts = Q.quantize(Q.NVFP4, bits)
+    el = np.stack([codes & 15, codes >> 4], axis=-1).reshape(8, 128)
+    val = Q._E2M1[el & 7] * np.where(el & 8, -1.0, 1.0)
+    sb = np.repeat(Q._E4M3[scales], 16, axis=1) * ts
+    assert np.all(np.abs(wb - val * sb) <= 1.0 * sb + 1e-12)
+    for r in range(8):
+        for b in range(8):
+            k = b * 16 + int(np.argmax(np.abs(wb[r, b * 16:(b + 1) * 16])))
+            assert Q._E2M1[el[r, k] & 7] in (4.0, 6.0), (r, b)
