@@ -513,8 +513,10 @@ inline Plan plan_for(int64_t R, int64_t C, int nmat, int M, int waves_per_cu = 0
 // Small products (a few thousand tiles, such as the experts a token picked) are
 // bound by the chain of round trips in each wave, not by bandwidth: this plan
 // minimises the rounds of workgroups times the chunks each wave streams in
-// turn, plus half a chunk per level of the split-K tree; among equals the
-// fewest waves.  nws lists the workgroup sizes the kernel is built for.
+// turn, plus half a chunk per level of the split-K tree, plus half the missing
+// fraction when fewer workgroups than CUs leave some CUs idle (the last tiles'
+// compute then piles up on the busy ones); among equals the fewest waves.  nws
+// lists the workgroup sizes the kernel is built for.
 inline Plan plan_latency(int64_t R, int64_t C, int waves_per_cu, std::initializer_list<int> nws) {
   Plan best = plan_nw4(R, C);
   double best_cost = 1e30;
@@ -529,7 +531,8 @@ inline Plan plan_latency(int64_t R, int64_t C, int waves_per_cu, std::initialize
       const int64_t per_round = (int64_t)kCUs * (waves_per_cu / nw) * nw;
       const int64_t rounds = (waves + per_round - 1) / per_round;
       const int64_t per_wave = (wg_chunks + nw - 1) / nw;
-      const double cost = (double)(rounds * per_wave) + 0.5 * tree_depth(S);
+      const double idle = R * S < kCUs ? (double)kCUs / (double)(R * S) - 1.0 : 0.0;
+      const double cost = (double)(rounds * per_wave) + 0.5 * tree_depth(S) + 0.5 * idle;
       if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && waves < best_waves)) {
         best = Plan{(int)S, (int)wg_chunks, nw};
         best_cost = cost;
