@@ -31,18 +31,29 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBPS = 8000.0
 
 
+# The files the dense and FP8-row product kernels (and their launch planning) are
+# built from; the committed counter summary is valid only while they are unchanged.
+TRAFFIC_SOURCES = ("bit_weight_gemv_fp4_amd/build.py", "bit_weight_gemv_fp4_amd/csrc/common.hpp",
+                   "bit_weight_gemv_fp4_amd/csrc/gemv_kernel.hpp", "bit_weight_gemv_fp4_amd/csrc/gemv_mfma.hpp",
+                   "bit_weight_gemv_fp4_amd/csrc/gemv.hip", "bit_weight_gemv_fp4_amd/csrc/gemv_nvfp4.hip",
+                   "bit_weight_gemv_fp4_amd/csrc/gemv_fp8.hip")
+
+
+def traffic_sources_hash():
+    import hashlib
+
+    return hashlib.sha256(b"".join((ROOT / q).read_bytes() for q in TRAFFIC_SOURCES)).hexdigest()[:16]
+
+
 def counter_traffic(kind):
     """HBM bytes per launch of `kind` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary (profiles/counters.json), or None when the kernel sources
     have changed since the counters were taken."""
-    import hashlib
-
     p = ROOT / "profiles" / "counters.json"
     if not p.exists():
         return None
     d = json.loads(p.read_text())
-    src = sorted((ROOT / "bit_weight_gemv_fp4_amd" / "csrc").glob("*"))
-    h = hashlib.sha256(b"".join(q.read_bytes() for q in src)).hexdigest()[:16]
+    h = traffic_sources_hash()
     k = d.get("kernels", {}).get(kind)
     if d.get("source_sha256_16") != h or not k:
         return None
