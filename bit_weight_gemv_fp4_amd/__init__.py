@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
-    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "Fp4gError", "PackedWeight", "MoeLayer",
+    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "MAX_M", "MAX_M_WIDE", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
     "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
     "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH", "Stream",
@@ -26,6 +26,7 @@ NVFP4, MXFP4, FP8_ROW = 1, 2, 3
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 OP_GEMV, OP_GATE_UP, OP_MOE, OP_LMHEAD, OP_GROUPED, OP_LMHEAD_ARGMAX = 1, 2, 3, 4, 5, 6
 MAX_GROUP = 4
+MAX_M, MAX_M_WIDE = 8, 16  # vectors per call; the wider range on the matrix-core path only
 LAYOUT_TILE64x256 = 0x46344731
 
 LIB_PATH = Path(__file__).resolve().parent / "libfp4gemv.so"
@@ -318,7 +319,8 @@ def fp4_gemv(W: PackedWeight, x: torch.Tensor, y: torch.Tensor | None = None, ws
 
 def fp4_skinny_gemm(W: PackedWeight, X: torch.Tensor, Y: torch.Tensor | None = None, path: int = PATH_AUTO,
                     ws=None, stream=None) -> torch.Tensor:
-    """Y[m] = W X[m] for X bf16 [M, d_in], M in 1..8; returns float32 [M, d_out]."""
+    """Y[m] = W X[m] for X bf16 [M, d_in], M in 1..16 (above 8 on the matrix-core path);
+    returns float32 [M, d_out]."""
     M = X.shape[0]
     if Y is None:
         Y = torch.empty((M, W.d_out), dtype=torch.float32, device=X.device)

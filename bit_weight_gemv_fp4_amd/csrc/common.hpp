@@ -26,7 +26,8 @@ constexpr int kTileNv = 9216;       // 8 KiB codes + 64 x 16 B E4M3 scales
 constexpr int kTileMx = 8704;       // 8 KiB codes + 64 x 8 B E8M0 scales
 constexpr int kTileF8 = 16384;      // 16 KiB codes (row scales follow all tiles)
 constexpr int kCodeBytes = 8192;
-constexpr int kMaxM = 8;
+constexpr int kMaxM = 8;       // vectors per call: VALU kernels, MoE, FP8 rows
+constexpr int kMaxMWide = 16;  // NVFP4/MXFP4 products on the matrix-core kernel
 constexpr int kWavesPerWg = 4;
 constexpr int kThreads = 256;
 // Every workspace starts with a fixed region of hand-off counters.  No call ever

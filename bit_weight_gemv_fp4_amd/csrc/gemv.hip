@@ -31,8 +31,11 @@ static bool use_mfma(int32_t path, uint32_t format, int M) {
   return M >= kMfmaMinM;
 }
 
-static bool valid_path(int32_t path, bool fp4) {
-  if (path == FP4G_PATH_AUTO || path == FP4G_PATH_VALU) return true;
+// A path the call can run: MFMA only for NVFP4/MXFP4; VALU only up to kMaxM
+// vectors (wider verify blocks run on the matrix cores alone).
+static bool valid_path(int32_t path, bool fp4, int M) {
+  if (path == FP4G_PATH_AUTO) return true;
+  if (path == FP4G_PATH_VALU) return M <= kMaxM;
   return path == FP4G_PATH_MFMA && fp4;
 }
 
@@ -61,14 +64,14 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   if (!X) return FP4G_E_NULL;
   for (int i = 0; i < n; ++i)
     if (!Y[i]) return FP4G_E_NULL;
-  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
+  if (M < 1 || M > (want_fp4 ? kMaxMWide : kMaxM)) return FP4G_E_SHAPE;
   if (!aligned(X, 16)) return FP4G_E_ALIGN;
   for (int i = 0; i < n; ++i)
     if (!aligned(Y[i], 16)) return FP4G_E_ALIGN;
   int64_t R_total = 0;
   for (int i = 0; i < n; ++i) R_total += row_groups(W[i]->d_out);
   const int64_t C = chunks(W[0]->d_in);
-  if (!valid_path(path, want_fp4)) return FP4G_E_PATH;
+  if (!valid_path(path, want_fp4, M)) return FP4G_E_PATH;
   const bool mfma = use_mfma(path, W[0]->format, M);
   const uint64_t need = gemv_ws_bytes_any(R_total, C, 1, M);
   const fp4g_status wst = check_ws(ws, ws_bytes, need);
@@ -109,8 +112,8 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (mfma)
-    e = W[0]->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, M), s)
-                                   : launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, M), s);
+    e = W[0]->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, W[0]->format, 1, M), s)
+                                   : launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, W[0]->format, 1, M), s);
   else if (W[0]->format == FP4G_NVFP4)
     e = launch_m<FP4G_NVFP4, 1, EPI_STORE>(M, pl.nw, p, grid, s);
   else if (W[0]->format == FP4G_MXFP4)
@@ -243,8 +246,8 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   if (Wg->format != Wu->format) return FP4G_E_FORMAT;
   if (Wg->d_out != Wu->d_out || Wg->d_in != Wu->d_in) return FP4G_E_SHAPE;
   if (!X || !H) return FP4G_E_NULL;
-  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
-  if (!valid_path(path, true)) return FP4G_E_PATH;
+  if (M < 1 || M > kMaxMWide) return FP4G_E_SHAPE;
+  if (!valid_path(path, true, M)) return FP4G_E_PATH;
   if (!aligned(X, 16) || !aligned(H, 16)) return FP4G_E_ALIGN;
   const bool mfma = use_mfma(path, Wg->format, M);
   const int64_t R = row_groups(Wg->d_out), C = chunks(Wg->d_in);
@@ -278,8 +281,8 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (mfma)
-    e = Wg->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, M), s)
-                                 : launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, M), s);
+    e = Wg->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, Wg->format, 2, M), s)
+                                 : launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, Wg->format, 2, M), s);
   else
     e = Wg->format == FP4G_NVFP4 ? launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s)
                                  : launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s);
@@ -287,7 +290,8 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
 }
 
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
-  if (!desc || M < 1 || M > kMaxM) return 0;
+  if (!desc || M < 1 || M > kMaxMWide) return 0;
+  if (M > kMaxM && op != FP4G_OP_GEMV && op != FP4G_OP_GATE_UP && op != FP4G_OP_GROUPED) return 0;
   if (op == FP4G_OP_MOE) return moe_ws_bytes((const fp4g_moe*)desc, M);
   if (op == FP4G_OP_LMHEAD_ARGMAX) return check_weight((const fp4g_weight*)desc, false) == FP4G_OK ? argmax_ws_bytes() : 0;
   if (op == FP4G_OP_GROUPED) {

@@ -456,8 +456,7 @@ struct Plan {
 // Four-wave workgroups: enough waves to cover HBM latency on all 256 CUs (about
 // eight per CU), with at least one chunk per wave; chunks spread evenly over the
 // S workgroups.  (The MoE and matrix-core kernels use this split.)
-inline Plan plan_nw4(int64_t R, int64_t C) {
-  const int64_t target_waves = 2048;
+inline Plan plan_nw4(int64_t R, int64_t C, int64_t target_waves = 2048) {
   int64_t q = (R * C) / target_waves;  // chunks per wave
   if (q < 1) q = 1;
   int64_t S = (C + kWavesPerWg * q - 1) / (kWavesPerWg * q);

@@ -1,29 +1,34 @@
-// gemv_mfma.hpp -- the matrix-core variant of the decode product for M = 1..8
+// gemv_mfma.hpp -- the matrix-core variant of the decode product for M = 1..16
 // vectors (the verify step of speculative decoding scores K+1 positions against
-// the same weights: feed, section "MTP: the drafter inside the checkpoint").
+// the same weights: feed, sections "MTP: the drafter inside the checkpoint" and
+// "More tokens per weight read", where blocks of up to 10 drafts are verified).
 //
 // Same packed tiles, same work split and same split-K exchange tree as the VALU
 // kernel (gemv_kernel.hpp); only the arithmetic differs.  The VALU kernel issues
-// one v_dot2 per weight pair and token, so its issue rate falls short of HBM
-// from M = 4 on.  Here the products run on v_mfma_f32_16x16x32_bf16:
+// one v_dot2 per weight pair and vector, so its issue rate falls short of HBM
+// from M = 4 on.  Here the products run on v_mfma_f32_16x16x32_bf16 with the
+// input as the A operand (16 rows: vectors) and the weights as the B operand
+// (16 columns: weight rows), so one instruction covers 16 weight rows x 32
+// columns for up to 16 vectors:
 //
-//  * A operand = weights, as loaded: lane i holds 32 columns of row i of the
-//    64-row group, so the A row of lane i is i % 16 and its K group is i / 16.
-//    The four K groups therefore carry four different weight rows.
-//  * B operand = a block-diagonal spread of the input: column c of B belongs to
-//    token c / 4 and K group c % 4, and is nonzero only in that K group.  Then
-//    D[r][c] = sum over 8 columns of W[16 (c % 4) + r][k] x_{c/4}[k]: every dot
-//    product lands in its own output element, four tokens per instruction (two
-//    instructions for M = 5..8).  Three quarters of each B are zeros; the matrix
-//    cores still have about 5x the rate needed.
-//  * E2M1 -> bf16 is exact (v_cvt_scalef32_pk_bf16_fp4), products are exact in
-//    FP32.  One block (16 columns NVFP4, 32 MXFP4) is summed by chained MFMAs into
-//    a fresh accumulator, then scaled once per row on the VALU: lane i's outputs
-//    are rows 16 (i % 4) + 4 (i / 16) + 0..3 of token (i / 4) % 4, so it loads
-//    those four rows' block scales.  Tiles stream as two halves (4 code slots
-//    and their scales) to keep the double-buffered fragments in 48 VGPRs.
-//  * The input columns of a workgroup's chunk range are staged in LDS (zero past
-//    d_in), with a 512-byte zero area that the off-diagonal lanes read.
+//  * B operand: the MFMA wants lane i to hold 8 consecutive columns (K group
+//    i / 16) of weight row i % 16, while the packed layout gives lane l all 32
+//    columns of one 1 KiB slot for row l.  A 4 x 4 transpose of dwords between
+//    the four 16-lane groups (two v_permlane32_swap and two v_permlane16_swap)
+//    turns the slot into four B operands, one per 16-row block of the 64-row
+//    group.  E2M1 -> bf16 is exact (v_cvt_scalef32_pk_bf16_fp4 with scale 1).
+//  * A operand: lane i reads 8 input columns of vector i % 16 (K group i / 16)
+//    from the LDS staging of the workgroup's input range; lanes with no vector
+//    read a zero area.
+//  * Block scales are applied in FP32 to each MFMA result, per weight row.  An
+//    MXFP4 block is one slot (32 columns): one MFMA per 16-row block.  An NVFP4
+//    block is half a slot: with M <= 8 the A rows 0..7 carry the vectors over
+//    the slot's first 16 columns and rows 8..15 over the last 16 (zeros in the
+//    other half), so one MFMA still gives both blocks' sums separately; with
+//    M > 8 each block takes its own MFMA.
+//  * A work item is kMfmaSlots code slots of one tile (half of it) and their
+//    scales, double-buffered.  The reduction across waves reuses the input's
+//    LDS area, so a workgroup holds no more LDS than its staged input.
 #pragma once
 #include "gemv_kernel.hpp"
 
@@ -32,23 +37,21 @@ namespace fp4g {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMfmaXBytes = 40960;  // LDS for the staged input of one workgroup (with the
-                                    // 16 KiB reduction buffer: under 64 KiB)
+constexpr int kMfmaXBytes = 40960;  // LDS for the staged input of one workgroup
 constexpr int kZeroBytes = 512;     // one chunk row of zeros
+constexpr int kMfmaRedOwn = 0;      // values per lane up to which the reduction has its own LDS
 
-// A fragment is half a tile: code slots 4h .. 4h+3 of lane i's row, and the
-// block scales of those slots for the lane's four output rows srow .. srow+3.
+constexpr int kMfmaSlots = 4;  // code slots per work item (half a tile: fewer registers, more waves)
+
+// A fragment: code slots SL h .. SL h + SL - 1 of lane l's row (as stored), and
+// the block scales of those slots for the rows 16 r + (l % 16), r < 4, whose
+// sums the lane computes (one byte per block, SW dwords per row).
 template <uint32_t FMT>
-struct MFrag;
-template <>
-struct MFrag<FP4G_NVFP4> {
-  u32x4 q[4];
-  u32x2 s[4];  // row srow + v: E4M3 scales of blocks 8h .. 8h+7
-};
-template <>
-struct MFrag<FP4G_MXFP4> {
-  u32x4 q[4];
-  uint32_t s[4];  // row srow + v: E8M0 scales of blocks 4h .. 4h+3
+struct MFrag {
+  static constexpr int SL = kMfmaSlots;
+  static constexpr int SW = FMT == FP4G_NVFP4 ? SL / 2 : SL / 4;
+  u32x4 q[SL];
+  uint32_t s[4][SW];
 };
 
 __device__ __forceinline__ uint32_t ld_stream1(const void* p) {
@@ -56,19 +59,28 @@ __device__ __forceinline__ uint32_t ld_stream1(const void* p) {
 }
 
 template <uint32_t FMT>
-__device__ __forceinline__ void load_mfrag(MFrag<FMT>& f, const uint8_t* tile, int half, int lane, int srow) {
+__device__ __forceinline__ void load_mfrag(MFrag<FMT>& f, const uint8_t* tile, int half, int lane) {
+  constexpr int SL = MFrag<FMT>::SL, SW = MFrag<FMT>::SW;
+  const int c = lane & 15;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.q[j] = ld_stream(tile + (4 * half + j) * 1024 + lane * 16);
-  if constexpr (FMT == FP4G_NVFP4) {
+  for (int j = 0; j < SL; ++j) f.q[j] = ld_stream(tile + (SL * half + j) * 1024 + lane * 16);
+  constexpr int rowb = FMT == FP4G_NVFP4 ? 16 : 8;  // scale bytes per row and tile
 #pragma unroll
-    for (int v = 0; v < 4; ++v) f.s[v] = ld_stream2(tile + kCodeBytes + (srow + v) * 16 + half * 8);
-  } else {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) f.s[v] = ld_stream1(tile + kCodeBytes + (srow + v) * 8 + half * 4);
+  for (int r = 0; r < 4; ++r) {
+    const uint8_t* sp = tile + kCodeBytes + (16 * r + c) * rowb + half * SW * 4;
+    if constexpr (SW == 4) {
+      const u32x4 v = ld_stream(sp);
+      f.s[r][0] = v[0], f.s[r][1] = v[1], f.s[r][2] = v[2], f.s[r][3] = v[3];
+    } else if constexpr (SW == 2) {
+      const u32x2 v = ld_stream2(sp);
+      f.s[r][0] = v[0], f.s[r][1] = v[1];
+    } else {
+      f.s[r][0] = ld_stream1(sp);
+    }
   }
 }
 
-// Eight E2M1 codes (one dword: columns 8d .. 8d+7 of the lane's 32) as bf16.
+// Eight E2M1 codes (one dword: 8 consecutive columns) as bf16.
 __device__ __forceinline__ bf16x8 e2m1x8_bf16(uint32_t dw) {
   const bf16x2 p0 = e2m1x2_bf16<0>(dw), p1 = e2m1x2_bf16<1>(dw);
   const bf16x2 p2 = e2m1x2_bf16<2>(dw), p3 = e2m1x2_bf16<3>(dw);
@@ -79,13 +91,38 @@ __device__ __forceinline__ bf16x8 lds_bf16x8(const uint8_t* base, int off) {
   return *reinterpret_cast<const bf16x8*>(base + off);
 }
 
+// Lane group g = l / 16 holds dword d of its rows in q[d]; afterwards lane group g
+// holds, in q[r], dword g of the rows of lane group r (the same l % 16): the
+// B operand of 16-row block r.
+__device__ __forceinline__ void transpose_slot(u32x4& q) {
+  const auto a = __builtin_amdgcn_permlane32_swap(q[0], q[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(q[1], q[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  q = u32x4{c[0], c[1], d[0], d[1]};
+}
+
+// Sum of x over lane i and lane i +- 32 (both halves end with the sum).
+__device__ __forceinline__ float add_halves(float x, int lane) {
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return x + __uint_as_float(lane < 32 ? t[1] : t[0]);
+}
+
 template <uint32_t FMT, int M, int NMAT, int EPI>
 __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
-  constexpr int NSET = (M + 3) / 4;  // MFMA column sets of four tokens
-  constexpr int NV = NMAT * NSET * 4;
+  // NVFP4 with up to 8 vectors: both blocks of a slot in one MFMA (A rows 8..15
+  // carry the second block); the outputs of lanes i and i + 32 then add up
+  constexpr bool PACK2 = FMT == FP4G_NVFP4 && M <= 8;
+  constexpr bool TWO = FMT == FP4G_NVFP4 && M > 8;  // one MFMA per NVFP4 block
+  constexpr int NR = PACK2 ? 2 : 4;                  // 16-row blocks per lane at the end
+  constexpr int NV = NMAT * NR * 4;                  // values per lane at the end
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : kTileMx;
-  __shared__ float red[kWavesPerWg][NV][64];
+  // Cross-wave reduction buffer: its own array up to 16 values per lane, else
+  // the staged-input area, reused once every wave has finished reading it.
+  constexpr bool kRedInX = NV > kMfmaRedOwn;
+  __shared__ float red_own[kRedInX ? 1 : kWavesPerWg][kRedInX ? 1 : NV][64];
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // [M][wg_chunks * 512] bf16, then zeros
+  float(*red)[NV][64] = kRedInX ? reinterpret_cast<float(*)[NV][64]>(xs) : reinterpret_cast<float(*)[NV][64]>(red_own);
 
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -100,25 +137,26 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
   const int c0 = min(wg_c1, wg_c0 + wave * per_wave);
   const int c1 = min(wg_c1, c0 + per_wave);
-  const int srow = 16 * (lane & 3) + 4 * (lane >> 4);  // first of the lane's four output rows
-  const int tok = (lane >> 2) & 3;                     // the lane's token within a set
+  const int cl = lane & 15;   // A row / B column of the lane
+  const int kg = lane >> 4;   // K group of the lane
   const int64_t tile0 = (int64_t)g * p.C;
-  // items (chunk, half, matrix), matrix fastest: with NMAT = 2 the even items
+  // items (chunk, part, matrix), matrix fastest: with NMAT = 2 the even items
   // are gate, the odd ones up
-  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / (2 * NMAT)) * TILE; };
-  auto item_half = [&](int it) { return (it / NMAT) & 1; };
+  constexpr int SL = MFrag<FMT>::SL, PER = 8 / SL;  // parts per tile
+  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / (PER * NMAT)) * TILE; };
+  auto item_half = [&](int it) { return (it / NMAT) % PER; };
 
   // first fragment in flight before the input is staged
-  const int n_items = (c1 - c0) * 2 * NMAT;
+  const int n_items = (c1 - c0) * PER * NMAT;
   MFrag<FMT> fa, fb;
-  if (n_items > 0) load_mfrag<FMT>(fa, item_tile(0), item_half(0), lane, srow);
+  if (n_items > 0) load_mfrag<FMT>(fa, item_tile(0), item_half(0), lane);
 
   // stage x[m][256 wg_c0 ..) for m < M (zero past d_in), then the zero area; all
   // loads are issued before the first LDS store
-  const int tstride = p.wg_chunks * 512;  // bytes per token row in LDS
+  const int tstride = p.wg_chunks * 512;  // bytes per vector in LDS
   {
     constexpr int kMaxPieces = kMfmaXBytes / 16 / kThreads;
-    const int per_tok = p.wg_chunks * 32;  // 16-byte pieces per token
+    const int per_tok = p.wg_chunks * 32;  // 16-byte pieces per vector
     const int pieces = M * per_tok;
     u32x4 v[kMaxPieces];
 #pragma unroll
@@ -142,93 +180,90 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   }
   __syncthreads();
 
-  // B operand addresses: a lane is on the diagonal when its column's K group
-  // (lane % 4) is its own K group (lane / 16)
-  const bool diag = (lane & 3) == (lane >> 4);
-  int boff[NSET];
-  bool bval[NSET];
+  // A operand addresses (bytes into xs, before the chunk and slot offsets): the
+  // lane's vector and K group, or the zero area.  Operand 0 is the only one
+  // except for NVFP4 with M > 8 (operand 0: first block, operand 1: second).
+  constexpr int NA = TWO ? 2 : 1;
+  int aoff[NA];
+  bool aval[NA];
+  if constexpr (PACK2) {
+    const int m = cl & 7;
+    aval[0] = m < M && (kg >> 1) == (cl >> 3);
+    aoff[0] = (aval[0] ? m * tstride : M * tstride) + kg * 16;
+  } else if constexpr (TWO) {
 #pragma unroll
-  for (int q = 0; q < NSET; ++q) {
-    bval[q] = diag && (4 * q + tok < M);
-    boff[q] = bval[q] ? (4 * q + tok) * tstride : M * tstride;
+    for (int b = 0; b < 2; ++b) {
+      aval[b] = cl < M && (kg >> 1) == b;
+      aoff[b] = (aval[b] ? cl * tstride : M * tstride) + kg * 16;
+    }
+  } else {
+    aval[0] = cl < M;
+    aoff[0] = (aval[0] ? cl * tstride : M * tstride) + kg * 16;
   }
 
-  f32x4 acc[NMAT][NSET];
+  f32x4 acc[NMAT][4];
 #pragma unroll
   for (int a = 0; a < NMAT; ++a)
 #pragma unroll
-    for (int q = 0; q < NSET; ++q) acc[a][q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int r = 0; r < 4; ++r) acc[a][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // items alternate matrices (NMAT = 2), so fragment fa always holds matrix 0
-  // and fb the last one: each call names its accumulators statically
-  auto consume = [&](const MFrag<FMT>& f, int it, f32x4(&ac)[NSET]) {
-    const int cc = c0 + it / (2 * NMAT) - wg_c0;  // chunk within the staged range
+  auto consume = [&](MFrag<FMT>& f, int it, f32x4(&ac)[4]) {
+    const int cc = c0 + it / (PER * NMAT) - wg_c0;  // chunk within the staged range
     const int half = item_half(it);
-    int bb[NSET];
 #pragma unroll
-    for (int q = 0; q < NSET; ++q) bb[q] = boff[q] + (bval[q] ? cc * 512 : 0);
+    for (int jj = 0; jj < SL; ++jj) {
+      const int j = SL * half + jj;  // slot within the chunk
+      bf16x8 xa[NA];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * half + jj;  // slot within the chunk
-      if constexpr (FMT == FP4G_NVFP4) {
+      for (int b = 0; b < NA; ++b) xa[b] = lds_bf16x8(xs, aoff[b] + (aval[b] ? cc * 512 : 0) + j * 64);
+      transpose_slot(f.q[jj]);
+      f32x4 d[NA][4];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {  // 16-column blocks 2j, 2j+1 = dwords 2h, 2h+1
-          const bf16x8 a0 = e2m1x8_bf16(f.q[jj][2 * h]);
-          const bf16x8 a1 = e2m1x8_bf16(f.q[jj][2 * h + 1]);
-          const int lb = 2 * jj + h;  // block within the half: dword lb/4, byte lb%4 of s[v]
-          float sc[4];
+      for (int r = 0; r < 4; ++r) {
+        const bf16x8 bw = e2m1x8_bf16(f.q[jj][r]);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const uint32_t sdw = f.s[v][lb >> 2];
-            sc[v] = (lb & 3) == 0 ? e4m3_f32<0>(sdw) : (lb & 3) == 1 ? e4m3_f32<1>(sdw)
-                  : (lb & 3) == 2 ? e4m3_f32<2>(sdw) : e4m3_f32<3>(sdw);
+        for (int b = 0; b < NA; ++b)
+          d[b][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[b], bw, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (FMT == FP4G_NVFP4) {
+          // blocks 2j (columns 0..15 of the slot) and 2j + 1 of row 16 r + cl:
+          // bytes 2jj, 2jj + 1 of the item's scale bytes
+          const uint32_t sdw = f.s[r][jj >> 1];
+          const float s0 = (jj & 1) ? e4m3_f32<2>(sdw) : e4m3_f32<0>(sdw);
+          const float s1 = (jj & 1) ? e4m3_f32<3>(sdw) : e4m3_f32<1>(sdw);
+          if constexpr (PACK2) {
+            const float sc = kg < 2 ? s0 : s1;  // output rows 0..7: first block, 8..15: second
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(d[0][r][v], sc, ac[r][v]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(d[1][r][v], s1, __builtin_fmaf(d[0][r][v], s0, ac[r][v]));
           }
+        } else {
+          const int e = (int)((f.s[r][jj >> 2] >> (8 * (jj & 3))) & 0xffu) - 127;
 #pragma unroll
-          for (int q = 0; q < NSET; ++q) {
-            const int off = bb[q] + (32 * j + 16 * h) * 2;
-            f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, lds_bf16x8(xs, off), f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                              0, 0, 0);
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, lds_bf16x8(xs, off + 16), t, 0, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) ac[q][v] = __builtin_fmaf(t[v], sc[v], ac[q][v]);
-          }
-        }
-      } else {
-        // one 32-column block per slot: byte jj of s[v]
-        int e[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) e[v] = (int)((f.s[v] >> (8 * jj)) & 0xffu) - 127;
-        bf16x8 av[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) av[d] = e2m1x8_bf16(f.q[jj][d]);
-#pragma unroll
-        for (int q = 0; q < NSET; ++q) {
-          const int off = bb[q] + 32 * j * 2;
-          f32x4 t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[0], lds_bf16x8(xs, off), f32x4{0.0f, 0.0f, 0.0f, 0.0f},
-                                                            0, 0, 0);
-#pragma unroll
-          for (int d = 1; d < 4; ++d)
-            t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[d], lds_bf16x8(xs, off + 16 * d), t, 0, 0, 0);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) ac[q][v] += __builtin_amdgcn_ldexpf(t[v], e[v]);
+          for (int v = 0; v < 4; ++v) ac[r][v] += __builtin_amdgcn_ldexpf(d[0][r][v], e);
         }
       }
-      // keep each slot's LDS reads and conversions next to its MFMAs (hoisting
-      // them across slots costs registers, then spills)
+      // keep each slot's LDS reads and conversions next to its MFMAs
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // items alternate matrices (NMAT = 2), so fragment fa always holds matrix 0
+  // and fb the last one: each call names its accumulators statically
   if (n_items > 0) {
     int it = 0;
     for (; it + 2 < n_items; it += 2) {
-      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane, srow);
+      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane);
       consume(fa, it, acc[0]);
-      load_mfrag<FMT>(fa, item_tile(it + 2), item_half(it + 2), lane, srow);
+      load_mfrag<FMT>(fa, item_tile(it + 2), item_half(it + 2), lane);
       consume(fb, it + 1, acc[NMAT - 1]);
     }
     if (it + 1 < n_items) {
-      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane, srow);
+      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane);
       consume(fa, it, acc[0]);
       consume(fb, it + 1, acc[NMAT - 1]);
     } else {
@@ -236,66 +271,90 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
     }
   }
 
+  // The lane's values: val[(a * NR + rr) * 4 + v] is matrix a, weight row
+  // 16 rb + cl with rb = rr (+ 2 in the upper half for PACK2), vector
+  // 4 (kg % 2) + v (PACK2) or 4 kg + v.
+  float val[NV];
 #pragma unroll
-  for (int a = 0; a < NMAT; ++a)
+  for (int a = 0; a < NMAT; ++a) {
+    if constexpr (PACK2) {
+      // lanes i and i + 32 hold the two blocks' sums of one (row, vector): add
+      // them, then the lower half keeps row blocks 0, 1 and the upper 2, 3
 #pragma unroll
-    for (int q = 0; q < NSET; ++q)
+      for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][(a * NSET + q) * 4 + v][lane] = acc[a][q][v];
+        for (int v = 0; v < 4; ++v) {
+          const float lo = add_halves(acc[a][rr][v], lane), hi = add_halves(acc[a][rr + 2][v], lane);
+          val[(a * NR + rr) * 4 + v] = lane < 32 ? lo : hi;
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) val[(a * NR + r) * 4 + v] = acc[a][r][v];
+    }
+  }
+
+  if constexpr (kRedInX) __syncthreads();  // every wave is past its last read of xs
+#pragma unroll
+  for (int i = 0; i < NV; ++i) red[wave][i][lane] = val[i];
   __syncthreads();
   if (wave != 0) return;
-
-  float val[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) val[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
 
-  // units: EPI_STORE rows (srow + 2w, srow + 2w + 1) of set q; EPI_SILU (gate,
-  // up) of row srow + v of set q
-  constexpr int NU = EPI == EPI_SILU ? 4 * NSET : 2 * NSET;
+  const int vbase = PACK2 ? 4 * (kg & 1) : 4 * kg;  // the lane's first vector
+  // units: EPI_SILU (gate, up) of (row block rr, vector vbase + v); EPI_STORE
+  // vectors (vbase + 2w, vbase + 2w + 1) of row block rr
+  constexpr int NU = EPI == EPI_SILU ? NR * 4 : NR * 2;
   float ua[NU], ub[NU];
   bool live[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     if constexpr (EPI == EPI_SILU) {
       ua[u] = val[u];
-      ub[u] = val[NSET * 4 + u];
+      ub[u] = val[NR * 4 + u];
+      live[u] = vbase + (u & 3) < M;
     } else {
       ua[u] = val[2 * u];
       ub[u] = val[2 * u + 1];
+      live[u] = vbase + 2 * (u & 1) < M;
     }
-    live[u] = true;
   }
   exchange_tree<NU>(p.slots, (int64_t)p.gbase[p.n] * 64, (int64_t)gt * 64 + lane, p.S, s, ua, ub, live);
 
   const int d_out = p.d_out[mem];
+  const int rb0 = PACK2 && lane >= 32 ? 2 : 0;
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     if (!live[u]) continue;
     if constexpr (EPI == EPI_SILU) {
-      const int q = u / 4, v = u % 4;
-      const int m = 4 * q + tok, row = g * 64 + srow + v;
+      const int rr = u / 4, v = u % 4;
+      const int m = vbase + v, row = g * 64 + 16 * (rb0 + rr) + cl;
       if (m < M && row < d_out) {
         const float gv = ua[u] * p.tscale[0], uv = ub[u] * p.tscale[1];
         p.h[(int64_t)m * d_out + row] = f32_to_bf16_rne(silu_f32(gv) * uv);
       }
     } else {
-      const int q = u / 2, w = u % 2;
-      const int m = 4 * q + tok, row = g * 64 + srow + 2 * w;
-      if (m < M) {
-        float* y = p.y[mem] + (int64_t)m * d_out;
-        if (row < d_out) y[row] = ua[u] * p.tscale[mem];
-        if (row + 1 < d_out) y[row + 1] = ub[u] * p.tscale[mem];
+      const int rr = u / 2, w = u % 2;
+      const int m = vbase + 2 * w, row = g * 64 + 16 * (rb0 + rr) + cl;
+      if (row < d_out) {
+        float* y = p.y[mem] + row;
+        if (m < M) y[(int64_t)m * d_out] = ua[u] * p.tscale[mem];
+        if (m + 1 < M) y[(int64_t)(m + 1) * d_out] = ub[u] * p.tscale[mem];
       }
     }
   }
 }
 
 // ---- launch planning for the MFMA kernel ------------------------------------------
-// The VALU plan, with S raised where needed so that a workgroup's staged input
-// (M rows of its chunk range) fits the LDS budget.
+// Four-wave workgroups as plan_nw4 lays them out (twice the waves above 8
+// vectors, where each slot takes two MFMAs per 16 rows), with S raised where
+// needed so that a workgroup's staged input (M rows of its chunk range) fits
+// the LDS budget.
 inline Plan plan_mfma(int64_t R, int64_t C, int nmat, int M) {
   (void)nmat;
-  Plan pl = plan_nw4(R, C);
+  Plan pl = plan_nw4(R, C, M > kMaxM ? 4096 : 2048);
   const int64_t max_chunks = kMfmaXBytes / (M * 512);
   if (pl.wg_chunks > max_chunks) {
     int64_t S = (C + max_chunks - 1) / max_chunks;
@@ -306,19 +365,27 @@ inline Plan plan_mfma(int64_t R, int64_t C, int nmat, int M) {
   return pl;
 }
 
-inline size_t mfma_lds_bytes(const Plan& pl, int M) { return (size_t)M * pl.wg_chunks * 512 + kZeroBytes; }
+// Dynamic LDS of a launch: the staged input, or the reduction buffer where it
+// lives there and is larger.
+inline size_t mfma_lds_bytes(const Plan& pl, uint32_t fmt, int nmat, int M) {
+  const size_t staged = (size_t)M * pl.wg_chunks * 512 + kZeroBytes;
+  const int nv = nmat * (fmt == FP4G_NVFP4 && M <= 8 ? 8 : 16);  // values per lane at the end
+  const size_t red = nv > kMfmaRedOwn ? (size_t)kWavesPerWg * nv * 64 * 4 : 0;
+  return staged > red ? staged : red;
+}
 
-// Exchange units per lane: the larger of the two kernels' needs.
+// Exchange units per lane: the larger of the two kernels' needs (the MFMA
+// kernel's for its widest case, either format).
 inline int64_t exchange_units_any(int nmat, int M) {
-  const int64_t nset = (M + 3) / 4;
-  const int64_t mf = nmat == 2 ? 4 * nset : 2 * nset;
+  const int64_t mf = nmat == 2 ? 16 : 8;
   const int64_t vu = exchange_units(nmat, M);
   return mf > vu ? mf : vu;
 }
 
 // Workspace for either kernel (the caller may choose the path per call).
 inline uint64_t gemv_ws_bytes_any(int64_t R_total, int64_t C, int nmat, int M) {
-  const Plan a = plan_for(R_total, C, nmat, M), b = plan_mfma(R_total, C, nmat, M);
+  const Plan b = plan_mfma(R_total, C, nmat, M);
+  const Plan a = M <= kMaxM ? plan_for(R_total, C, nmat, M) : b;  // wider: matrix cores only
   const int64_t nodes = tree_nodes(a.S) > tree_nodes(b.S) ? tree_nodes(a.S) : tree_nodes(b.S);
   return (uint64_t)nodes * exchange_units_any(nmat, M) * R_total * 64 * 8;
 }
@@ -331,6 +398,7 @@ hipError_t launch_mfma(int M, const GemvParams& p, unsigned grid, size_t lds, hi
     k_gemv_mfma<FMT, MM, NMAT, EPI><<<grid, kThreads, lds, s>>>(p); \
     break;
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
 #undef FP4G_CASE
     default: return hipErrorInvalidValue;
   }

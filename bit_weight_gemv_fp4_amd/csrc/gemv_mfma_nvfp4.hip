@@ -1,7 +1,6 @@
-// gemv_mfma_nvfp4.hip -- NVFP4 instantiations of the matrix-core kernel (gemv_mfma.hpp).
+// gemv_mfma_nvfp4.hip -- NVFP4 plain-product instantiations of the matrix-core kernel (gemv_mfma.hpp).
 #include "gemv_mfma.hpp"
 
 namespace fp4g {
 template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
-template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
 }  // namespace fp4g

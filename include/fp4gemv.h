@@ -82,9 +82,11 @@ typedef enum { FP4G_NVFP4 = 1, FP4G_MXFP4 = 2, FP4G_FP8_ROW = 3 } fp4g_format;
 /* Kernel path of the NVFP4/MXFP4 products.  VALU: one v_dot2 per weight pair and
  * vector.  MFMA: the products on the matrix cores (bf16 MFMA on exact bf16
  * weights; block scales applied per block in FP32).  AUTO takes MFMA from M = 3
- * on and VALU below.  FP8 rows have only the VALU kernel: MFMA is refused there
- * with FP4G_E_PATH.  Both paths give the same results up to the order of the
- * FP32 additions. */
+ * on and VALU below.  The VALU kernel takes up to 8 vectors, the MFMA kernel up
+ * to 16 (FP4G_MAX_M_WIDE: a verify block of up to 15 drafts, feed section "More
+ * tokens per weight read"); VALU with more than 8 is FP4G_E_PATH.  FP8 rows have
+ * only the VALU kernel: MFMA is refused there with FP4G_E_PATH.  Both paths give
+ * the same results up to the order of the FP32 additions. */
 typedef enum { FP4G_PATH_AUTO = 0, FP4G_PATH_VALU = 1, FP4G_PATH_MFMA = 2 } fp4g_path;
 
 /* Operation ids for fp4g_workspace_bytes. */
@@ -99,6 +101,11 @@ typedef enum {
 
 /* Most matrices one fp4_gemv_grouped call takes. */
 #define FP4G_MAX_GROUP 4
+/* Vectors per call: 1..FP4G_MAX_M everywhere, up to FP4G_MAX_M_WIDE for the
+ * NVFP4/MXFP4 products (fp4_skinny_gemm, fp4_gemv_grouped, fp4_gate_up_silu) on
+ * the matrix-core path. */
+#define FP4G_MAX_M 8
+#define FP4G_MAX_M_WIDE 16
 
 /* A packed weight matrix.  A plain view: it owns nothing.  Filled in by
  * fp4g_pack; callers must not edit it. */
@@ -238,14 +245,15 @@ uint64_t fp4g_workspace_bytes(int32_t op, const void* desc_host, int32_t M);
 int32_t fp4_gemv(const fp4g_weight* W_host, const uint16_t* x_dev, float* y_dev, void* ws_dev,
                  uint64_t ws_bytes, void* stream);
 
-/* Y_dev[m][r] = sum_k w[r][k] * X_dev[m][k] for m < M, M in 1..8 (the verify
- * product of speculative decoding).  X_dev: bf16 [M][d_in]; Y_dev: f32 [M][d_out].
+/* Y_dev[m][r] = sum_k w[r][k] * X_dev[m][k] for m < M, M in 1..16 (the verify
+ * product of speculative decoding; above 8 on the matrix-core path only).  X_dev: bf16 [M][d_in]; Y_dev: f32 [M][d_out].
  * path: fp4g_path. */
 int32_t fp4_skinny_gemm(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M, float* Y_dev,
                         int32_t path, void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* Several products of one input in one launch: Y_dev[i][m][r] = sum_k
- * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..8.  X_dev: bf16
+ * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..16 (above 8 on
+ * the matrix-core path only).  X_dev: bf16
  * [M][d_in]; Y_dev: host array of G->n device pointers, each f32 [M][w_i.d_out],
  * 16-B aligned and disjoint.  path: fp4g_path.  Each member's results are those
  * of fp4_skinny_gemm on it alone up to the order of the FP32 additions. */
@@ -253,7 +261,8 @@ int32_t fp4_gemv_grouped(const fp4g_group* G_host, const uint16_t* X_dev, int32_
                          float* const* Y_host, int32_t path, void* ws_dev, uint64_t ws_bytes, void* stream);
 
 /* Fused MLP front half: g = Wg X_m, u = Wu X_m, H_dev[m][r] = bf16_rne(SiLU(g[r]) *
- * u[r]) with SiLU(z) = z / (1 + e^-z), for m < M in 1..8.  Wg and Wu are NVFP4 or
+ * u[r]) with SiLU(z) = z / (1 + e^-z), for m < M in 1..16 (above 8 on the
+ * matrix-core path only).  Wg and Wu are NVFP4 or
  * MXFP4 matrices of one shape d_ff x hidden (feed, section "Decode speed is bytes
  * divided by bandwidth": gate and up projections are 17408 x 5120 in the dense
  * model).  X_dev: bf16 [M][hidden]; H_dev: bf16 [M][d_ff]. */

@@ -103,7 +103,10 @@ def test_skinny_and_lmhead_error_paths():
     d = good_desc()
     X, Y = FAKE + (1 << 30), FAKE + (2 << 30)
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 0, Y, 0, None, 0, None) == E_SHAPE
-    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 9, Y, 0, None, 0, None) == E_SHAPE
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 17, Y, 0, None, 0, None) == E_SHAPE
+    # 9..16 vectors run on the matrix cores only
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 9, Y, fg.PATH_VALU, None, 0, None) == E_PATH
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 16, Y, fg.PATH_VALU, None, 0, None) == E_PATH
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, 7, None, 0, None) == E_PATH
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, -1, None, 0, None) == E_PATH
     assert L.fp8_lmhead_gemv(ctypes.byref(d), X, 1, Y, None, 0, None) == E_FORMAT  # NVFP4 given
@@ -134,7 +137,8 @@ def test_grouped_error_paths():
     assert call_grouped(group_desc()) == E_SHAPE                       # n = 0
     G = group_desc(q, k); G.n = 5
     assert call_grouped(G) == E_SHAPE                                  # n > 4
-    assert call_grouped(group_desc(q, k), M=9) == E_SHAPE
+    assert call_grouped(group_desc(q, k), M=17) == E_SHAPE
+    assert call_grouped(group_desc(q, k), M=9, path=fg.PATH_VALU) == E_PATH
     k2 = good_desc(fg.MXFP4, d_out=64); k2.packed = FAKE + (8 << 30)
     assert call_grouped(group_desc(q, k2)) == E_FORMAT                 # mixed formats
     k3 = good_desc(d_out=64, d_in=256); k3.packed = FAKE + (8 << 30)
@@ -211,6 +215,8 @@ def test_gate_up_error_paths():
     u3 = good_desc(fmt=fg.MXFP4)
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u3), X, 1, H, 0, None, 0, None) == E_FORMAT
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, 3, None, 0, None) == E_PATH
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 17, H, 0, None, 0, None) == E_SHAPE
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 9, H, fg.PATH_VALU, None, 0, None) == E_PATH
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, None, 0, None, 0, None) == E_NULL
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, X, 0, None, 0, None) == E_ALIAS
 
@@ -303,6 +309,15 @@ def test_workspace_queries():
     assert fg.workspace_bytes(fg.OP_GEMV, good_desc(d_out=64, d_in=256), 1) == 0  # one row group, one chunk
     assert fg.workspace_bytes(99, good_desc(), 1) == 0
     assert fg.workspace_bytes(fg.OP_GEMV, good_desc(), 0) == 0
+    # up to 16 vectors for the NVFP4/MXFP4 products, 8 for the FP8 head and MoE
+    big = good_desc(d_out=5120, d_in=17408)
+    assert fg.workspace_bytes(fg.OP_GEMV, big, 16) > 0
+    assert fg.workspace_bytes(fg.OP_GATE_UP, good_desc(d_out=17408, d_in=5120), 16) > 0
+    assert fg.workspace_bytes(fg.OP_GEMV, big, 17) == 0
+    assert fg.workspace_bytes(fg.OP_LMHEAD, good_desc(fg.FP8_ROW, 5120, 17408), 8) > 0
+    assert fg.workspace_bytes(fg.OP_LMHEAD, good_desc(fg.FP8_ROW, 5120, 17408), 9) == 0
+    assert fg.workspace_bytes(fg.OP_MOE, moe_desc(), 9) == 0
+    assert fg.MAX_M == 8 and fg.MAX_M_WIDE == 16
     bad = good_desc(); bad.layout_tag = 0
     assert fg.workspace_bytes(fg.OP_GEMV, bad, 1) == 0
 

@@ -604,3 +604,79 @@ def test_workspace_reuse_across_shapes():
         X = datagen.bf16_normal((3, shape[1]), 22, device=DEV)
         Y = fg.fp4_skinny_gemm(W, X, ws=ws)
         check_product(Y, host, bits(X), rows=sample_rows(shape[0], 64))
+
+
+# ---- wider verify blocks: 9..16 vectors on the matrix-core kernel -----------------------------
+
+
+@pytest.mark.parametrize("path", [fg.PATH_AUTO, fg.PATH_MFMA])
+@pytest.mark.parametrize("M", [9, 11, 16])
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_wide_verify_skinny_matches_oracle(fmt, M, path):
+    """A verify block of K + 1 = 9..16 positions (the feed verifies up to 11)."""
+    log("wide skinny", fmt, M, path)
+    for shape in ((200, 1056), (70, 288), (5120, 5120)):
+        W, host = make(fmt, *shape, seed=3)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("Xw", M, shape), device=DEV)
+        Y = fg.fp4_skinny_gemm(W, X, path=path)
+        check_product(Y, host, bits(X))
+
+
+@pytest.mark.parametrize("M", [9, 11, 16])
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_wide_verify_gate_up_and_grouped(fmt, M):
+    log("wide gate_up/grouped", fmt, M)
+    for shape in ((200, 1056), (130, 544)):
+        Wg, hg = make(fmt, *shape, seed=5)
+        Wu, hu = make(fmt, *shape, seed=6)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("Xgw", M, shape), device=DEV)
+        check_h(fg.fp4_gate_up_silu(Wg, Wu, X), hg, hu, bits(X))
+    shapes = [(70, 1056), (1, 1056), (200, 1056)]
+    mats = [make(fmt, o, i, seed=("grpw", j)) for j, (o, i) in enumerate(shapes)]
+    X = datagen.bf16_normal((M, 1056), datagen.tensor_seed("grpXw", M), device=DEV)
+    for (W, host), Y in zip(mats, fg.fp4_gemv_grouped(fg.Group([W for W, _ in mats]), X)):
+        check_product(Y, host, bits(X))
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_wide_verify_exact_sums(fmt):
+    """Power-of-two scales mixed per block with x in {-1, 0, 1}: every partial sum
+    is representable, so 9..16 vectors must give the oracle's sums bit for bit
+    (a token or row mapped to the wrong output column breaks this); split counts
+    up to 63 across the tree."""
+    log("wide exact", fmt)
+    for shape in ((130, 1056), (64, 17408), (70, 256 * 63)):
+        gen = torch.Generator(DEV).manual_seed(shape[0] + shape[1] + 7)
+        mat = datagen.matrix(fmt, *shape, datagen.tensor_seed("exactw", fmt, shape), device=DEV)
+        sc = exact_scales(fmt, shape, gen)
+        W = fg.pack(fmt, mat["codes"], sc)
+        for M in (9, 12, 16):
+            X = torch.randint(-1, 2, (M, shape[1]), generator=gen, device=DEV).to(torch.bfloat16)
+            Y, _ = oracle.gemv(fmt, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
+            got = fg.fp4_skinny_gemm(W, X).clone()
+            assert np.array_equal(got.cpu().double().numpy(), Y), (shape, M)
+            assert torch.equal(fg.fp4_skinny_gemm(W, X), got), (shape, M)
+
+
+@pytest.mark.parametrize("M", [11, 16])
+def test_wide_verify_config4_mlp(M):
+    """The dense MLP (gate/up 17408x5120 + SiLU*mul, down 5120x17408) at a verify
+    block of 11 (K = 10) and 16 positions, sampled rows."""
+    log("wide C4 MLP", M)
+    Wg, hg = make(fg.NVFP4, 17408, 5120, seed=200)
+    Wu, hu = make(fg.NVFP4, 17408, 5120, seed=201)
+    Wd, hd = make(fg.NVFP4, 5120, 17408, seed=202)
+    X = datagen.bf16_normal((M, 5120), datagen.tensor_seed("C2x", M), device=DEV)
+    H = fg.fp4_gate_up_silu(Wg, Wu, X)
+    Y = fg.fp4_skinny_gemm(Wd, H)
+    check_h(H, hg, hu, bits(X), rows=sample_rows(17408, 160, seed=M))
+    check_product(Y, hd, bits(H), rows=sample_rows(5120, 160, seed=M + 10))
+
+
+def test_wide_verify_refuses_the_valu_path():
+    W, _ = make(fg.NVFP4, 200, 1056, seed=3)
+    X = datagen.bf16_normal((9, 1056), 5, device=DEV)
+    with pytest.raises(fg.Fp4gError):
+        fg.fp4_skinny_gemm(W, X, path=fg.PATH_VALU)
+    with pytest.raises(fg.Fp4gError):
+        fg.fp4_skinny_gemm(W, datagen.bf16_normal((17, 1056), 5, device=DEV))
