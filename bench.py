@@ -65,8 +65,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "head", "copy"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3m", "c4", "c5", "head", "copy"],
+                    help="c3m: the dense stream in the checkpoint's mixed NVFP4/FP8 layout")
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
+    ap.add_argument("--router", action="store_true",
+                    help="c5: compute each layer's router logits with an FP8 512x2560 product of x")
     ap.add_argument("--cpu-sample-layers", type=int, default=24,
                     help="full layers the CPU oracle runs for cpu_baseline (about 0.45 s each on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -194,6 +197,60 @@ def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
     return step, keep, sops
 
 
+def build_mixed_stream(fg, datagen, torch, M=1):
+    """The dense decode chain in the checkpoint's mixed layout: FP8 row-scaled
+    projections (linear attention in 48 layers, full attention in every fourth),
+    NVFP4 MLPs in layers 0..55 and FP8 MLPs in the last 8, then the FP8 head."""
+    dev = "cuda"
+    H, F = datagen.HIDDEN, datagen.FFN
+    step = Step()
+    keep = []
+    x = datagen.bf16_normal((M, H), datagen.tensor_seed("c3m", "x"), device=dev)
+    wide = {i: datagen.bf16_normal((M, i), datagen.tensor_seed("c3m", "x", i), device=dev) for i in (6144, 10240)}
+    h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, H), dtype=torch.float32, device=dev)
+    keep += [x, h, y, wide]
+
+    def mat(fmt, L, name, o, i):
+        m = datagen.matrix(fmt, o, i, datagen.tensor_seed("c3m", L, name), device=dev)
+        W = fg.pack(fmt, m["codes"], m["scales"], m["tensor_scale"])
+        del m
+        keep.append(W)
+        return W
+
+    def product(fmt, W, xin, out):
+        if fmt == fg.FP8_ROW:
+            return lambda: fg.fp8_lmhead_gemv(W, xin, out)
+        return lambda: fg.fp4_skinny_gemm(W, xin, out)
+
+    for L in range(datagen.LAYERS):
+        shapes = datagen.MIXED_ATTN_SHAPES if datagen.mixed_full_attention(L) else datagen.MIXED_GDN_SHAPES
+        ws = [mat(fg.FP8_ROW, L, f"proj{j}", o, i) for j, (o, i) in enumerate(shapes)]
+        into = [j for j, (o, i) in enumerate(shapes) if i == H]     # projections of x: one grouped launch
+        G = fg.Group([ws[j] for j in into])
+        ys = [torch.empty((M, shapes[j][0]), dtype=torch.float32, device=dev) for j in into]
+        keep += [G, ys]
+        step.add("proj_in", (lambda G=G, ys=ys: fg.fp4_gemv_grouped(G, x, ys)),
+                 sum(fg.packed_bytes(fg.FP8_ROW, *shapes[j]) + 4 * M * shapes[j][0] for j in into) + 2 * M * H)
+        for j, (o, i) in enumerate(shapes):
+            if j not in into:
+                step.add("proj_out", product(fg.FP8_ROW, ws[j], wide[i], y),
+                         algorithmic_gemv_bytes(fg, fg.FP8_ROW, o, i, M))
+        fmt = fg.NVFP4 if L < datagen.MIXED_FP8_MLP_FROM else fg.FP8_ROW
+        Wg, Wu, Wd = mat(fmt, L, "gate", F, H), mat(fmt, L, "up", F, H), mat(fmt, L, "down", H, F)
+        kind = "gate_up_silu" if fmt == fg.NVFP4 else "gate_up_silu_fp8"
+        step.add(kind, (lambda Wg=Wg, Wu=Wu: fg.fp4_gate_up_silu(Wg, Wu, x, h)),
+                 2 * fg.packed_bytes(fmt, F, H) + M * H * 2 + M * F * 2)
+        step.add("down" if fmt == fg.NVFP4 else "down_fp8", product(fmt, Wd, h, y),
+                 algorithmic_gemv_bytes(fg, fmt, H, F, M))
+    Wh = mat(fg.FP8_ROW, "head", "head", datagen.VOCAB, H)
+    logits = torch.empty((M, datagen.VOCAB), dtype=torch.float32, device=dev)
+    keep.append(logits)
+    step.add("lm_head", (lambda: fg.fp8_lmhead_gemv(Wh, x, logits)),
+             algorithmic_gemv_bytes(fg, fg.FP8_ROW, datagen.VOCAB, H, M))
+    return step, keep
+
+
 def weights_only_bytes_dense(fg, datagen, layers, with_head=True):
     H, F = datagen.HIDDEN, datagen.FFN
     per_layer = 2 * fg.packed_bytes(fg.NVFP4, F, H) + fg.packed_bytes(fg.NVFP4, H, F)
@@ -208,7 +265,7 @@ def copies_for(nbytes, min_total=1 << 30):
     return max(1, -(-min_total // nbytes))
 
 
-def build_other(name, M, fg, datagen, torch, path=0):
+def build_other(name, M, fg, datagen, torch, path=0, router=False):
     dev = "cuda"
     H, F = datagen.HIDDEN, datagen.FFN
     keep = []
@@ -307,9 +364,22 @@ def build_other(name, M, fg, datagen, torch, path=0):
         logits_out = torch.empty((M, datagen.MOE_VOCAB), dtype=torch.float32, device=dev)
         keep += [X, Y, ids, wts, logits_out]
         moe_bytes = 0
+        routers = []
+        if router:
+            for L in range(len(layers)):
+                m = datagen.matrix(fg.FP8_ROW, E, Hm, datagen.tensor_seed("c5", "router", L), device=dev)
+                routers.append(fg.pack(fg.FP8_ROW, m["codes"], m["scales"]))
+                del m
+            keep += routers
         for r in range(R):
             for L, layer in enumerate(layers):
-                lg = datagen.router_logits(M, E, datagen.tensor_seed("c5", "logits", r, L), device=dev)
+                if router:
+                    lg = torch.empty((M, E), dtype=torch.float32, device=dev)
+                    fg.fp8_lmhead_gemv(routers[L], X, lg)
+                    step.add("router", (lambda Wr=routers[L], lg=lg: fg.fp8_lmhead_gemv(Wr, X, lg)),
+                             algorithmic_gemv_bytes(fg, fg.FP8_ROW, E, Hm, M))
+                else:
+                    lg = datagen.router_logits(M, E, datagen.tensor_seed("c5", "logits", r, L), device=dev)
                 keep.append(lg)
                 # algorithmic bytes: the realised union of experts (+ shared), logits, x, y
                 _, rid, _ = fg.moe_route_gemv(layer, X, lg, Y, ids, wts)
@@ -319,7 +389,8 @@ def build_other(name, M, fg, datagen, torch, path=0):
                 step.add("moe", (lambda layer=layer, lg=lg: fg.moe_route_gemv(layer, X, lg, Y, ids, wts)), nbytes)
             step.add("lm_head", (lambda: fg.fp8_lmhead_gemv(Wh, X, logits_out)),
                      algorithmic_gemv_bytes(fg, fg.FP8_ROW, datagen.MOE_VOCAB, Hm, M))
-        return step, keep, (f"MoE decode, M={M}: 40 layers x [route top-8 of 512 + shared, MXFP4 experts "
+        return step, keep, (f"MoE decode, M={M}: 40 layers x [{'FP8 router 512x2560, ' if router else ''}"
+                            f"route top-8 of 512 + shared, MXFP4 experts "
                             f"gate/up 768x2560, down 2560x768] + FP8 LM head 157184x2560"), "moe"
     raise ValueError(name)
 
@@ -409,9 +480,15 @@ def main():
             step_launches = step
             step = sstep
             dominant = "decode_stream"
+    elif args.workload == "c3m":
+        step, keep = build_mixed_stream(fg, datagen, torch, M=M)
+        workload = (f"full dense weight stream in the mixed layout, M={M}: 64 layers of FP8 projections (48 linear "
+                    f"attention 12288x5120 + 5120x10240, 16 full attention 12288x5120 + 2 x 1024x5120 + 5120x6144), "
+                    f"MLPs 17408x5120 x2 + 5120x17408 NVFP4 in layers 0-55 and FP8 in 56-63, + FP8 LM head 248320x5120")
+        dominant = "gate_up_silu"
     else:
         path = {"auto": fg.PATH_AUTO, "valu": fg.PATH_VALU, "mfma": fg.PATH_MFMA}[args.path]
-        step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch, path)
+        step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch, path, args.router)
     bytes_per_step = step.bytes() / step.steps_per_replay
     engine = args.engine if args.workload == "c3" else "launches"
     # one eager pass allocates the workspace and checks every launch
@@ -453,7 +530,7 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "implied_tok_s": round(1e3 / ms_per_step, 2) if args.workload in ("c3", "c5") else None,
+        "implied_tok_s": round(1e3 / ms_per_step, 2) if args.workload in ("c3", "c3m", "c5") else None,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -6,13 +6,14 @@
 namespace fp4g {
 
 // Per-format launchers (gemv_kernel.hpp), instantiated in gemv_nvfp4.hip,
-// gemv_mxfp4.hip and gemv_fp8.hip.
+// gemv_mxfp4.hip, gemv_fp8.hip and gemv_fp8_silu.hip.
 extern template hipError_t launch_m<FP4G_NVFP4, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_NVFP4, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_MXFP4, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_ARGMAX>(int, int, const GemvParams&, unsigned, hipStream_t);
+extern template hipError_t launch_m<FP4G_FP8_ROW, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
 // Matrix-core launchers (gemv_mfma.hpp), in gemv_mfma_nvfp4.hip and gemv_mfma_mxfp4.hip.
 extern template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
 extern template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
@@ -100,8 +101,9 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
     gb += row_groups(W[i]->d_out);
   }
   p.gbase[n] = (int)gb;
-  if (W[0]->format == FP4G_FP8_ROW)  // row scales follow the tiles
-    p.rs = (const float*)((const uint8_t*)W[0]->packed + row_groups(W[0]->d_out) * C * kTileF8);
+  if (W[0]->format == FP4G_FP8_ROW)  // row scales follow each member's tiles
+    for (int i = 0; i < n; ++i)
+      p.rs[i] = (const float*)((const uint8_t*)W[i]->packed + row_groups(W[i]->d_out) * C * kTileF8);
   p.x = X;
   p.slots = need ? (unsigned long long*)ws : nullptr;
   p.d_in = W[0]->d_in;
@@ -176,7 +178,8 @@ int32_t fp4_gemv_grouped(const fp4g_group* G, const uint16_t* X, int32_t M, floa
   if (!Y) return FP4G_E_NULL;
   const fp4g_weight* W[kMaxGroup];
   for (int i = 0; i < G->n; ++i) W[i] = &G->w[i];
-  return run_group(W, G->n, true, X, M, Y, path, ws, ws_bytes, stream);
+  // NVFP4/MXFP4 members, or FP8 row-scaled ones (projections of a mixed layout)
+  return run_group(W, G->n, G->w[0].format != FP4G_FP8_ROW, X, M, Y, path, ws, ws_bytes, stream);
 }
 
 int32_t fp8_lmhead_gemv(const fp4g_weight* W, const uint16_t* X, int32_t M, float* logits, void* ws,
@@ -214,7 +217,7 @@ int32_t fp8_lmhead_argmax(const fp4g_weight* W, const uint16_t* X, int32_t M, in
   // tiles are contiguous, their row scales sit after all the matrix's tiles
   const uint8_t* base = (const uint8_t*)W->packed;
   p.w[0] = base + (int64_t)(row_begin / kRowsPerGroup) * C * kTileF8;
-  p.rs = (const float*)(base + R_all * C * kTileF8) + row_begin;
+  p.rs[0] = (const float*)(base + R_all * C * kTileF8) + row_begin;
   p.tscale[0] = 1.0f;
   p.y[0] = logits;
   p.d_out[0] = n_rows;
@@ -239,15 +242,17 @@ int32_t fp8_lmhead_argmax(const fp4g_weight* W, const uint16_t* X, int32_t M, in
 
 int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uint16_t* X, int32_t M, uint16_t* H,
                          int32_t path, void* ws, uint64_t ws_bytes, void* stream) {
-  fp4g_status st = check_weight(Wg, true);
+  // NVFP4/MXFP4 pairs, or FP8 row-scaled pairs (the FP8 MLPs of a mixed layout)
+  const bool fp4 = Wg && Wg->format != FP4G_FP8_ROW;
+  fp4g_status st = check_weight(Wg, fp4);
   if (st != FP4G_OK) return st;
-  st = check_weight(Wu, true);
+  st = check_weight(Wu, fp4);
   if (st != FP4G_OK) return st;
   if (Wg->format != Wu->format) return FP4G_E_FORMAT;
   if (Wg->d_out != Wu->d_out || Wg->d_in != Wu->d_in) return FP4G_E_SHAPE;
   if (!X || !H) return FP4G_E_NULL;
-  if (M < 1 || M > kMaxMWide) return FP4G_E_SHAPE;
-  if (!valid_path(path, true, M)) return FP4G_E_PATH;
+  if (M < 1 || M > (fp4 ? kMaxMWide : kMaxM)) return FP4G_E_SHAPE;
+  if (!valid_path(path, fp4, M)) return FP4G_E_PATH;
   if (!aligned(X, 16) || !aligned(H, 16)) return FP4G_E_ALIGN;
   const bool mfma = use_mfma(path, Wg->format, M);
   const int64_t R = row_groups(Wg->d_out), C = chunks(Wg->d_in);
@@ -270,6 +275,10 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   p.d_out[0] = Wg->d_out;
   p.gbase[0] = 0;
   p.gbase[1] = (int)R;
+  if (!fp4) {  // row scales follow each matrix's tiles
+    p.rs[0] = (const float*)((const uint8_t*)Wg->packed + R * C * kTileF8);
+    p.rs[1] = (const float*)((const uint8_t*)Wu->packed + R * C * kTileF8);
+  }
   p.x = X;
   p.h = H;
   p.slots = need ? (unsigned long long*)ws : nullptr;
@@ -283,9 +292,12 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   if (mfma)
     e = Wg->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, Wg->format, 2, M), s)
                                  : launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, Wg->format, 2, M), s);
+  else if (Wg->format == FP4G_NVFP4)
+    e = launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s);
+  else if (Wg->format == FP4G_MXFP4)
+    e = launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s);
   else
-    e = Wg->format == FP4G_NVFP4 ? launch_m<FP4G_NVFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s)
-                                 : launch_m<FP4G_MXFP4, 2, EPI_SILU>(M, pl.nw, p, grid, s);
+    e = launch_m<FP4G_FP8_ROW, 2, EPI_SILU>(M, pl.nw, p, grid, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 
@@ -297,18 +309,22 @@ uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
   if (op == FP4G_OP_GROUPED) {
     const fp4g_group* G = (const fp4g_group*)desc;
     if (check_group(G) != FP4G_OK) return 0;
+    const bool fp4 = G->w[0].format != FP4G_FP8_ROW;
+    if (!fp4 && M > kMaxM) return 0;
     int64_t R = 0;
     for (int i = 0; i < G->n; ++i) {
-      if (check_weight(&G->w[i], true) != FP4G_OK) return 0;
+      if (check_weight(&G->w[i], fp4) != FP4G_OK) return 0;
       if (G->w[i].format != G->w[0].format || G->w[i].d_in != G->w[0].d_in) return 0;
       R += row_groups(G->w[i].d_out);
     }
     return gemv_ws_bytes_any(R, chunks(G->w[0].d_in), 1, M);
   }
   const fp4g_weight* W = (const fp4g_weight*)desc;
-  const bool fp4 = op != FP4G_OP_LMHEAD;
   if (op != FP4G_OP_GEMV && op != FP4G_OP_GATE_UP && op != FP4G_OP_LMHEAD) return 0;
+  // FP8 rows: the head, or a gate/up pair of a mixed layout (up to kMaxM vectors)
+  const bool fp4 = op == FP4G_OP_GEMV || (op == FP4G_OP_GATE_UP && W->format != FP4G_FP8_ROW);
   if (check_weight(W, fp4) != FP4G_OK) return 0;
+  if (!fp4 && M > kMaxM) return 0;
   return gemv_ws_bytes_any(row_groups(W->d_out), chunks(W->d_in), op == FP4G_OP_GATE_UP ? 2 : 1, M);
 }
 

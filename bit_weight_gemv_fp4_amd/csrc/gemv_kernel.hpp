@@ -53,7 +53,7 @@ struct GemvParams {
   const uint16_t* x;          // bf16 [M][d_in]
   uint16_t* h;                // EPI_SILU: bf16 [M][d_out[0]]
   unsigned long long* slots;  // split-K exchange slots, zero between calls
-  const float* rs;            // FP8 rows: the row scales of rows 0.. of this launch
+  const float* rs[kMaxGroup];  // FP8 rows: member i's row scales (EPI_SILU: gate, up)
   unsigned long long* amax;   // EPI_ARGMAX: [kArgSlots][kMaxM] keys, zero between calls
   int32_t* top_idx;           // EPI_ARGMAX: [M] row of the largest logit (+ row_base)
   float* top_val;             // EPI_ARGMAX: [M] the largest logit
@@ -270,15 +270,15 @@ template <uint32_t FMT, int M, int NMAT, int EPI>
 __device__ __forceinline__ void finish_unit(const GemvParams& p, int mem, int row, int u, float a, float b) {
   if (row >= p.d_out[mem]) return;
   if constexpr (EPI == EPI_STORE || EPI == EPI_ARGMAX) {
-    const float sc = FMT == FP4G_FP8_ROW ? p.rs[row] : p.tscale[mem];
+    const float sc = FMT == FP4G_FP8_ROW ? p.rs[mem][row] : p.tscale[mem];
     const int m0 = 2 * u;
     if (EPI == EPI_STORE || p.y[0]) {
       p.y[mem][(int64_t)m0 * p.d_out[mem] + row] = a * sc;
       if (m0 + 1 < M) p.y[mem][(int64_t)(m0 + 1) * p.d_out[mem] + row] = b * sc;
     }
   } else {
-    const float g = a * p.tscale[0];
-    const float v = b * p.tscale[1];
+    const float g = a * (FMT == FP4G_FP8_ROW ? p.rs[0][row] : p.tscale[0]);
+    const float v = b * (FMT == FP4G_FP8_ROW ? p.rs[1][row] : p.tscale[1]);
     p.h[(int64_t)u * p.d_out[0] + row] = f32_to_bf16_rne(silu_f32(g) * v);
   }
 }
@@ -293,7 +293,7 @@ template <uint32_t FMT, int M, int NU>
 __device__ __forceinline__ void argmax_epilogue(const GemvParams& p, int row, int lane, const float (&ua)[NU],
                                                 const float (&ub)[NU], const bool (&live)[NU]) {
   const bool valid = row < p.d_out[0];
-  const float sc = valid ? (FMT == FP4G_FP8_ROW ? p.rs[row] : p.tscale[0]) : 0.0f;
+  const float sc = valid ? (FMT == FP4G_FP8_ROW ? p.rs[0][row] : p.tscale[0]) : 0.0f;
   uint64_t key[M];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
@@ -342,20 +342,20 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
   const int full_chunks = p.d_in / kChunkK;  // chunks with all 8 pieces present
   const int tail_pieces = (p.d_in % kChunkK) / kPieceK;
 
-  // Items are (chunk, matrix) pairs visited chunk-major; FP8 (chunk, half).
+  // Items are (chunk, half, matrix) visited chunk-major, matrix fastest; an FP8
+  // tile is streamed as two halves, an NVFP4/MXFP4 tile whole.
   constexpr bool F8 = FMT == FP4G_FP8_ROW;
-  constexpr int PER = F8 ? 2 : NMAT;  // items per chunk
+  constexpr int HALVES = F8 ? 2 : 1;
+  constexpr int PER = HALVES * NMAT;  // items per chunk
   const int n_items = (c1 - c0) * PER;
   const int64_t tile0 = (int64_t)g * p.C;
   auto item_tile = [&](int it) {
-    if constexpr (F8)
-      return w0 + (tile0 + c0 + it / 2) * TILE + (it & 1) * (kHalfFp8 * 1024);
-    else
-      return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / NMAT) * TILE;
+    const uint8_t* t = (it % NMAT ? w1 : w0) + (tile0 + c0 + it / PER) * TILE;
+    return F8 ? t + ((it / NMAT) % HALVES) * (kHalfFp8 * 1024) : t;
   };
   auto consume = [&](const Frag<FMT>& f, int it) {
     const int c = c0 + it / PER;
-    const int half = F8 ? (it & 1) : 0;
+    const int half = F8 ? (it / NMAT) % HALVES : 0;
     const uint32_t* xc = x32 + (int64_t)c * (kChunkK / 2) + half * (kHalfFp8 * 8);
     float part[M];
 #pragma unroll

@@ -106,13 +106,30 @@ def matrix(fmt: int, d_out: int, d_in: int, seed: int, device="cpu", batch: int 
     return {"format": fmt, "d_out": d_out, "d_in": d_in, "codes": codes, "scales": scales, "tensor_scale": 1.0}
 
 
-# ---- the five workloads (shapes from the pages; see the design doc for the recipe) ----
+# ---- the workloads' shapes (from the pages) ----
 
 HIDDEN = 5120          # dense model hidden size
 FFN = 17408            # dense MLP intermediate size
 ATTN_SHAPES = ((12288, 5120), (12288, 5120), (5120, 12288), (7680, 5120))
 LAYERS = 64
 VOCAB = 248320
+
+# The mixed layout of the dense checkpoint (feed, section "Fewer bytes per weight:
+# NVFP4": the MLPs of layers 0..55 are NVFP4; the attention and linear-attention
+# projections, the output layer and the MLPs of the last 8 layers are FP8;
+# section "Decode speed is bytes divided by bandwidth" puts full attention in
+# every fourth layer, linear attention in the other 48).  The pages give only the
+# largest projection, 12288x5120, and the byte shares (MLP 59%, linear attention
+# 31%, full attention 9% of 17.83 GB): these projection shapes are a reading that
+# reproduces both (17.78 GB for 64 layers, 19.05 GB with the head).
+MIXED_FP8_MLP_FROM = 56                                        # first layer with an FP8 MLP
+MIXED_GDN_SHAPES = ((12288, 5120), (5120, 10240))              # linear attention: in, out
+MIXED_ATTN_SHAPES = ((12288, 5120), (1024, 5120), (1024, 5120), (5120, 6144))  # q, k, v, out
+
+
+def mixed_full_attention(layer: int) -> bool:
+    return layer % 4 == 3
+
 
 MOE_HIDDEN = 2560
 MOE_FF = 768

@@ -262,10 +262,12 @@ int32_t fp4_gemv_grouped(const fp4g_group* G_host, const uint16_t* X_dev, int32_
 
 /* Fused MLP front half: g = Wg X_m, u = Wu X_m, H_dev[m][r] = bf16_rne(SiLU(g[r]) *
  * u[r]) with SiLU(z) = z / (1 + e^-z), for m < M in 1..16 (above 8 on the
- * matrix-core path only).  Wg and Wu are NVFP4 or
- * MXFP4 matrices of one shape d_ff x hidden (feed, section "Decode speed is bytes
- * divided by bandwidth": gate and up projections are 17408 x 5120 in the dense
- * model).  X_dev: bf16 [M][hidden]; H_dev: bf16 [M][d_ff]. */
+ * matrix-core path only).  Wg and Wu are NVFP4 or MXFP4 matrices of one shape
+ * d_ff x hidden (feed, section "Decode speed is bytes divided by bandwidth":
+ * gate and up projections are 17408 x 5120 in the dense model), or two FP8_ROW
+ * matrices, each with its own row scales (the FP8 MLPs of the last layers in the
+ * feed's mixed checkpoint, section "Fewer bytes per weight: NVFP4"; VALU path,
+ * M in 1..8).  X_dev: bf16 [M][hidden]; H_dev: bf16 [M][d_ff]. */
 int32_t fp4_gate_up_silu(const fp4g_weight* Wg_host, const fp4g_weight* Wu_host,
                          const uint16_t* X_dev, int32_t M, uint16_t* H_dev, int32_t path,
                          void* ws_dev, uint64_t ws_bytes, void* stream);

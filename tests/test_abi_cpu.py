@@ -143,8 +143,10 @@ def test_grouped_error_paths():
     assert call_grouped(group_desc(q, k2)) == E_FORMAT                 # mixed formats
     k3 = good_desc(d_out=64, d_in=256); k3.packed = FAKE + (8 << 30)
     assert call_grouped(group_desc(q, k3)) == E_SHAPE                  # mixed d_in
-    f8 = good_desc(fg.FP8_ROW)
-    assert call_grouped(group_desc(f8)) == E_FORMAT                    # FP8 rows go to the head call
+    f8 = good_desc(fg.FP8_ROW); f8b = good_desc(fg.FP8_ROW, d_out=64); f8b.packed = FAKE + (8 << 30)
+    assert call_grouped(group_desc(f8, k)) == E_FORMAT                 # FP8 rows with NVFP4
+    assert call_grouped(group_desc(f8, f8b), path=fg.PATH_MFMA) == E_PATH  # FP8 rows: VALU only
+    assert call_grouped(group_desc(f8, f8b), M=9) == E_SHAPE
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), 0]) == E_NULL
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (3 << 30) + 4]) == E_ALIGN
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (2 << 30) + 256]) == E_ALIAS
@@ -217,6 +219,13 @@ def test_gate_up_error_paths():
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, 3, None, 0, None) == E_PATH
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 17, H, 0, None, 0, None) == E_SHAPE
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 9, H, fg.PATH_VALU, None, 0, None) == E_PATH
+    # FP8 row pairs (a mixed layout's FP8 MLPs): VALU only, up to 8 vectors, one format per pair
+    g8, u8 = good_desc(fg.FP8_ROW), good_desc(fg.FP8_ROW); u8.packed = FAKE + (8 << 30)
+    assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u), X, 1, H, 0, None, 0, None) == E_FORMAT
+    assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u8), X, 1, H, fg.PATH_MFMA, None, 0, None) == E_PATH
+    assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u8), X, 9, H, 0, None, 0, None) == E_SHAPE
+    big8 = good_desc(fg.FP8_ROW, 17408, 5120)
+    assert fg.workspace_bytes(fg.OP_GATE_UP, big8, 8) > 0 and fg.workspace_bytes(fg.OP_GATE_UP, big8, 9) == 0
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, None, 0, None, 0, None) == E_NULL
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, X, 0, None, 0, None) == E_ALIAS
 

@@ -72,3 +72,35 @@ def test_seeds_are_stable_and_distinct():
     a = datagen.matrix(datagen.NVFP4, 64, 256, 3)
     b = datagen.matrix(datagen.NVFP4, 64, 256, 3)
     assert torch.equal(a["codes"], b["codes"]) and torch.equal(a["scales"], b["scales"])
+
+
+def test_mixed_layout_reproduces_the_pages_byte_split():
+    """The mixed-layout workload (FP8 projections, NVFP4 MLPs in layers 0..55, FP8
+    MLPs in 56..63) is a reading of the pages' shapes: it must reproduce their
+    layer bytes (17.83 GB), step bytes with the head (19.10 GB) and the shares of
+    MLP / linear attention / full attention (59 / 31 / 9%)."""
+    import json
+    from pathlib import Path
+
+    import bit_weight_gemv_fp4_amd as fg
+
+    page = json.loads((Path(__file__).parent / "golden" / "page_numbers.json").read_text())
+    H, F = datagen.HIDDEN, datagen.FFN
+    nv = lambda o, i: fg.packed_bytes(fg.NVFP4, o, i)
+    f8 = lambda o, i: fg.packed_bytes(fg.FP8_ROW, o, i)
+    full = [L for L in range(datagen.LAYERS) if datagen.mixed_full_attention(L)]
+    assert len(full) == datagen.LAYERS // page["byte_shares_of_layers"]["full_attention_every"]
+    assert datagen.LAYERS - len(full) == page["byte_shares_of_layers"]["linear_attention_layers"]
+    assert datagen.MIXED_FP8_MLP_FROM == page["mixed_layout"]["nvfp4_mlp_layers"][1] + 1
+    assert max(o * i for o, i in datagen.MIXED_GDN_SHAPES + datagen.MIXED_ATTN_SHAPES) == 12288 * 5120
+    mlp = sum(3 * (nv if L < datagen.MIXED_FP8_MLP_FROM else f8)(F, H) for L in range(datagen.LAYERS))
+    gdn = sum(f8(o, i) for L in range(datagen.LAYERS) if L not in full for o, i in datagen.MIXED_GDN_SHAPES)
+    att = sum(f8(o, i) for L in full for o, i in datagen.MIXED_ATTN_SHAPES)
+    layers = mlp + gdn + att
+    shares = page["byte_shares_of_layers"]
+    assert abs(mlp / layers - shares["mlp"]) < 0.01
+    assert abs(gdn / layers - shares["linear_attention"]) < 0.01
+    assert abs(att / layers - shares["full_attention"]) < 0.01
+    assert abs(layers / 1e9 - page["bytes_per_step_gb"]["layers_gb"]) / page["bytes_per_step_gb"]["layers_gb"] < 0.005
+    step = layers + f8(datagen.VOCAB, H)
+    assert abs(step / 1e9 - page["bytes_per_step_gb"]["value"]) / page["bytes_per_step_gb"]["value"] < 0.005

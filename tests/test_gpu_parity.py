@@ -1,8 +1,10 @@
 """GPU parity of every C-ABI entry point against the FP64 oracle.  Needs gfx950.
 
-Bars (derived in the design doc):
+Bars:
   * packing / unpacking and top-k ids: bit-exact;
-  * products: |y_gpu - y_ref| <= 2e-3 * sum_k |w x| per row;
+  * products: |y_gpu - y_ref| <= 2e-3 * sum_k |w x| per row (every product w x is
+    exact in FP32, so only the FP32 summation rounds; a decode or layout slip
+    breaks the bound);
   * fused h = bf16(SiLU(g) u): |h - h_ref| <= 1.1 tg (|u| + tu) + |SiLU(g)| tu + 2^-8 |h_ref|,
     with tg, tu the product bounds of g and u;
   * MoE gate weights: relative 1e-5; MoE output given the GPU's own h and gate
@@ -680,3 +682,59 @@ def test_wide_verify_refuses_the_valu_path():
         fg.fp4_skinny_gemm(W, X, path=fg.PATH_VALU)
     with pytest.raises(fg.Fp4gError):
         fg.fp4_skinny_gemm(W, datagen.bf16_normal((17, 1056), 5, device=DEV))
+
+
+# ---- mixed layout: FP8 row-scaled MLPs and projections, the MoE router ---------------------
+
+
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_fp8_gate_up_silu_matches_oracle(M):
+    """The FP8 MLPs of a mixed layout: gate and up as FP8 rows, each with its own
+    row scales, fused with SiLU * mul (ragged shapes, tails of 32 columns)."""
+    log("fp8 gate_up", M)
+    for shape in ((200, 1056), (130, 544), (64, 256)):
+        Wg, hg = make(fg.FP8_ROW, *shape, seed=15)
+        Wu, hu = make(fg.FP8_ROW, *shape, seed=16)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("X8g", M, shape), device=DEV)
+        check_h(fg.fp4_gate_up_silu(Wg, Wu, X), hg, hu, bits(X))
+
+
+def test_fp8_mlp_full_size():
+    """One FP8 MLP of the dense model (gate/up 17408x5120, down 5120x17408), sampled rows."""
+    log("fp8 MLP full")
+    Wg, hg = make(fg.FP8_ROW, 17408, 5120, seed=300)
+    Wu, hu = make(fg.FP8_ROW, 17408, 5120, seed=301)
+    Wd, hd = make(fg.FP8_ROW, 5120, 17408, seed=302)
+    x = datagen.bf16_normal((1, 5120), 303, device=DEV)
+    H = fg.fp4_gate_up_silu(Wg, Wu, x)
+    check_h(H, hg, hu, bits(x), rows=sample_rows(17408, 160, seed=3))
+    check_product(fg.fp8_lmhead_gemv(Wd, H), hd, bits(H), rows=sample_rows(5120, 160, seed=4))
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_fp8_grouped_projections(M):
+    """FP8 projections of one input in one launch (members with their own row
+    scales): equal to the single-matrix products up to the FP32 summation order."""
+    log("fp8 grouped", M)
+    shapes = [(300, 1056), (64, 1056), (128, 1056)]
+    mats = [make(fg.FP8_ROW, o, i, seed=("g8", j)) for j, (o, i) in enumerate(shapes)]
+    X = datagen.bf16_normal((M, 1056), datagen.tensor_seed("g8X", M), device=DEV)
+    Ys = fg.fp4_gemv_grouped(fg.Group([W for W, _ in mats]), X)
+    for (W, host), Y in zip(mats, Ys):
+        check_product(Y, host, bits(X))
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_router_gemv_feeds_moe(M):
+    """The MoE router as an FP8 row-scaled 512x2560 product in front of
+    moe_route_gemv: its logits within the product bound, then the full layer
+    (512 MXFP4 experts, top-8 + shared) routed on those very logits, checked
+    stage by stage against the oracle (ids exact)."""
+    log("router -> moe", M)
+    Wr, hr = make(fg.FP8_ROW, datagen.MOE_EXPERTS, datagen.MOE_HIDDEN, seed=310)
+    X = datagen.bf16_normal((M, datagen.MOE_HIDDEN), datagen.tensor_seed("rX", M), device=DEV)
+    logits = fg.fp8_lmhead_gemv(Wr, X)
+    check_product(logits, hr, bits(X))
+    layer, expert, sh = build_moe(fg.MXFP4, datagen.MOE_EXPERTS, datagen.MOE_TOPK, datagen.MOE_HIDDEN,
+                                  datagen.MOE_FF, seed=311)
+    check_moe(layer, expert, sh, X, logits, datagen.MOE_TOPK)
