@@ -39,6 +39,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaXBytes = 40960;  // LDS for the staged input of one workgroup
 constexpr int kZeroBytes = 512;     // one chunk row of zeros
+// Each vector's staged row is padded by 64 bytes: rows then start 16 banks apart
+// (64 banks of 4 bytes), so the lanes that read the same columns of different
+// vectors (an A operand) hit different banks instead of one.
+constexpr int kXPad = 64;
 constexpr int kMfmaRedOwn = 0;      // values per lane up to which the reduction has its own LDS
 
 constexpr int kMfmaSlots = 4;  // code slots per work item (half a tile: fewer registers, more waves)
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   // the staged-input area, reused once every wave has finished reading it.
   constexpr bool kRedInX = NV > kMfmaRedOwn;
   __shared__ float red_own[kRedInX ? 1 : kWavesPerWg][kRedInX ? 1 : NV][64];
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // [M][wg_chunks * 512] bf16, then zeros
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // [M][wg_chunks * 512 + kXPad] bf16, then zeros
   float(*red)[NV][64] = kRedInX ? reinterpret_cast<float(*)[NV][64]>(xs) : reinterpret_cast<float(*)[NV][64]>(red_own);
 
   const int lane = threadIdx.x & 63;
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
 
   // stage x[m][256 wg_c0 ..) for m < M (zero past d_in), then the zero area; all
   // loads are issued before the first LDS store
-  const int tstride = p.wg_chunks * 512;  // bytes per vector in LDS
+  const int tstride = p.wg_chunks * 512 + kXPad;  // bytes per vector in LDS
   {
     constexpr int kMaxPieces = kMfmaXBytes / 16 / kThreads;
     const int per_tok = p.wg_chunks * 32;  // 16-byte pieces per vector
@@ -368,7 +372,7 @@ inline Plan plan_mfma(int64_t R, int64_t C, int nmat, int M) {
 // Dynamic LDS of a launch: the staged input, or the reduction buffer where it
 // lives there and is larger.
 inline size_t mfma_lds_bytes(const Plan& pl, uint32_t fmt, int nmat, int M) {
-  const size_t staged = (size_t)M * pl.wg_chunks * 512 + kZeroBytes;
+  const size_t staged = (size_t)M * (pl.wg_chunks * 512 + kXPad) + kZeroBytes;
   const int nv = nmat * (fmt == FP4G_NVFP4 && M <= 8 ? 8 : 16);  // values per lane at the end
   const size_t red = nv > kMfmaRedOwn ? (size_t)kWavesPerWg * nv * 64 * 4 : 0;
   return staged > red ? staged : red;
