@@ -7,14 +7,22 @@ dense weight stream of one decoded token at M = 1 -- 64 layers, each an NVFP4 ML
 attention projections (12288x5120, 12288x5120, 5120x12288, 7680x5120), then an
 FP8 E4M3 LM head 248320x5120 with FP32 row scales: 19.11 GB of weights per token,
 the figure the mdjawad.com DGX Spark feed counts (19.10 GB).  A step is one token:
-385 kernel launches replayed from one HIP graph.  Inputs are seeded synthetic
-tensors already resident in HBM.
+257 kernel launches (per layer gate/up, down, the three projections of x as one
+grouped launch, the output projection; then the head) replayed from one HIP
+graph.  Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints ONE JSON line: achieved GB/s (algorithmic bytes / time), implied tok/s,
 the roofline of the dominant kernel (timed live with HIP events), and the
 FP64 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload c3|c1|c2|c4|c5]
+    python bench.py [--steps K] [--warmup W] [--workload c3|c3m|c1|c2|c4|c5|head|copy]
+                    [--M vectors] [--path auto|valu|mfma] [--router] [--breakdown]
+
+Other workloads: c1 one 5120x5120 NVFP4 GEMV; c2 the NVFP4 MLP; c4 the MLP at a
+verify block of M vectors (up to 16); c3m the dense stream in the checkpoint's
+mixed NVFP4/FP8 layout; c5 the MoE decode (--router: router logits from an FP8
+product of x); head the FP8 head with the fused greedy pick and a draft head;
+copy a 1 GiB device copy (the reference for HBM counter calibration).
 """
 from __future__ import annotations
 

@@ -345,8 +345,8 @@ class Group:
 
 
 def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, path: int = PATH_AUTO, ws=None, stream=None):
-    """Ys[i][m] = W_i X[m] for every member W_i of G, X bf16 [M, d_in] (or [d_in]);
-    returns the list of float32 [M, d_out_i] outputs."""
+    """Ys[i][m] = W_i X[m] for every member W_i of G (NVFP4/MXFP4, or FP8 rows),
+    X bf16 [M, d_in] (or [d_in]); returns the list of float32 [M, d_out_i] outputs."""
     X2 = X if X.dim() == 2 else X.view(1, -1)
     M = X2.shape[0]
     if Ys is None:
@@ -360,7 +360,8 @@ def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, path: int = PATH_AUTO, 
 
 def fp4_gate_up_silu(Wg: PackedWeight, Wu: PackedWeight, X: torch.Tensor, H: torch.Tensor | None = None,
                      path: int = PATH_AUTO, ws=None, stream=None) -> torch.Tensor:
-    """H = bf16(SiLU(Wg X) * (Wu X)) for X bf16 [M, d_in]; returns bf16 [M, d_out]."""
+    """H = bf16(SiLU(Wg X) * (Wu X)) for X bf16 [M, d_in] (an NVFP4/MXFP4 pair, or
+    an FP8 row-scaled pair); returns bf16 [M, d_out]."""
     X2 = X if X.dim() == 2 else X.view(1, -1)
     M = X2.shape[0]
     if H is None:

@@ -253,10 +253,12 @@ int32_t fp4_skinny_gemm(const fp4g_weight* W_host, const uint16_t* X_dev, int32_
 
 /* Several products of one input in one launch: Y_dev[i][m][r] = sum_k
  * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..16 (above 8 on
- * the matrix-core path only).  X_dev: bf16
- * [M][d_in]; Y_dev: host array of G->n device pointers, each f32 [M][w_i.d_out],
- * 16-B aligned and disjoint.  path: fp4g_path.  Each member's results are those
- * of fp4_skinny_gemm on it alone up to the order of the FP32 additions. */
+ * the matrix-core path only).  Members share format and d_in: NVFP4 or MXFP4,
+ * or FP8_ROW with each member's own row scales (the FP8 projections of a mixed
+ * layout; VALU path, M in 1..8).  X_dev: bf16 [M][d_in]; Y_dev: host array of
+ * G->n device pointers, each f32 [M][w_i.d_out], 16-B aligned and disjoint.
+ * path: fp4g_path.  Each member's results are those of fp4_skinny_gemm (FP8:
+ * fp8_lmhead_gemv) on it alone up to the order of the FP32 additions. */
 int32_t fp4_gemv_grouped(const fp4g_group* G_host, const uint16_t* X_dev, int32_t M,
                          float* const* Y_host, int32_t path, void* ws_dev, uint64_t ws_bytes, void* stream);
 
