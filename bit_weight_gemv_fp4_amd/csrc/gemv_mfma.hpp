@@ -112,8 +112,23 @@ __device__ __forceinline__ float add_halves(float x, int lane) {
   return x + __uint_as_float(lane < 32 ? t[1] : t[0]);
 }
 
-template <uint32_t FMT, int M, int NMAT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
+// The mixture-of-experts gate/up product on this kernel (MOE = true): row group
+// gt of the launch is (slot gt / rg, group gt % rg); slot i multiplies expert
+// route[1 + i] (-1: the shared expert), slots from route[0] on do nothing, and h
+// goes to slot i's rows of the workspace, [slot][M][d_ff].
+struct MfmaMoe {
+  const int32_t* route;  // [0] = slots in use, [1 + i] = expert of slot i (-1 = shared)
+  uint64_t stride[2];    // bytes between experts: gate, up (p.w[0], p.w[1] = expert 0)
+  const uint8_t* sh[2];  // the shared expert's gate, up
+  float sh_ts[2];        // and their tensor scales
+  int rg;                // 64-row groups per expert
+  uint16_t* hdbg;        // optional bf16 [M][k + shared][d_ff]: h per (token, pick)
+  const int32_t* ids;    // [M][k] picked experts
+  int k, nh;             // picks per token; k + shared
+};
+
+template <uint32_t FMT, int M, int NMAT, int EPI, bool MOE = false>
+__global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   // NVFP4 with up to 8 vectors: both blocks of a slot in one MFMA (A rows 8..15
   // carry the second block); the outputs of lanes i and i + 32 then add up
   constexpr bool PACK2 = FMT == FP4G_NVFP4 && M <= 8;
@@ -132,10 +147,19 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
   const int wave = wave_id();
   const int gt = uniform(blockIdx.x / p.S);
   const int s = uniform(blockIdx.x % p.S);
-  const int mem = NMAT == 1 ? member_of(p, gt) : 0;
-  const int g = gt - p.gbase[mem];
+  const int mem = NMAT == 1 && !MOE ? member_of(p, gt) : 0;
+  int g = gt - p.gbase[mem];
   const uint8_t* w0 = p.w[mem];
   const uint8_t* w1 = NMAT == 2 ? p.w[1] : w0;
+  int slot = 0, expert = 0;
+  if constexpr (MOE) {
+    slot = uniform(gt / q.rg);
+    g = gt - slot * q.rg;
+    if (slot >= q.route[0]) return;  // past the realised union: no byte read
+    expert = q.route[1 + slot];
+    w0 = expert >= 0 ? p.w[0] + (uint64_t)expert * q.stride[0] : q.sh[0];
+    w1 = expert >= 0 ? p.w[1] + (uint64_t)expert * q.stride[1] : q.sh[1];
+  }
   const int wg_c0 = s * p.wg_chunks;
   const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
   const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
@@ -336,8 +360,20 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p) {
       const int rr = u / 4, v = u % 4;
       const int m = vbase + v, row = g * 64 + 16 * (rb0 + rr) + cl;
       if (m < M && row < d_out) {
-        const float gv = ua[u] * p.tscale[0], uv = ub[u] * p.tscale[1];
-        p.h[(int64_t)m * d_out + row] = f32_to_bf16_rne(silu_f32(gv) * uv);
+        const float tg = MOE && expert < 0 ? q.sh_ts[0] : p.tscale[0];
+        const float tu = MOE && expert < 0 ? q.sh_ts[1] : p.tscale[1];
+        const uint16_t hv = f32_to_bf16_rne(silu_f32(ua[u] * tg) * (ub[u] * tu));
+        p.h[((int64_t)slot * M + m) * d_out + row] = hv;
+        if constexpr (MOE) {
+          if (q.hdbg) {
+            if (expert < 0) {
+              q.hdbg[((int64_t)m * q.nh + q.k) * d_out + row] = hv;
+            } else {
+              for (int j = 0; j < q.k; ++j)
+                if (q.ids[m * q.k + j] == expert) q.hdbg[((int64_t)m * q.nh + j) * d_out + row] = hv;
+            }
+          }
+        }
       }
     } else {
       const int rr = u / 2, w = u % 2;
@@ -399,10 +435,25 @@ hipError_t launch_mfma(int M, const GemvParams& p, unsigned grid, size_t lds, hi
   switch (M) {
 #define FP4G_CASE(MM)                                                       \
   case MM:                                                                  \
-    k_gemv_mfma<FMT, MM, NMAT, EPI><<<grid, kThreads, lds, s>>>(p); \
+    k_gemv_mfma<FMT, MM, NMAT, EPI><<<grid, kThreads, lds, s>>>(p, MfmaMoe{}); \
     break;
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
     FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The mixture-of-experts gate/up launch (M = 3..8).
+template <uint32_t FMT>
+hipError_t launch_mfma_moe(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds, hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM)                                                                 \
+  case MM:                                                                            \
+    k_gemv_mfma<FMT, MM, 2, EPI_SILU, true><<<grid, kThreads, lds, s>>>(p, q); \
+    break;
+    FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
 #undef FP4G_CASE
     default: return hipErrorInvalidValue;
   }

@@ -27,14 +27,29 @@
 //             experts need no combine step; the K shares meet in the exchange
 //             tree, whose survivor writes Y.
 //
-// Both kernels use the tile loop, the split-K tree and the launch planner of the
-// dense product (gemv_kernel.hpp).  Results are deterministic.
+// From M = 3 vectors on, the gate/up half runs on the matrix cores instead:
+// k_moe_route (one workgroup) routes the tokens once and writes the tables, then
+// the matrix-core product (gemv_mfma.hpp) takes each slot's expert from them, and
+// k_moe_down follows as above.
+//
+// The kernels use the tile loop, the split-K tree and the launch planner of the
+// dense product (gemv_kernel.hpp, gemv_mfma.hpp).  Results are deterministic.
 #include <algorithm>
 
-#include "gemv_kernel.hpp"
+#include "gemv_mfma.hpp"
 
 namespace fp4g {
+
+// Matrix-core gate/up launchers, in gemv_mfma_moe.hip.
+extern template hipError_t launch_mfma_moe<FP4G_NVFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
+                                                       hipStream_t);
+extern template hipError_t launch_mfma_moe<FP4G_MXFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
+                                                       hipStream_t);
+
 namespace {
+
+constexpr int kMoeMfmaMinM = 3;  // gate/up on the matrix cores from this many vectors
+constexpr int kMoeMfmaUnits = 16;  // exchange units per lane of that kernel's fused epilogue (at most)
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 8;
@@ -161,6 +176,31 @@ __device__ __forceinline__ float coef_of(const RouteLds<M>& r, const MoeParams& 
   return c;
 }
 
+// The routing outputs and tables: top-k ids and weights, the slots' experts and
+// their per-token coefficients (gate weight x down tensor scale), slot count.
+template <int M, int NW>
+__device__ void write_route_tables(const MoeParams& p, const RouteLds<M>& r) {
+  for (int i = threadIdx.x; i < M * p.K; i += NW * 64) {
+    const int m = i / p.K, j = i % p.K;
+    p.topk_ids[i] = r.ids[m][j];
+    p.topk_w[i] = r.w[m][j];
+  }
+  for (int i = threadIdx.x; i < r.n_slots; i += NW * 64) {
+    p.route[1 + i] = r.uni[i];
+    const float tsd = r.uni[i] >= 0 ? p.ts_down : p.ts_sh_down;
+    for (int m = 0; m < M; ++m) p.coef[i * M + m] = coef_of<M>(r, p, i, m) * tsd;
+  }
+  if (threadIdx.x == 0) p.route[0] = r.n_slots;
+}
+
+// Routing alone (in front of the matrix-core gate/up): one workgroup of 4 waves.
+template <int M>
+__global__ __launch_bounds__(256) void k_moe_route(MoeParams p) {
+  __shared__ RouteLds<M> r;
+  route_tokens<M, 4>(p, r);
+  write_route_tables<M, 4>(p, r);
+}
+
 template <uint32_t FMT, int M, int NW>
 __global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : kTileMx;
@@ -170,19 +210,7 @@ __global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
   route_tokens<M, NW>(p, r);
 
   const int lane = threadIdx.x & 63, wave = wave_id();
-  if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i < M * p.K; i += NW * 64) {
-      const int m = i / p.K, j = i % p.K;
-      p.topk_ids[i] = r.ids[m][j];
-      p.topk_w[i] = r.w[m][j];
-    }
-    for (int i = threadIdx.x; i < r.n_slots; i += NW * 64) {
-      p.route[1 + i] = r.uni[i];
-      const float tsd = r.uni[i] >= 0 ? p.ts_down : p.ts_sh_down;
-      for (int m = 0; m < M; ++m) p.coef[i * M + m] = coef_of<M>(r, p, i, m) * tsd;
-    }
-    if (threadIdx.x == 0) p.route[0] = r.n_slots;
-  }
+  if (blockIdx.x == 0) write_route_tables<M, NW>(p, r);
 
   const int per_slot = p.Rg * p.S_up;
   const int slot = uniform(blockIdx.x / per_slot);
@@ -356,6 +384,9 @@ struct MoeLayout {
 constexpr int kUpWavesPerCu = 12;
 inline Plan plan_up(int64_t R, int64_t C) { return plan_latency(R, C, kUpWavesPerCu, {4, 8, 12}); }
 inline Plan plan_dn(int64_t R, int64_t C, int M) { return plan_latency(R, C, M <= 5 ? 16 : 12, {4, 8, 16}); }
+// gate/up plan and exchange units per lane for M vectors (either kernel)
+inline Plan plan_gu(int64_t R, int64_t C, int M) { return M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C); }
+inline int units_gu(int M) { return M >= kMoeMfmaMinM ? kMoeMfmaUnits : M; }
 
 // Workspace: exchange slots first, sized for the largest need over M = 1..8
 // (they must start zero-filled and every call leaves them zero), then the
@@ -373,18 +404,18 @@ MoeLayout moe_layout(const fp4g_moe* mo, int M) {
   L.Cg = chunks(mo->hidden);
   L.Rd = row_groups(mo->hidden);
   L.Cd = chunks(mo->d_ff);
-  L.up = plan_up(L.Rg * L.n_slots_max, L.Cg);
+  L.up = plan_gu(L.Rg * L.n_slots_max, L.Cg, M);
   L.dn = plan_dn(L.Rd, L.Cd * L.n_slots_max, M);
   uint64_t slot_bytes = 0;
   for (int m = 1; m <= kMaxM; ++m) {
     const int ns = n_slots_for(mo, m);
-    const Plan up = plan_up(L.Rg * ns, L.Cg), dn = plan_dn(L.Rd, L.Cd * ns, m);
-    const uint64_t b = align256(8ull * tree_nodes(up.S) * m * ns * L.Rg * 64) +
+    const Plan up = plan_gu(L.Rg * ns, L.Cg, m), dn = plan_dn(L.Rd, L.Cd * ns, m);
+    const uint64_t b = align256(8ull * tree_nodes(up.S) * units_gu(m) * ns * L.Rg * 64) +
                        align256(8ull * tree_nodes(dn.S) * ((m + 1) / 2) * L.Rd * 64);
     slot_bytes = std::max(slot_bytes, b);
   }
   L.off_x_up = 0;
-  L.off_x_dn = align256(8ull * tree_nodes(L.up.S) * M * L.n_slots_max * L.Rg * 64);
+  L.off_x_dn = align256(8ull * tree_nodes(L.up.S) * units_gu(M) * L.n_slots_max * L.Rg * 64);
   const int ns8 = n_slots_for(mo, kMaxM);
   uint64_t o = slot_bytes;
   L.off_route = o;
@@ -424,17 +455,29 @@ fp4g_status check_moe(const fp4g_moe* mo) {
   return FP4G_OK;
 }
 
-template <uint32_t FMT, int M>
-hipError_t launch_moe_m(const MoeParams& p, const Plan& up, const Plan& dn, unsigned grid_up, unsigned grid_dn,
-                        hipStream_t s) {
-  switch (up.nw) {
-    case 4: k_moe_up<FMT, M, 4><<<grid_up, 256, 0, s>>>(p); break;
-    case 8: k_moe_up<FMT, M, 8><<<grid_up, 512, 0, s>>>(p); break;
-    case 12: k_moe_up<FMT, M, 12><<<grid_up, 768, 0, s>>>(p); break;
+// The matrix-core gate/up's view of the layer (used from kMoeMfmaMinM vectors on).
+struct MoeMfma {
+  GemvParams gp;
+  MfmaMoe q;
+  size_t lds;
+};
 
-    default: return hipErrorInvalidValue;
+template <uint32_t FMT, int M>
+hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, const Plan& dn, unsigned grid_up,
+                        unsigned grid_dn, hipStream_t s) {
+  if constexpr (M >= kMoeMfmaMinM) {
+    k_moe_route<M><<<1, 256, 0, s>>>(p);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (launch_mfma_moe<FMT>(M, mf.gp, mf.q, grid_up, mf.lds, s) != hipSuccess) return hipErrorLaunchFailure;
+  } else {
+    switch (up.nw) {
+      case 4: k_moe_up<FMT, M, 4><<<grid_up, 256, 0, s>>>(p); break;
+      case 8: k_moe_up<FMT, M, 8><<<grid_up, 512, 0, s>>>(p); break;
+      case 12: k_moe_up<FMT, M, 12><<<grid_up, 768, 0, s>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   switch (dn.nw) {
     case 4: k_moe_down<FMT, M, 4><<<grid_dn, 256, 0, s>>>(p); break;
     case 8: k_moe_down<FMT, M, 8><<<grid_dn, 512, 0, s>>>(p); break;
@@ -450,12 +493,12 @@ hipError_t launch_moe_m(const MoeParams& p, const Plan& up, const Plan& dn, unsi
 }
 
 template <uint32_t FMT>
-hipError_t launch_moe(int M, const MoeParams& p, const Plan& up, const Plan& dn, unsigned grid_up, unsigned grid_dn,
-                      hipStream_t s) {
+hipError_t launch_moe(int M, const MoeParams& p, const MoeMfma& mf, const Plan& up, const Plan& dn, unsigned grid_up,
+                      unsigned grid_dn, hipStream_t s) {
   switch (M) {
 #define FP4G_CASE(MM) \
   case MM:            \
-    return launch_moe_m<FMT, MM>(p, up, dn, grid_up, grid_dn, s);
+    return launch_moe_m<FMT, MM>(p, mf, up, dn, grid_up, grid_dn, s);
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
 #undef FP4G_CASE
     default: return hipErrorInvalidValue;
@@ -549,9 +592,42 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   p.S_dn = L.dn.S;
   const unsigned grid_up = (unsigned)(L.n_slots_max * L.Rg * L.up.S);
   const unsigned grid_dn = (unsigned)(L.Rd * L.dn.S);
+  MoeMfma mf{};
+  if (M >= kMoeMfmaMinM) {
+    GemvParams& gp = mf.gp;
+    gp.n = 1;
+    gp.w[0] = p.gate;
+    gp.w[1] = p.up;
+    gp.tscale[0] = p.ts_gate;
+    gp.tscale[1] = p.ts_up;
+    gp.d_out[0] = mo->d_ff;
+    gp.gbase[0] = 0;
+    gp.gbase[1] = (int)(L.n_slots_max * L.Rg);
+    gp.x = X;
+    gp.h = p.hbuf;
+    gp.slots = p.x_up;
+    gp.d_in = mo->hidden;
+    gp.C = (int)L.Cg;
+    gp.S = L.up.S;
+    gp.wg_chunks = L.up.wg_chunks;
+    MfmaMoe& q = mf.q;
+    q.route = p.route;
+    q.stride[0] = p.sg;
+    q.stride[1] = p.su;
+    q.sh[0] = p.sh_gate;
+    q.sh[1] = p.sh_up;
+    q.sh_ts[0] = p.ts_sh_gate;
+    q.sh_ts[1] = p.ts_sh_up;
+    q.rg = (int)L.Rg;
+    q.hdbg = H;
+    q.ids = topk_ids;
+    q.k = mo->top_k;
+    q.nh = nh;
+    mf.lds = mfma_lds_bytes(L.up, mo->gate.format, 2, M);
+  }
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = mo->gate.format == FP4G_NVFP4
-                           ? launch_moe<FP4G_NVFP4>(M, p, L.up, L.dn, grid_up, grid_dn, s)
-                           : launch_moe<FP4G_MXFP4>(M, p, L.up, L.dn, grid_up, grid_dn, s);
+                           ? launch_moe<FP4G_NVFP4>(M, p, mf, L.up, L.dn, grid_up, grid_dn, s)
+                           : launch_moe<FP4G_MXFP4>(M, p, mf, L.up, L.dn, grid_up, grid_dn, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
