@@ -107,6 +107,7 @@ __device__ void route_tokens(const MoeParams& p, RouteLds<M>& r) {
       key[t] = (t < per_lane && e < p.E) ? pick_key(lg[e], e) : 0ull;
     }
     const bool wide = per_lane > kPer / 2;  // uniform: more than 512 experts
+    float myv = 0.0f, v0 = 0.0f;           // lane j < K: the logit of pick j; the largest
     for (int j = 0; j < p.K; ++j) {
       uint64_t best = key[0];
 #pragma unroll
@@ -118,17 +119,22 @@ __device__ void route_tokens(const MoeParams& p, RouteLds<M>& r) {
       best = wave_max_key(best);
 #pragma unroll
       for (int t = 0; t < kPer; ++t) key[t] = key[t] == best ? 0ull : key[t];
+      const float bv = key_value(best);
+      if (j == 0) v0 = bv;  // picks come in descending order
+      if (lane == j) myv = bv;
       if (lane == 0) {
         r.ids[m][j] = key_index(best);
-        r.v[m][j] = key_value(best);
+        r.v[m][j] = bv;
       }
     }
-    if (lane == 0) {
-      // picks are in descending order, so the first is the maximum
-      float z = 0.0f;
-      for (int j = 0; j < p.K; ++j) z += expf(r.v[m][j] - r.v[m][0]);
-      for (int j = 0; j < p.K; ++j) r.w[m][j] = expf(r.v[m][j] - r.v[m][0]) / z;
-    }
+    // softmax over the K picks, one pick per lane (lanes 0..7; K <= 8): the sum
+    // of the exponentials by a butterfly over those lanes
+    const float ej = lane < p.K ? expf(myv - v0) : 0.0f;
+    float z = ej;
+    z += __shfl_xor(z, 1, 64);
+    z += __shfl_xor(z, 2, 64);
+    z += __shfl_xor(z, 4, 64);
+    if (lane < p.K) r.w[m][lane] = ej / z;
   }
   __syncthreads();
   if (threadIdx.x < M * p.K) {
@@ -185,10 +191,11 @@ __device__ void write_route_tables(const MoeParams& p, const RouteLds<M>& r) {
     p.topk_ids[i] = r.ids[m][j];
     p.topk_w[i] = r.w[m][j];
   }
-  for (int i = threadIdx.x; i < r.n_slots; i += NW * 64) {
-    p.route[1 + i] = r.uni[i];
+  for (int i = threadIdx.x; i < r.n_slots; i += NW * 64) p.route[1 + i] = r.uni[i];
+  for (int t = threadIdx.x; t < r.n_slots * M; t += NW * 64) {  // one (slot, token) per thread
+    const int i = t / M, m = t - i * M;
     const float tsd = r.uni[i] >= 0 ? p.ts_down : p.ts_sh_down;
-    for (int m = 0; m < M; ++m) p.coef[i * M + m] = coef_of<M>(r, p, i, m) * tsd;
+    p.coef[t] = coef_of<M>(r, p, i, m) * tsd;
   }
   if (threadIdx.x == 0) p.route[0] = r.n_slots;
 }
