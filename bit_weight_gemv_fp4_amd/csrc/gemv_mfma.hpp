@@ -112,23 +112,33 @@ __device__ __forceinline__ float add_halves(float x, int lane) {
   return x + __uint_as_float(lane < 32 ? t[1] : t[0]);
 }
 
-// The mixture-of-experts gate/up product on this kernel (MOE = true): row group
-// gt of the launch is (slot gt / rg, group gt % rg); slot i multiplies expert
-// route[1 + i] (-1: the shared expert), slots from route[0] on do nothing, and h
-// goes to slot i's rows of the workspace, [slot][M][d_ff].
+// Mixture-of-experts modes of this kernel.
+//  MODE 1, gate/up: row group gt of the launch is (slot gt / rg, group gt % rg);
+//    slot i multiplies expert route[1 + i] (-1: the shared expert), slots from
+//    route[0] on do nothing, and h goes to slot i's rows of the workspace,
+//    [slot][M][d_ff].
+//  MODE 2, down: the K dimension runs over the union's slots, cd chunks each
+//    (chunk v is chunk v % cd of slot v / cd's expert, its input that slot's h);
+//    each chunk's products are weighted per token by coef[slot][token] (gate
+//    weight x down tensor scale) before they add up, so the experts need no
+//    combine step.  Chunks past the realised union do nothing.
 struct MfmaMoe {
   const int32_t* route;  // [0] = slots in use, [1 + i] = expert of slot i (-1 = shared)
-  uint64_t stride[2];    // bytes between experts: gate, up (p.w[0], p.w[1] = expert 0)
-  const uint8_t* sh[2];  // the shared expert's gate, up
-  float sh_ts[2];        // and their tensor scales
-  int rg;                // 64-row groups per expert
+  uint64_t stride[2];    // bytes between experts: gate, up (p.w[0], p.w[1] = expert 0); down: [0]
+  const uint8_t* sh[2];  // the shared expert's gate, up; down: [0]
+  float sh_ts[2];        // and their tensor scales (gate/up)
+  int rg;                // 64-row groups per expert (gate/up)
   uint16_t* hdbg;        // optional bf16 [M][k + shared][d_ff]: h per (token, pick)
   const int32_t* ids;    // [M][k] picked experts
   int k, nh;             // picks per token; k + shared
+  const float* coef;     // down: [slot][M]
+  const uint16_t* hbuf;  // down: bf16 [slot][M][d_ff]
+  int cd, dff;           // down: chunks per slot; d_ff
 };
 
-template <uint32_t FMT, int M, int NMAT, int EPI, bool MOE = false>
+template <uint32_t FMT, int M, int NMAT, int EPI, int MODE = 0>
 __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q) {
+  constexpr bool MOE = MODE == 1, MOED = MODE == 2;
   // NVFP4 with up to 8 vectors: both blocks of a slot in one MFMA (A rows 8..15
   // carry the second block); the outputs of lanes i and i + 32 then add up
   constexpr bool PACK2 = FMT == FP4G_NVFP4 && M <= 8;
@@ -163,15 +173,29 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q)
   const int wg_c0 = s * p.wg_chunks;
   const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
   const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
-  const int c0 = min(wg_c1, wg_c0 + wave * per_wave);
-  const int c1 = min(wg_c1, c0 + per_wave);
+  int c0 = min(wg_c1, wg_c0 + wave * per_wave);
+  int c1 = min(wg_c1, c0 + per_wave);
+  int n_valid = p.C;  // chunks that carry data (down: those of the realised union)
+  if constexpr (MOED) {
+    n_valid = uniform(q.route[0]) * q.cd;
+    c1 = min(c1, n_valid);
+    c0 = min(c0, c1);
+  }
   const int cl = lane & 15;   // A row / B column of the lane
   const int kg = lane >> 4;   // K group of the lane
-  const int64_t tile0 = (int64_t)g * p.C;
+  const int64_t tile0 = (int64_t)g * (MOED ? q.cd : p.C);
   // items (chunk, part, matrix), matrix fastest: with NMAT = 2 the even items
   // are gate, the odd ones up
   constexpr int SL = MFrag<FMT>::SL, PER = 8 / SL;  // parts per tile
-  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / (PER * NMAT)) * TILE; };
+  auto item_tile = [&](int it) {
+    const int cv = c0 + it / (PER * NMAT);
+    if constexpr (MOED) {
+      const int sl = cv / q.cd, e = q.route[1 + sl];
+      const uint8_t* base = e >= 0 ? p.w[0] + (uint64_t)e * q.stride[0] : q.sh[0];
+      return base + (tile0 + (cv - sl * q.cd)) * TILE;
+    }
+    return (it % NMAT ? w1 : w0) + (tile0 + cv) * TILE;
+  };
   auto item_half = [&](int it) { return (it / NMAT) % PER; };
 
   // first fragment in flight before the input is staged
@@ -192,8 +216,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q)
       const int idx = threadIdx.x + k * kThreads;
       v[k] = u32x4{0u, 0u, 0u, 0u};
       const int m = idx / per_tok, r = idx - m * per_tok;
-      const int col = wg_c0 * kChunkK + r * 8;
-      if (idx < pieces && col < p.d_in) v[k] = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.d_in + col);
+      if constexpr (MOED) {
+        // chunk cv of the union: columns of slot cv / cd's h (zero past d_ff and
+        // past the union)
+        const int cv = wg_c0 + r / 32, sl = cv / q.cd, col = (cv - sl * q.cd) * kChunkK + (r % 32) * 8;
+        if (idx < pieces && cv < n_valid && col < q.dff)
+          v[k] = *reinterpret_cast<const u32x4*>(q.hbuf + ((int64_t)sl * M + m) * q.dff + col);
+      } else {
+        const int col = wg_c0 * kChunkK + r * 8;
+        if (idx < pieces && col < p.d_in) v[k] = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.d_in + col);
+      }
     }
 #pragma unroll
     for (int k = 0; k < kMaxPieces; ++k) {
@@ -238,6 +270,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q)
   auto consume = [&](MFrag<FMT>& f, int it, f32x4(&ac)[4]) {
     const int cc = c0 + it / (PER * NMAT) - wg_c0;  // chunk within the staged range
     const int half = item_half(it);
+    // weights of the lane's four vectors (MoE down: the chunk's slot's
+    // coefficients; 1 otherwise, which the compiler folds away)
+    float cf[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (MOED) {
+      const int sl = (cc + wg_c0) / q.cd;
+      const int tb = PACK2 ? 4 * (kg & 1) : 4 * kg;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cf[v] = tb + v < M ? q.coef[sl * M + tb + v] : 0.0f;
+    }
 #pragma unroll
     for (int jj = 0; jj < SL; ++jj) {
       const int j = SL * half + jj;  // slot within the chunk
@@ -264,15 +305,16 @@ __global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q)
           if constexpr (PACK2) {
             const float sc = kg < 2 ? s0 : s1;  // output rows 0..7: first block, 8..15: second
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(d[0][r][v], sc, ac[r][v]);
+            for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(d[0][r][v], sc * cf[v], ac[r][v]);
           } else {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(d[1][r][v], s1, __builtin_fmaf(d[0][r][v], s0, ac[r][v]));
+            for (int v = 0; v < 4; ++v)
+              ac[r][v] = __builtin_fmaf(d[1][r][v], s1 * cf[v], __builtin_fmaf(d[0][r][v], s0 * cf[v], ac[r][v]));
           }
         } else {
           const int e = (int)((f.s[r][jj >> 2] >> (8 * (jj & 3))) & 0xffu) - 127;
 #pragma unroll
-          for (int v = 0; v < 4; ++v) ac[r][v] += __builtin_amdgcn_ldexpf(d[0][r][v], e);
+          for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(__builtin_amdgcn_ldexpf(d[0][r][v], e), cf[v], ac[r][v]);
         }
       }
       // keep each slot's LDS reads and conversions next to its MFMAs
@@ -445,13 +487,28 @@ hipError_t launch_mfma(int M, const GemvParams& p, unsigned grid, size_t lds, hi
   return hipGetLastError();
 }
 
-// The mixture-of-experts gate/up launch (M = 3..8).
+// The mixture-of-experts gate/up (MODE 1) and down (MODE 2) launches, M = 3..8.
 template <uint32_t FMT>
 hipError_t launch_mfma_moe(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds, hipStream_t s) {
   switch (M) {
 #define FP4G_CASE(MM)                                                                 \
   case MM:                                                                            \
-    k_gemv_mfma<FMT, MM, 2, EPI_SILU, true><<<grid, kThreads, lds, s>>>(p, q); \
+    k_gemv_mfma<FMT, MM, 2, EPI_SILU, 1><<<grid, kThreads, lds, s>>>(p, q); \
+    break;
+    FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <uint32_t FMT>
+hipError_t launch_mfma_moe_down(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds,
+                                hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM)                                                           \
+  case MM:                                                                      \
+    k_gemv_mfma<FMT, MM, 1, EPI_STORE, 2><<<grid, kThreads, lds, s>>>(p, q); \
     break;
     FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
 #undef FP4G_CASE

@@ -45,11 +45,17 @@ extern template hipError_t launch_mfma_moe<FP4G_NVFP4>(int, const GemvParams&, c
                                                        hipStream_t);
 extern template hipError_t launch_mfma_moe<FP4G_MXFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
                                                        hipStream_t);
+extern template hipError_t launch_mfma_moe_down<FP4G_NVFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
+                                                            hipStream_t);
+extern template hipError_t launch_mfma_moe_down<FP4G_MXFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
+                                                            hipStream_t);
 
 namespace {
 
-constexpr int kMoeMfmaMinM = 3;  // gate/up on the matrix cores from this many vectors
-constexpr int kMoeMfmaUnits = 16;  // exchange units per lane of that kernel's fused epilogue (at most)
+constexpr int kMoeMfmaMinM = 3;    // gate/up on the matrix cores from this many vectors
+constexpr int kMoeMfmaDnMinM = 5;  // down on the matrix cores from this many (measured crossover)
+constexpr int kMoeMfmaUnits = 16;  // exchange units per lane of that kernel: fused epilogue (at most)
+constexpr int kMoeMfmaUnitsDn = 8;  // and plain products (at most)
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 8;
@@ -394,6 +400,11 @@ inline Plan plan_dn(int64_t R, int64_t C, int M) { return plan_latency(R, C, M <
 // gate/up plan and exchange units per lane for M vectors (either kernel)
 inline Plan plan_gu(int64_t R, int64_t C, int M) { return M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C); }
 inline int units_gu(int M) { return M >= kMoeMfmaMinM ? kMoeMfmaUnits : M; }
+// down plan and units: C counts the union's slots x d_ff chunks
+inline Plan plan_down(int64_t R, int64_t C, int M) {
+  return M >= kMoeMfmaDnMinM ? plan_mfma(R, C, 1, M) : plan_dn(R, C, M);
+}
+inline int units_dn(int M) { return M >= kMoeMfmaDnMinM ? kMoeMfmaUnitsDn : (M + 1) / 2; }
 
 // Workspace: exchange slots first, sized for the largest need over M = 1..8
 // (they must start zero-filled and every call leaves them zero), then the
@@ -412,13 +423,13 @@ MoeLayout moe_layout(const fp4g_moe* mo, int M) {
   L.Rd = row_groups(mo->hidden);
   L.Cd = chunks(mo->d_ff);
   L.up = plan_gu(L.Rg * L.n_slots_max, L.Cg, M);
-  L.dn = plan_dn(L.Rd, L.Cd * L.n_slots_max, M);
+  L.dn = plan_down(L.Rd, L.Cd * L.n_slots_max, M);
   uint64_t slot_bytes = 0;
   for (int m = 1; m <= kMaxM; ++m) {
     const int ns = n_slots_for(mo, m);
-    const Plan up = plan_gu(L.Rg * ns, L.Cg, m), dn = plan_dn(L.Rd, L.Cd * ns, m);
+    const Plan up = plan_gu(L.Rg * ns, L.Cg, m), dn = plan_down(L.Rd, L.Cd * ns, m);
     const uint64_t b = align256(8ull * tree_nodes(up.S) * units_gu(m) * ns * L.Rg * 64) +
-                       align256(8ull * tree_nodes(dn.S) * ((m + 1) / 2) * L.Rd * 64);
+                       align256(8ull * tree_nodes(dn.S) * units_dn(m) * L.Rd * 64);
     slot_bytes = std::max(slot_bytes, b);
   }
   L.off_x_up = 0;
@@ -464,9 +475,9 @@ fp4g_status check_moe(const fp4g_moe* mo) {
 
 // The matrix-core gate/up's view of the layer (used from kMoeMfmaMinM vectors on).
 struct MoeMfma {
-  GemvParams gp;
-  MfmaMoe q;
-  size_t lds;
+  GemvParams gp, gpd;  // gate/up, down
+  MfmaMoe q, qd;
+  size_t lds, lds_d;
 };
 
 template <uint32_t FMT, int M>
@@ -485,16 +496,20 @@ hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, c
     }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
-  switch (dn.nw) {
-    case 4: k_moe_down<FMT, M, 4><<<grid_dn, 256, 0, s>>>(p); break;
-    case 8: k_moe_down<FMT, M, 8><<<grid_dn, 512, 0, s>>>(p); break;
-    case 16:
-      if constexpr (M <= 5) {  // and for plain products up to M = 5
-        k_moe_down<FMT, M, 16><<<grid_dn, 1024, 0, s>>>(p);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  if constexpr (M >= kMoeMfmaDnMinM) {
+    return launch_mfma_moe_down<FMT>(M, mf.gpd, mf.qd, grid_dn, mf.lds_d, s);
+  } else {
+    switch (dn.nw) {
+      case 4: k_moe_down<FMT, M, 4><<<grid_dn, 256, 0, s>>>(p); break;
+      case 8: k_moe_down<FMT, M, 8><<<grid_dn, 512, 0, s>>>(p); break;
+      case 16:
+        if constexpr (M <= 5) {  // and for plain products up to M = 5
+          k_moe_down<FMT, M, 16><<<grid_dn, 1024, 0, s>>>(p);
+          break;
+        }
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
@@ -631,6 +646,28 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
     q.k = mo->top_k;
     q.nh = nh;
     mf.lds = mfma_lds_bytes(L.up, mo->gate.format, 2, M);
+    GemvParams& gd = mf.gpd;
+    gd.n = 1;
+    gd.w[0] = p.down;
+    gd.tscale[0] = 1.0f;  // the coefficients carry the down tensor scales
+    gd.y[0] = Y;
+    gd.d_out[0] = mo->hidden;
+    gd.gbase[0] = 0;
+    gd.gbase[1] = (int)L.Rd;
+    gd.slots = p.x_dn;
+    gd.d_in = mo->d_ff;
+    gd.C = (int)(L.Cd * L.n_slots_max);
+    gd.S = L.dn.S;
+    gd.wg_chunks = L.dn.wg_chunks;
+    MfmaMoe& qd = mf.qd;
+    qd.route = p.route;
+    qd.stride[0] = p.sd;
+    qd.sh[0] = p.sh_down;
+    qd.coef = p.coef;
+    qd.hbuf = p.hbuf;
+    qd.cd = (int)L.Cd;
+    qd.dff = mo->d_ff;
+    mf.lds_d = mfma_lds_bytes(L.dn, mo->gate.format, 1, M);
   }
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = mo->gate.format == FP4G_NVFP4
