@@ -206,12 +206,15 @@ __device__ void write_route_tables(const MoeParams& p, const RouteLds<M>& r) {
   if (threadIdx.x == 0) p.route[0] = r.n_slots;
 }
 
-// Routing alone (in front of the matrix-core gate/up): one workgroup of 4 waves.
+// Routing alone (in front of the matrix-core gate/up): one workgroup, one wave
+// per token (at least 4).
 template <int M>
-__global__ __launch_bounds__(256) void k_moe_route(MoeParams p) {
+constexpr int route_waves() { return M > 4 ? M : 4; }
+template <int M>
+__global__ __launch_bounds__(route_waves<M>() * 64) void k_moe_route(MoeParams p) {
   __shared__ RouteLds<M> r;
-  route_tokens<M, 4>(p, r);
-  write_route_tables<M, 4>(p, r);
+  route_tokens<M, route_waves<M>()>(p, r);
+  write_route_tables<M, route_waves<M>()>(p, r);
 }
 
 template <uint32_t FMT, int M, int NW>
@@ -484,7 +487,7 @@ template <uint32_t FMT, int M>
 hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, const Plan& dn, unsigned grid_up,
                         unsigned grid_dn, hipStream_t s) {
   if constexpr (M >= kMoeMfmaMinM) {
-    k_moe_route<M><<<1, 256, 0, s>>>(p);
+    k_moe_route<M><<<1, route_waves<M>() * 64, 0, s>>>(p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (launch_mfma_moe<FMT>(M, mf.gp, mf.q, grid_up, mf.lds, s) != hipSuccess) return hipErrorLaunchFailure;
   } else {
