@@ -4,8 +4,8 @@
 // The Ling-3.0 MoE decode article (magicnetworld.com, sec. 3 and the sec. 4
 // flowchart) routes each token to 8 of 512 experts plus a shared expert, reads
 // only the chosen experts' weights and accumulates back to the hidden size; its
-// sec. 8 notes that M tokens read the union of their experts.  Two launches, and
-// routing never leaves the device:
+// sec. 8 notes that M tokens read the union of their experts.  Routing never
+// leaves the device.  For M = 1, 2 two launches:
 //
 //  k_moe_up   Every workgroup first routes all M tokens itself (top-k of the
 //             logits by a wave arg-max per pick, softmax over the k picked, the
@@ -30,7 +30,8 @@
 // From M = 3 vectors on, the gate/up half runs on the matrix cores instead:
 // k_moe_route (one workgroup) routes the tokens once and writes the tables, then
 // the matrix-core product (gemv_mfma.hpp) takes each slot's expert from them, and
-// k_moe_down follows as above.
+// k_moe_down follows as above; from M = 5 on the down half also runs on the
+// matrix-core kernel (its down mode).  Measured crossovers set both thresholds.
 //
 // The kernels use the tile loop, the split-K tree and the launch planner of the
 // dense product (gemv_kernel.hpp, gemv_mfma.hpp).  Results are deterministic.

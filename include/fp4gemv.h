@@ -286,7 +286,7 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg_host, const fp4g_weight* Wu_host,
  * Only the union of the M tokens' experts is read from memory; routing never
  * leaves the device.  Two launches for M = 1, 2 (every gate/up workgroup routes
  * the tokens itself); three from M = 3 on (routing once, gate/up on the matrix
- * cores, down).
+ * cores, then down: on the VALU up to M = 4, on the matrix cores from M = 5).
  *   X_dev       bf16 [M][hidden];  logits_dev f32 [M][num_experts];
  *   Y_dev       f32  [M][hidden];
  *   topk_ids_dev i32 [M][top_k];  topk_w_dev f32 [M][top_k];
