@@ -552,7 +552,7 @@ def check_moe(layer, expert, sh_host, X, logits, k, has_shared=True):
     return ids
 
 
-@pytest.mark.parametrize("M", [1, 2, 5, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
 def test_moe_small(M):
     log("moe small", M)
     layer, expert, sh = build_moe(fg.MXFP4, 16, 4, 256, 128, seed=1)
@@ -576,9 +576,10 @@ def test_moe_ties_and_repeat():
     assert torch.equal(Y1, Y2)
 
 
-@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("M", [1, 4, 6, 8])
 def test_config5_moe_layer(M):
-    """Ling-3.0-flash-shaped MoE layer: 512 MXFP4 experts 768x2560 / 2560x768, top-8 + shared."""
+    """Ling-3.0-flash-shaped MoE layer: 512 MXFP4 experts 768x2560 / 2560x768, top-8 + shared
+    (M = 1: VALU gate/up and down; 4: matrix-core gate/up; 6, 8: both halves on the matrix cores)."""
     log("C5 moe", M)
     layer, expert, sh = build_moe(fg.MXFP4, 512, 8, 2560, 768, seed=5)
     X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("C5x", M), device=DEV)
