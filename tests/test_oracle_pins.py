@@ -470,3 +470,91 @@ def test_quant_nvfp4_error_within_a_grid_step():
         for b in range(8):
             k = b * 16 + int(np.argmax(np.abs(wb[r, b * 16:(b + 1) * 16])))
             assert Q._E2M1[el[r, k] & 7] in (4.0, 6.0), (r, b)
+
+
+# ---- W4A8: MXFP8 activations ------------------------------------------------------------------
+from oracle import w4a8 as A8  # noqa: E402
+
+
+def _bf16_bits(x):
+    return torch.tensor(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _w4a8_inputs(M, d_in, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((M, d_in)).astype(np.float32)
+    x[0, :32] = 0.0                       # an all-zero block
+    x[-1, 32:64] *= 1e-6                  # tiny values (E4M3 subnormal range of the block)
+    x[-1, 64:96] *= 1e4                   # a large block
+    return _bf16_bits(x)
+
+
+def test_w4a8_block_scale_is_the_smallest_without_saturation():
+    """Every block's 2^e is the smallest power of two that keeps amax / 2^e <=
+    448, so no element saturates (checked against exact float arithmetic)."""
+    bits = _w4a8_inputs(3, 256, 1)
+    x = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, scales = A8.quantize_mxfp8(bits)
+    for m in range(3):
+        for b in range(8):
+            amax = np.max(np.abs(x[m, 32 * b:32 * b + 32]))
+            e = int(scales[m, b]) - 127
+            if amax == 0:
+                assert e == 0 and not codes[m, 32 * b:32 * b + 32].any()
+                continue
+            assert amax / 2.0 ** e <= 448.0 < amax / 2.0 ** (e - 1)
+
+
+def test_w4a8_elements_are_the_nearest_e4m3():
+    """Each element is the nearest E4M3 value of x / 2^e by brute force over the
+    whole grid (ties to the even code), with the sign restored."""
+    bits = _w4a8_inputs(2, 128, 2)
+    x = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, scales = A8.quantize_mxfp8(bits)
+    grid = np.array([Q._E4M3[c] for c in range(127)])
+    for m in range(2):
+        for k in range(128):
+            q = abs(x[m, k]) / 2.0 ** (int(scales[m, k // 32]) - 127)
+            d = np.abs(grid - q)
+            best = np.flatnonzero(d == d.min())
+            c = int(codes[m, k]) & 0x7F
+            assert c in best and (len(best) == 1 or c % 2 == 0), (m, k, q, c)
+            assert (codes[m, k] >> 7) == (1 if (x[m, k] < 0 and c != 0) else 0)
+
+
+def test_w4a8_representable_inputs_round_trip():
+    """Activations that are E4M3 values times a block's power of two, with the
+    block maximum at 448 * 2^e, quantise without loss."""
+    g = np.random.default_rng(3)
+    e = g.integers(-20, 10, size=(2, 4))
+    vals = Q._E4M3[g.integers(0, 127, size=(2, 128))] * np.where(g.random((2, 128)) < 0.5, -1, 1)
+    vals[:, ::32] = 448.0
+    x = vals * np.exp2(np.repeat(e, 32, axis=1))
+    bits = _bf16_bits(x)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64), x)
+    codes, scales = A8.quantize_mxfp8(bits)
+    assert np.array_equal(scales.astype(np.int64) - 127, e)
+    assert np.array_equal(A8.dequant_mxfp8(codes, scales), x)
+
+
+def test_w4a8_product_is_the_gemv_of_the_quantised_activations():
+    """The W4A8 product equals the (independently pinned) C oracle's GEMV of the
+    dequantised activations, which are exact in bf16; and it stays within the
+    activation rounding of the bf16-activation product."""
+    mat = datagen.matrix(datagen.MXFP4, 96, 256, 5)
+    bits = _w4a8_inputs(3, 256, 4)
+    Y, A = A8.gemv(datagen.MXFP4, mat["codes"], mat["scales"], 1.0, bits)
+    codes, scales = A8.quantize_mxfp8(bits)
+    xq = A8.dequant_mxfp8(codes, scales)
+    xq_bits = _bf16_bits(xq)
+    assert np.array_equal((xq_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64), xq)
+    Yc, _ = oracle.gemv(datagen.MXFP4, mat["codes"], mat["scales"], 1.0, xq_bits)
+    assert np.allclose(Y, Yc, rtol=1e-12, atol=1e-12 * A.max())
+    # against the bf16-activation product: |x - xq| <= 2^-4 |x| + half an E4M3
+    # subnormal step (2^-10 * 2^e) per element
+    x = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    Yb, _ = oracle.gemv(datagen.MXFP4, mat["codes"], mat["scales"], 1.0, bits)
+    W = oracle.dequant(datagen.MXFP4, mat["codes"], mat["scales"])
+    step = np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, axis=1) - 10)
+    bound = (2.0 ** -4 * np.abs(x) + step) @ np.abs(W).T
+    assert np.all(np.abs(Y - Yb) <= bound * (1 + 1e-12))
