@@ -73,8 +73,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3m", "c4", "c5", "head", "copy"],
-                    help="c3m: the dense stream in the checkpoint's mixed NVFP4/FP8 layout")
+    ap.add_argument("--workload", default="c3",
+                    choices=["c1", "c2", "c3", "c3m", "c4", "c5", "head", "skinny", "copy"],
+                    help="c3m: the dense stream in the checkpoint's mixed NVFP4/FP8 layout; skinny: one "
+                         "17408x5120 product at M vectors (--fmt, --path)")
+    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"], help="weight format of the skinny workload")
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
     ap.add_argument("--router", action="store_true",
                     help="c5: compute each layer's router logits with an FP8 512x2560 product of x")
@@ -82,7 +85,7 @@ def parse():
                     help="full layers the CPU oracle runs for cpu_baseline (about 0.45 s each on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
-    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma"],
+    ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "a8"],
                     help="kernel path of the NVFP4/MXFP4 products (auto: MFMA from M = 3 on)")
     ap.add_argument("--engine", default="launches", choices=["stream", "launches"],
                     help="stream: one persistent launch per step (fp4_stream_run); launches: one launch per product")
@@ -273,10 +276,25 @@ def copies_for(nbytes, min_total=1 << 30):
     return max(1, -(-min_total // nbytes))
 
 
-def build_other(name, M, fg, datagen, torch, path=0, router=False):
+def build_other(name, M, fg, datagen, torch, path=0, router=False, fmt=None):
     dev = "cuda"
     H, F = datagen.HIDDEN, datagen.FFN
     keep = []
+    if name == "skinny":
+        fmt = fmt or fg.NVFP4
+        nb = fg.packed_bytes(fmt, F, H)
+        R = copies_for(nb)
+        step = Step(R)
+        X = datagen.bf16_normal((M, H), datagen.tensor_seed("skinny", "x", M), device=dev)
+        Y = torch.empty((M, F), dtype=torch.float32, device=dev)
+        keep += [X, Y]
+        for r in range(R):
+            m = datagen.matrix(fmt, F, H, datagen.tensor_seed("skinny", r), device=dev)
+            W = fg.pack(fmt, m["codes"], m["scales"], m["tensor_scale"])
+            keep.append(W)
+            step.add("skinny", (lambda W=W: fg.fp4_skinny_gemm(W, X, Y, path=path)), algorithmic_gemv_bytes(fg, fmt, F, H, M))
+        name_f = "NVFP4" if fmt == fg.NVFP4 else "MXFP4"
+        return step, keep, f"one {name_f} product 17408x5120 at M={M} ({R} copies rotated)", "skinny"
     if name == "c1":
         nb = fg.packed_bytes(fg.NVFP4, H, H)
         R = copies_for(nb)
@@ -473,7 +491,7 @@ def main():
     if args.workload == "copy":
         return copy_calibration(torch)
     dev = "cuda"
-    M = args.M or (4 if args.workload in ("c4",) else 1)
+    M = args.M or (4 if args.workload in ("c4", "skinny") else 1)
     t_setup = time.perf_counter()
     if args.workload == "c3":
         step, keep, sops = build_dense_stream(fg, datagen, torch, datagen.LAYERS, True, M=M)
@@ -495,8 +513,9 @@ def main():
                     f"MLPs 17408x5120 x2 + 5120x17408 NVFP4 in layers 0-55 and FP8 in 56-63, + FP8 LM head 248320x5120")
         dominant = "gate_up_silu"
     else:
-        path = {"auto": fg.PATH_AUTO, "valu": fg.PATH_VALU, "mfma": fg.PATH_MFMA}[args.path]
-        step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch, path, args.router)
+        path = {"auto": fg.PATH_AUTO, "valu": fg.PATH_VALU, "mfma": fg.PATH_MFMA, "a8": fg.PATH_A8}[args.path]
+        fmt = {"nvfp4": fg.NVFP4, "mxfp4": fg.MXFP4}[args.fmt]
+        step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch, path, args.router, fmt)
     bytes_per_step = step.bytes() / step.steps_per_replay
     engine = args.engine if args.workload == "c3" else "launches"
     # one eager pass allocates the workspace and checks every launch

@@ -15,7 +15,7 @@ from pathlib import Path
 import torch
 
 __all__ = [
-    "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA",
+    "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_A8",
     "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "MAX_M", "MAX_M_WIDE", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
     "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
@@ -23,7 +23,7 @@ __all__ = [
 ]
 
 NVFP4, MXFP4, FP8_ROW = 1, 2, 3
-PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_VALU, PATH_MFMA, PATH_A8 = 0, 1, 2, 3
 OP_GEMV, OP_GATE_UP, OP_MOE, OP_LMHEAD, OP_GROUPED, OP_LMHEAD_ARGMAX = 1, 2, 3, 4, 5, 6
 MAX_GROUP = 4
 MAX_M, MAX_M_WIDE = 8, 16  # vectors per call; the wider range on the matrix-core path only

@@ -57,6 +57,16 @@ __device__ __forceinline__ u32x2 ld_stream2(const void* p) {
 
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
 
+// E4M3FN code of t >= 0 (finite), round to nearest even, saturating at 448
+// (the load-time quantisers and the 8-bit activation staging).
+__device__ __forceinline__ uint32_t e4m3_rne_pos(float t) {
+  if (t >= 448.0f) return 126u;
+  if (t < 0.015625f) return (uint32_t)rintf(t * 512.0f);  // m x 2^-9; m = 8 is code 8 = 2^-6
+  const int E = (int)((__float_as_uint(t) >> 23) & 0xffu) - 127;  // floor(log2 t), t normal
+  const float m = rintf((__builtin_amdgcn_ldexpf(t, -E) - 1.0f) * 8.0f);  // exact up to the rounding
+  return (uint32_t)(((E + 7) << 3) + (int)m);  // m = 8 carries into the exponent
+}
+
 // Two E2M1 codes (byte SEL of dw: bits 0-3 -> .x, bits 4-7 -> .y) to exact bf16.
 template <int SEL>
 __device__ __forceinline__ bf16x2 e2m1x2_bf16(uint32_t dw) {

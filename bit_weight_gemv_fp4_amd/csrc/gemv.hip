@@ -1,7 +1,7 @@
 // gemv.hip -- launch planning, host-side validation and the product entry points
 // fp4_gemv, fp4_skinny_gemm, fp4_gemv_grouped, fp4_gate_up_silu and
 // fp8_lmhead_gemv.  The kernel itself is in gemv_kernel.hpp.
-#include "gemv_mfma.hpp"
+#include "gemv_a8.hpp"
 
 namespace fp4g {
 
@@ -14,6 +14,8 @@ extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, int, const Gem
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_ARGMAX>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
+// W4A8 launcher (gemv_a8.hpp), in gemv_a8.hip.
+hipError_t launch_a8_ext(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s);
 // Matrix-core launchers (gemv_mfma.hpp), in gemv_mfma_nvfp4.hip and gemv_mfma_mxfp4.hip.
 extern template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
 extern template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
@@ -37,7 +39,7 @@ static bool use_mfma(int32_t path, uint32_t format, int M) {
 static bool valid_path(int32_t path, bool fp4, int M) {
   if (path == FP4G_PATH_AUTO) return true;
   if (path == FP4G_PATH_VALU) return M <= kMaxM;
-  return path == FP4G_PATH_MFMA && fp4;
+  return (path == FP4G_PATH_MFMA || path == FP4G_PATH_A8) && fp4;
 }
 
 // Workspace check shared by every entry point: NULL only when nothing is needed,
@@ -73,7 +75,9 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   for (int i = 0; i < n; ++i) R_total += row_groups(W[i]->d_out);
   const int64_t C = chunks(W[0]->d_in);
   if (!valid_path(path, want_fp4, M)) return FP4G_E_PATH;
-  const bool mfma = use_mfma(path, W[0]->format, M);
+  const bool a8 = path == FP4G_PATH_A8;  // W4A8: MXFP4 weights only
+  if (a8 && W[0]->format != FP4G_MXFP4) return FP4G_E_PATH;
+  const bool mfma = a8 || use_mfma(path, W[0]->format, M);
   const uint64_t need = gemv_ws_bytes_any(R_total, C, 1, M);
   const fp4g_status wst = check_ws(ws, ws_bytes, need);
   if (wst != FP4G_OK) return wst;
@@ -113,7 +117,9 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   const unsigned grid = (unsigned)(R_total * pl.S);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (mfma)
+  if (a8)
+    e = launch_a8_ext(M, p, grid, a8_lds_bytes(pl, M), s);
+  else if (mfma)
     e = W[0]->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, W[0]->format, 1, M), s)
                                    : launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, W[0]->format, 1, M), s);
   else if (W[0]->format == FP4G_NVFP4)
@@ -252,7 +258,7 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   if (Wg->d_out != Wu->d_out || Wg->d_in != Wu->d_in) return FP4G_E_SHAPE;
   if (!X || !H) return FP4G_E_NULL;
   if (M < 1 || M > (fp4 ? kMaxMWide : kMaxM)) return FP4G_E_SHAPE;
-  if (!valid_path(path, fp4, M)) return FP4G_E_PATH;
+  if (!valid_path(path, fp4, M) || path == FP4G_PATH_A8) return FP4G_E_PATH;
   if (!aligned(X, 16) || !aligned(H, 16)) return FP4G_E_ALIGN;
   const bool mfma = use_mfma(path, Wg->format, M);
   const int64_t R = row_groups(Wg->d_out), C = chunks(Wg->d_in);

@@ -1,0 +1,213 @@
+// gemv_a8.hpp -- MXFP4 weights times 8-bit activations (W4A8, the Ling-3.0 MoE
+// article's measured configuration, sec. 5-6) on the scaled matrix cores of
+// gfx950: v_mfma_scale_f32_16x16x128_f8f6f4 with the activations as the FP8
+// E4M3 A operand and the weights as the FP4 E2M1 B operand, both with their own
+// E8M0 scale per 32 K, applied by the instruction.
+//
+//  * Staging: each workgroup quantises its input range to MXFP8 in LDS -- per
+//    vector and 32 columns the smallest power of two 2^e with amax / 2^e <= 448
+//    (E4M3's largest value, so nothing saturates), elements E4M3 of x / 2^e
+//    rounded to nearest even -- codes [M][chunks * 256] and scales
+//    [M][chunks * 8], zero past d_in.
+//  * Operand layouts of the instruction (measured on the device): B lane i holds
+//    column i % 16 (a weight row), K 32 (i / 16) .. +31 in its first 4 dwords --
+//    one packed slot after the 16-lane-group transpose (once per dword); A lane
+//    i holds row i % 16 (a vector) with K 16 (i / 16) .. +15 in bytes 0-15 and
+//    K 64 + 16 (i / 16) .. +15 in bytes 16-31; the scale of lane i applies to K
+//    block i / 16 of its row or column.
+//  * One MFMA per 16-row block and half tile (4 slots = K 128), accumulating in
+//    place: no conversion and no scale arithmetic on the VALU.
+// The split-K tree and the epilogue are those of the other kernels.
+#pragma once
+#include "gemv_mfma.hpp"
+
+namespace fp4g {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// LDS of a launch: codes + scales of M vectors (rows padded by 64 bytes), then a
+// zero area of one window, or the reduction buffer where that is larger.
+inline size_t a8_lds_bytes(const Plan& pl, int M) {
+  const size_t staged = (size_t)M * (pl.wg_chunks * 264 + kXPad) + kZeroBytes;
+  const size_t red = (size_t)kWavesPerWg * 16 * 64 * 4;
+  return staged > red ? staged : red;
+}
+
+template <int M>
+__global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
+  constexpr int NV = 16;  // values per lane at the end: rows 16 r + cl, vectors 4 kg + v
+  constexpr int TILE = kTileMx;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  float(*red)[NV][64] = reinterpret_cast<float(*)[NV][64]>(xs);  // after the products
+
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int gt = uniform(blockIdx.x / p.S);
+  const int s = uniform(blockIdx.x % p.S);
+  const int mem = member_of(p, gt);
+  const int g = gt - p.gbase[mem];
+  const uint8_t* w0 = p.w[mem];
+  const int wg_c0 = s * p.wg_chunks;
+  const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
+  const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
+  const int c0 = min(wg_c1, wg_c0 + wave * per_wave);
+  const int c1 = min(wg_c1, c0 + per_wave);
+  const int cl = lane & 15, kg = lane >> 4;
+  const int64_t tile0 = (int64_t)g * p.C;
+  auto item_tile = [&](int it) { return w0 + (tile0 + c0 + it / 2) * TILE; };
+
+  const int n_items = (c1 - c0) * 2;  // half tiles
+  MFrag<FP4G_MXFP4> fa, fb;
+  if (n_items > 0) load_mfrag<FP4G_MXFP4>(fa, item_tile(0), 0, lane);
+
+  // staging: codes of vector m at m * cstride, its scales at sbase + m * sstride
+  const int cstride = p.wg_chunks * 256 + kXPad;
+  const int sbase = M * cstride, sstride = p.wg_chunks * 8;
+  const int zbase = sbase + M * sstride + ((16 - (M * sstride) % 16) % 16);  // 16-B aligned zero area
+  {
+    const int nblk = M * p.wg_chunks * 8;  // 32-column blocks
+    for (int b = threadIdx.x; b < nblk; b += kThreads) {
+      const int m = b / (p.wg_chunks * 8), j = b - m * (p.wg_chunks * 8);
+      const int col = wg_c0 * kChunkK + j * 32;
+      u32x4 v[4] = {};
+      if (col < p.d_in) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.d_in + col + 8 * k);
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          amax = fmaxf(amax, fabsf(__uint_as_float(v[k][d] << 16)));
+          amax = fmaxf(amax, fabsf(__uint_as_float(v[k][d] & 0xffff0000u)));
+        }
+      int e = 0;
+      if (amax > 0.0f) {
+        int ex;
+        const float mant = frexpf(amax, &ex);  // amax = mant 2^ex, mant in [0.5, 1)
+        e = mant <= 0.875f ? ex - 9 : ex - 8;  // the smallest e with amax / 2^e <= 448 = 0.875 2^9
+        e = min(max(e, -127), 127);
+      }
+      uint32_t out[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float x = __uint_as_float(h ? (v[k][d] & 0xffff0000u) : (v[k][d] << 16));
+            const uint32_t c = e4m3_rne_pos(__builtin_amdgcn_ldexpf(fabsf(x), -e));
+            pair |= ((x < 0.0f && c != 0) ? (c | 0x80u) : c) << (8 * h);
+          }
+          // columns 8k + 2d, 8k + 2d + 1 -> bytes 8k + 2d .. of the block
+          const int byte = 8 * k + 2 * d;
+          out[byte / 4] = (byte % 4 == 0) ? pair : (out[byte / 4] | (pair << 16));
+        }
+      uint8_t* dst = xs + m * cstride + j * 32;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<u32x4*>(dst + 16 * q) = u32x4{out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]};
+      xs[sbase + m * sstride + j] = (uint8_t)(e + 127);
+    }
+    if (threadIdx.x < 8) *reinterpret_cast<u32x4*>(xs + zbase + threadIdx.x * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+
+  const bool aval = cl < M;
+  f32x4 acc[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto consume = [&](MFrag<FP4G_MXFP4>& f, int it) {
+    const int cc = c0 + it / 2 - wg_c0;  // chunk within the staged range
+    const int h = it & 1;                // half: K window 128 h .. of the chunk
+    // A: the lane's vector's codes (K 16 kg .. and 64 + 16 kg ..) and block scale
+    const int abase = aval ? cl * cstride + cc * 256 + h * 128 : zbase;
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + abase + 16 * kg);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + abase + 64 + 16 * kg);
+    const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const int sa = aval ? (int)xs[sbase + cl * sstride + cc * 8 + h * 4 + kg] : 127;
+    // B: slot kg of rows 16 r + cl (transpose of the four slots, one dword at a time)
+    u32x4 t[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      t[d] = u32x4{f.q[0][d], f.q[1][d], f.q[2][d], f.q[3][d]};
+      transpose_slot(t[d]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const i32x8 bv = {(int)t[0][r], (int)t[1][r], (int)t[2][r], (int)t[3][r], 0, 0, 0, 0};
+      const int sb = (int)((f.s[r][0] >> (8 * kg)) & 0xffu);  // block 4 h + kg of row 16 r + cl
+      acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[r], 0, 4, 0, sa, 0, sb);
+    }
+  };
+
+  if (n_items > 0) {
+    int it = 0;
+    for (; it + 2 < n_items; it += 2) {
+      load_mfrag<FP4G_MXFP4>(fb, item_tile(it + 1), 1, lane);
+      consume(fa, it);
+      load_mfrag<FP4G_MXFP4>(fa, item_tile(it + 2), 0, lane);
+      consume(fb, it + 1);
+    }
+    if (it + 1 < n_items) {
+      load_mfrag<FP4G_MXFP4>(fb, item_tile(it + 1), 1, lane);
+      consume(fa, it);
+      consume(fb, it + 1);
+    } else {
+      consume(fa, it);
+    }
+  }
+
+  __syncthreads();  // every wave is past its last read of the staging area
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][r * 4 + v][lane] = acc[r][v];
+  __syncthreads();
+  if (wave != 0) return;
+  float val[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) val[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
+
+  constexpr int NU = 8;  // (vector 4 kg + 2 w, + 1) of row block r: unit 2 r + w
+  float ua[NU], ub[NU];
+  bool live[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    ua[u] = val[2 * u];
+    ub[u] = val[2 * u + 1];
+    live[u] = 4 * kg + 2 * (u & 1) < M;
+  }
+  exchange_tree<NU>(p.slots, (int64_t)p.gbase[p.n] * 64, (int64_t)gt * 64 + lane, p.S, s, ua, ub, live);
+  const int d_out = p.d_out[mem];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    if (!live[u]) continue;
+    const int r = u / 2, w = u % 2;
+    const int m = 4 * kg + 2 * w, row = g * 64 + 16 * r + cl;
+    if (row < d_out) {
+      float* y = p.y[mem] + row;
+      if (m < M) y[(int64_t)m * d_out] = ua[u] * p.tscale[mem];
+      if (m + 1 < M) y[(int64_t)(m + 1) * d_out] = ub[u] * p.tscale[mem];
+    }
+  }
+}
+
+inline hipError_t launch_a8(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM)                                        \
+  case MM:                                                   \
+    k_gemv_a8<MM><<<grid, kThreads, lds, s>>>(p);            \
+    break;
+    FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4g

@@ -17,15 +17,6 @@
 namespace fp4g {
 namespace {
 
-// E4M3FN code of t >= 0 (finite), round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_rne_pos(float t) {
-  if (t >= 448.0f) return 126u;
-  if (t < 0.015625f) return (uint32_t)rintf(t * 512.0f);  // m x 2^-9; m = 8 is code 8 = 2^-6
-  const int E = (int)((__float_as_uint(t) >> 23) & 0xffu) - 127;  // floor(log2 t), t normal
-  const float m = rintf((__builtin_amdgcn_ldexpf(t, -E) - 1.0f) * 8.0f);  // exact up to the rounding
-  return (uint32_t)(((E + 7) << 3) + (int)m);  // m = 8 carries into the exponent
-}
-
 // E4M3FN code (0..126) to its value.
 __device__ __forceinline__ float e4m3_val(uint32_t c) {
   const int e = (int)(c >> 3), m = (int)(c & 7u);

@@ -86,8 +86,14 @@ typedef enum { FP4G_NVFP4 = 1, FP4G_MXFP4 = 2, FP4G_FP8_ROW = 3 } fp4g_format;
  * to 16 (FP4G_MAX_M_WIDE: a verify block of up to 15 drafts, feed section "More
  * tokens per weight read"); VALU with more than 8 is FP4G_E_PATH.  FP8 rows have
  * only the VALU kernel: MFMA is refused there with FP4G_E_PATH.  Both paths give
- * the same results up to the order of the FP32 additions. */
-typedef enum { FP4G_PATH_AUTO = 0, FP4G_PATH_VALU = 1, FP4G_PATH_MFMA = 2 } fp4g_path;
+ * the same results up to the order of the FP32 additions.
+ * A8 (W4A8; fp4_skinny_gemm and fp4_gemv_grouped on MXFP4 weights only, M in
+ * 1..16, else FP4G_E_PATH): the input is first quantised per vector and 32
+ * columns to E4M3 with an E8M0 scale, the smallest 2^e with amax / 2^e <= 448,
+ * round to nearest even (the Ling-3.0 article measures MXFP4 experts with 8-bit
+ * activations, sec. 5-6); the product of those activations is then exact up
+ * to the order of the FP32 additions (scaled FP4 x FP8 matrix cores). */
+typedef enum { FP4G_PATH_AUTO = 0, FP4G_PATH_VALU = 1, FP4G_PATH_MFMA = 2, FP4G_PATH_A8 = 3 } fp4g_path;
 
 /* Operation ids for fp4g_workspace_bytes. */
 typedef enum {

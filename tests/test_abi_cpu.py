@@ -109,6 +109,7 @@ def test_skinny_and_lmhead_error_paths():
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 16, Y, fg.PATH_VALU, None, 0, None) == E_PATH
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, 7, None, 0, None) == E_PATH
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, -1, None, 0, None) == E_PATH
+    assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, fg.PATH_A8, None, 0, None) == E_PATH  # A8: MXFP4 only
     assert L.fp8_lmhead_gemv(ctypes.byref(d), X, 1, Y, None, 0, None) == E_FORMAT  # NVFP4 given
     f8 = good_desc(fmt=fg.FP8_ROW)
     assert L.fp8_lmhead_gemv(ctypes.byref(f8), X, 9, Y, None, 0, None) == E_SHAPE

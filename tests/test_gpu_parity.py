@@ -739,3 +739,62 @@ def test_router_gemv_feeds_moe(M):
     layer, expert, sh = build_moe(fg.MXFP4, datagen.MOE_EXPERTS, datagen.MOE_TOPK, datagen.MOE_HIDDEN,
                                   datagen.MOE_FF, seed=311)
     check_moe(layer, expert, sh, X, logits, datagen.MOE_TOPK)
+
+
+# ---- W4A8: MXFP4 weights x MXFP8 activations on the scaled matrix cores ------------------------
+from oracle import w4a8 as oracle_a8  # noqa: E402
+
+
+def check_a8(Y, host, X_bits, rows=None):
+    Yr, A = oracle_a8.gemv(fg.MXFP4, host["codes"], host["scales"], host["tensor_scale"], X_bits)
+    y = Y.detach().cpu().double().numpy().reshape(Yr.shape[0], -1)
+    if rows is not None:
+        y, Yr, A = y[:, rows], Yr[:, rows], A[:, rows]
+    bad = np.abs(y - Yr) > TOL * A
+    assert not bad.any(), f"{bad.sum()} outputs out of bound"
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+def test_a8_matches_w4a8_oracle(M):
+    """The input quantised to MXFP8 inside the kernel, then the exact product:
+    within the product bound of the W4A8 oracle (ragged shapes, tails)."""
+    log("a8", M)
+    for shape in ((200, 1056), (70, 288), (96, 5120)):
+        W, host = make(fg.MXFP4, *shape, seed=60)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("a8X", M, shape), device=DEV)
+        X[0, :32] = 0.0           # an all-zero block
+        X[-1, 32:64] *= 1e-6      # tiny values (E4M3 subnormals of their block)
+        check_a8(fg.fp4_skinny_gemm(W, X, path=fg.PATH_A8), host, bits(X))
+
+
+def test_a8_exact_sums():
+    """Power-of-two weight scales and x in {-1, 0, 1}: the activations quantise
+    without loss and every partial sum is representable, so the W4A8 product
+    equals the oracle bit for bit, and repeats bit for bit."""
+    log("a8 exact")
+    for shape in ((130, 1056), (64, 5120)):
+        gen = torch.Generator(DEV).manual_seed(shape[0] + 77)
+        mat = datagen.matrix(fg.MXFP4, *shape, datagen.tensor_seed("a8exact", shape), device=DEV)
+        sc = exact_scales(fg.MXFP4, shape, gen)
+        W = fg.pack(fg.MXFP4, mat["codes"], sc)
+        for M in (1, 5, 16):
+            X = torch.randint(-1, 2, (M, shape[1]), generator=gen, device=DEV).to(torch.bfloat16)
+            Yr, _ = oracle_a8.gemv(fg.MXFP4, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
+            got = fg.fp4_skinny_gemm(W, X, path=fg.PATH_A8).clone()
+            assert np.array_equal(got.cpu().double().numpy(), Yr), (shape, M)
+            assert torch.equal(fg.fp4_skinny_gemm(W, X, path=fg.PATH_A8), got)
+
+
+def test_a8_grouped_and_refusals():
+    log("a8 grouped")
+    shapes = [(70, 1056), (1, 1056), (200, 1056)]
+    mats = [make(fg.MXFP4, o, i, seed=("a8g", j)) for j, (o, i) in enumerate(shapes)]
+    X = datagen.bf16_normal((4, 1056), datagen.tensor_seed("a8gX"), device=DEV)
+    for (W, host), Y in zip(mats, fg.fp4_gemv_grouped(fg.Group([W for W, _ in mats]), X, path=fg.PATH_A8)):
+        check_a8(Y, host, bits(X))
+    Wn, _ = make(fg.NVFP4, 64, 256, seed=61)
+    with pytest.raises(fg.Fp4gError):
+        fg.fp4_skinny_gemm(Wn, datagen.bf16_normal((2, 256), 1, device=DEV), path=fg.PATH_A8)
+    Wg, _ = make(fg.MXFP4, 64, 256, seed=62)
+    with pytest.raises(fg.Fp4gError):
+        fg.fp4_gate_up_silu(Wg, Wg, datagen.bf16_normal((2, 256), 1, device=DEV), path=fg.PATH_A8)
