@@ -94,13 +94,13 @@ __global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
       for (int k = 0; k < 4; ++k)
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          uint32_t pair = 0;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float x = __uint_as_float(h ? (v[k][d] & 0xffff0000u) : (v[k][d] << 16));
-            const uint32_t c = e4m3_rne_pos(__builtin_amdgcn_ldexpf(fabsf(x), -e));
-            pair |= ((x < 0.0f && c != 0) ? (c | 0x80u) : c) << (8 * h);
-          }
+          // x / 2^e is exact (a bf16 value scaled by a power of two) and at most
+          // 448 in magnitude; the hardware conversion rounds it to nearest even
+          // like the element rule above (a negative value that rounds to zero
+          // gives the -0 code, a zero product on the matrix cores).
+          const float x0 = __builtin_amdgcn_ldexpf(__uint_as_float(v[k][d] << 16), -e);
+          const float x1 = __builtin_amdgcn_ldexpf(__uint_as_float(v[k][d] & 0xffff0000u), -e);
+          const uint32_t pair = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xffffu;
           // columns 8k + 2d, 8k + 2d + 1 -> bytes 8k + 2d .. of the block
           const int byte = 8 * k + 2 * d;
           out[byte / 4] = (byte % 4 == 0) ? pair : (out[byte / 4] | (pair << 16));

@@ -92,7 +92,8 @@ typedef enum { FP4G_NVFP4 = 1, FP4G_MXFP4 = 2, FP4G_FP8_ROW = 3 } fp4g_format;
  * columns to E4M3 with an E8M0 scale, the smallest 2^e with amax / 2^e <= 448,
  * round to nearest even (the Ling-3.0 article measures MXFP4 experts with 8-bit
  * activations, sec. 5-6); the product of those activations is then exact up
- * to the order of the FP32 additions (scaled FP4 x FP8 matrix cores). */
+ * to the order of the FP32 additions (scaled FP4 x FP8 matrix cores).  x must
+ * be finite on this path. */
 typedef enum { FP4G_PATH_AUTO = 0, FP4G_PATH_VALU = 1, FP4G_PATH_MFMA = 2, FP4G_PATH_A8 = 3 } fp4g_path;
 
 /* Operation ids for fp4g_workspace_bytes. */
