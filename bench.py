@@ -77,7 +77,7 @@ def parse():
                     choices=["c1", "c2", "c3", "c3m", "c4", "c5", "head", "skinny", "copy"],
                     help="c3m: the dense stream in the checkpoint's mixed NVFP4/FP8 layout; skinny: one "
                          "17408x5120 product at M vectors (--fmt, --path)")
-    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"], help="weight format of the skinny workload")
+    ap.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"], help="weight format of the skinny, c2 and c4 workloads")
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
     ap.add_argument("--router", action="store_true",
                     help="c5: compute each layer's router logits with an FP8 512x2560 product of x")
@@ -309,7 +309,8 @@ def build_other(name, M, fg, datagen, torch, path=0, router=False, fmt=None):
         keep += [x, y]
         return step, keep, f"single NVFP4 GEMV 5120x5120, M=1 ({R} weight copies rotated)", "gemv"
     if name in ("c2", "c4"):
-        nb = 3 * fg.packed_bytes(fg.NVFP4, F, H)
+        fmt = fmt or fg.NVFP4
+        nb = 3 * fg.packed_bytes(fmt, F, H)
         R = copies_for(nb)
         step = Step(R)
         X = datagen.bf16_normal((M, H), datagen.tensor_seed(name, "x", M), device=dev)
@@ -319,19 +320,20 @@ def build_other(name, M, fg, datagen, torch, path=0, router=False, fmt=None):
         for r in range(R):
             ws = []
             for nm, (o, i) in (("gate", (F, H)), ("up", (F, H)), ("down", (H, F))):
-                m = datagen.matrix(fg.NVFP4, o, i, datagen.tensor_seed(name, r, nm), device=dev)
-                ws.append(fg.pack(fg.NVFP4, m["codes"], m["scales"]))
+                m = datagen.matrix(fmt, o, i, datagen.tensor_seed(name, r, nm), device=dev)
+                ws.append(fg.pack(fmt, m["codes"], m["scales"]))
             keep += ws
             Wg, Wu, Wd = ws
             step.add("gate_up_silu", (lambda Wg=Wg, Wu=Wu: fg.fp4_gate_up_silu(Wg, Wu, X, h, path=path)),
-                     2 * fg.packed_bytes(fg.NVFP4, F, H) + M * H * 2 + M * F * 2)
+                     2 * fg.packed_bytes(fmt, F, H) + M * H * 2 + M * F * 2)
             if M == 1 and path == fg.PATH_AUTO:
                 fn = (lambda Wd=Wd: fg.fp4_gemv(Wd, h.view(-1), y.view(-1)))
             else:
                 fn = (lambda Wd=Wd: fg.fp4_skinny_gemm(Wd, h, y, path=path))
-            step.add("down", fn, algorithmic_gemv_bytes(fg, fg.NVFP4, H, F, M))
+            step.add("down", fn, algorithmic_gemv_bytes(fg, fmt, H, F, M))
         what = "dense MLP" if name == "c2" else "speculative-verify MLP"
-        return step, keep, f"{what}, NVFP4 gate/up 17408x5120 + SiLU*mul, down 5120x17408, M={M} ({R} copies rotated)", \
+        name_f = "NVFP4" if fmt == fg.NVFP4 else "MXFP4"
+        return step, keep, f"{what}, {name_f} gate/up 17408x5120 + SiLU*mul, down 5120x17408, M={M} ({R} copies rotated)", \
             "gate_up_silu"
     if name == "head":
         # the dense model's FP8 head: plain logits, fused greedy pick, and a draft

@@ -361,7 +361,8 @@ def fp4_gemv_grouped(G: Group, X: torch.Tensor, Ys=None, path: int = PATH_AUTO, 
 def fp4_gate_up_silu(Wg: PackedWeight, Wu: PackedWeight, X: torch.Tensor, H: torch.Tensor | None = None,
                      path: int = PATH_AUTO, ws=None, stream=None) -> torch.Tensor:
     """H = bf16(SiLU(Wg X) * (Wu X)) for X bf16 [M, d_in] (an NVFP4/MXFP4 pair, or
-    an FP8 row-scaled pair); returns bf16 [M, d_out]."""
+    an FP8 row-scaled pair); returns bf16 [M, d_out].  PATH_A8 (MXFP4 pairs):
+    both products take X quantised to MXFP8."""
     X2 = X if X.dim() == 2 else X.view(1, -1)
     M = X2.shape[0]
     if H is None:

@@ -14,8 +14,9 @@ extern template hipError_t launch_m<FP4G_MXFP4, 2, EPI_SILU>(int, int, const Gem
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_STORE>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 1, EPI_ARGMAX>(int, int, const GemvParams&, unsigned, hipStream_t);
 extern template hipError_t launch_m<FP4G_FP8_ROW, 2, EPI_SILU>(int, int, const GemvParams&, unsigned, hipStream_t);
-// W4A8 launcher (gemv_a8.hpp), in gemv_a8.hip.
+// W4A8 launchers (gemv_a8.hpp), in gemv_a8.hip: plain products and gate/up.
 hipError_t launch_a8_ext(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s);
+hipError_t launch_a8_silu_ext(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s);
 // Matrix-core launchers (gemv_mfma.hpp), in gemv_mfma_nvfp4.hip and gemv_mfma_mxfp4.hip.
 extern template hipError_t launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(int, const GemvParams&, unsigned, size_t, hipStream_t);
 extern template hipError_t launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(int, const GemvParams&, unsigned, size_t, hipStream_t);
@@ -118,7 +119,7 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (a8)
-    e = launch_a8_ext(M, p, grid, a8_lds_bytes(pl, M), s);
+    e = launch_a8_ext(M, p, grid, a8_lds_bytes(pl, M, 1), s);
   else if (mfma)
     e = W[0]->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, W[0]->format, 1, M), s)
                                    : launch_mfma<FP4G_MXFP4, 1, EPI_STORE>(M, p, grid, mfma_lds_bytes(pl, W[0]->format, 1, M), s);
@@ -258,9 +259,11 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   if (Wg->d_out != Wu->d_out || Wg->d_in != Wu->d_in) return FP4G_E_SHAPE;
   if (!X || !H) return FP4G_E_NULL;
   if (M < 1 || M > (fp4 ? kMaxMWide : kMaxM)) return FP4G_E_SHAPE;
-  if (!valid_path(path, fp4, M) || path == FP4G_PATH_A8) return FP4G_E_PATH;
+  if (!valid_path(path, fp4, M)) return FP4G_E_PATH;
+  const bool a8 = path == FP4G_PATH_A8;  // W4A8: MXFP4 weights only
+  if (a8 && Wg->format != FP4G_MXFP4) return FP4G_E_PATH;
   if (!aligned(X, 16) || !aligned(H, 16)) return FP4G_E_ALIGN;
-  const bool mfma = use_mfma(path, Wg->format, M);
+  const bool mfma = a8 || use_mfma(path, Wg->format, M);
   const int64_t R = row_groups(Wg->d_out), C = chunks(Wg->d_in);
   const uint64_t need = gemv_ws_bytes_any(R, C, 2, M);
   st = check_ws(ws, ws_bytes, need);
@@ -295,7 +298,9 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   const unsigned grid = (unsigned)(R * pl.S);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (mfma)
+  if (a8)
+    e = launch_a8_silu_ext(M, p, grid, a8_lds_bytes(pl, M, 2), s);
+  else if (mfma)
     e = Wg->format == FP4G_NVFP4 ? launch_mfma<FP4G_NVFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, Wg->format, 2, M), s)
                                  : launch_mfma<FP4G_MXFP4, 2, EPI_SILU>(M, p, grid, mfma_lds_bytes(pl, Wg->format, 2, M), s);
   else if (Wg->format == FP4G_NVFP4)

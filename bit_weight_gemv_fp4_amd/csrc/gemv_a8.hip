@@ -3,6 +3,9 @@
 
 namespace fp4g {
 hipError_t launch_a8_ext(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s) {
-  return launch_a8(M, p, grid, lds, s);
+  return launch_a8<1, EPI_STORE>(M, p, grid, lds, s);
+}
+hipError_t launch_a8_silu_ext(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s) {
+  return launch_a8<2, EPI_SILU>(M, p, grid, lds, s);
 }
 }  // namespace fp4g

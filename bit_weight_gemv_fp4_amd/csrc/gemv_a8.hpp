@@ -17,7 +17,9 @@
 //    block i / 16 of its row or column.
 //  * One MFMA per 16-row block and half tile (4 slots = K 128), accumulating in
 //    place: no conversion and no scale arithmetic on the VALU.
-// The split-K tree and the epilogue are those of the other kernels.
+//  * Gate and up (NMAT = 2, the fused SiLU epilogue): one staging serves both
+//    matrices; the items alternate matrices as in the bf16 matrix-core kernel.
+// The split-K tree and the epilogues are those of the other kernels.
 #pragma once
 #include "gemv_mfma.hpp"
 
@@ -27,15 +29,17 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // LDS of a launch: codes + scales of M vectors (rows padded by 64 bytes), then a
 // zero area of one window, or the reduction buffer where that is larger.
-inline size_t a8_lds_bytes(const Plan& pl, int M) {
+inline size_t a8_lds_bytes(const Plan& pl, int M, int nmat) {
   const size_t staged = (size_t)M * (pl.wg_chunks * 264 + kXPad) + kZeroBytes;
-  const size_t red = (size_t)kWavesPerWg * 16 * 64 * 4;
+  const size_t red = (size_t)kWavesPerWg * 16 * nmat * 64 * 4;
   return staged > red ? staged : red;
 }
 
-template <int M>
+template <int M, int NMAT, int EPI>
 __global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
-  constexpr int NV = 16;  // values per lane at the end: rows 16 r + cl, vectors 4 kg + v
+  static_assert((NMAT == 1 && EPI == EPI_STORE) || (NMAT == 2 && EPI == EPI_SILU), "A8: plain or gate/up");
+  // values per lane at the end: matrix a, rows 16 r + cl, vectors 4 kg + v
+  constexpr int NV = 16 * NMAT;
   constexpr int TILE = kTileMx;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
   float(*red)[NV][64] = reinterpret_cast<float(*)[NV][64]>(xs);  // after the products
@@ -47,6 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
   const int mem = member_of(p, gt);
   const int g = gt - p.gbase[mem];
   const uint8_t* w0 = p.w[mem];
+  const uint8_t* w1 = p.w[NMAT - 1];  // up (NMAT = 2; the group has one member)
   const int wg_c0 = s * p.wg_chunks;
   const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
   const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
@@ -54,9 +59,11 @@ __global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
   const int c1 = min(wg_c1, c0 + per_wave);
   const int cl = lane & 15, kg = lane >> 4;
   const int64_t tile0 = (int64_t)g * p.C;
-  auto item_tile = [&](int it) { return w0 + (tile0 + c0 + it / 2) * TILE; };
+  // items (chunk, half, matrix), matrix fastest
+  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / (2 * NMAT)) * TILE; };
+  auto item_half = [&](int it) { return (it / NMAT) & 1; };
 
-  const int n_items = (c1 - c0) * 2;  // half tiles
+  const int n_items = (c1 - c0) * 2 * NMAT;
   MFrag<FP4G_MXFP4> fa, fb;
   if (n_items > 0) load_mfrag<FP4G_MXFP4>(fa, item_tile(0), 0, lane);
 
@@ -116,13 +123,15 @@ __global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
   __syncthreads();
 
   const bool aval = cl < M;
-  f32x4 acc[4];
+  f32x4 acc[NMAT][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int a = 0; a < NMAT; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[a][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto consume = [&](MFrag<FP4G_MXFP4>& f, int it) {
-    const int cc = c0 + it / 2 - wg_c0;  // chunk within the staged range
-    const int h = it & 1;                // half: K window 128 h .. of the chunk
+  auto consume = [&](MFrag<FP4G_MXFP4>& f, int it, f32x4(&ac)[4]) {
+    const int cc = c0 + it / (2 * NMAT) - wg_c0;  // chunk within the staged range
+    const int h = item_half(it);                  // half: K window 128 h .. of the chunk
     // A: the lane's vector's codes (K 16 kg .. and 64 + 16 kg ..) and block scale
     const int abase = aval ? cl * cstride + cc * 256 + h * 128 : zbase;
     const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + abase + 16 * kg);
@@ -140,67 +149,85 @@ __global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
     for (int r = 0; r < 4; ++r) {
       const i32x8 bv = {(int)t[0][r], (int)t[1][r], (int)t[2][r], (int)t[3][r], 0, 0, 0, 0};
       const int sb = (int)((f.s[r][0] >> (8 * kg)) & 0xffu);  // block 4 h + kg of row 16 r + cl
-      acc[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[r], 0, 4, 0, sa, 0, sb);
+      ac[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, ac[r], 0, 4, 0, sa, 0, sb);
     }
   };
 
+  // fa holds even items and fb odd ones: with NMAT = 2 gate and up
   if (n_items > 0) {
     int it = 0;
     for (; it + 2 < n_items; it += 2) {
-      load_mfrag<FP4G_MXFP4>(fb, item_tile(it + 1), 1, lane);
-      consume(fa, it);
-      load_mfrag<FP4G_MXFP4>(fa, item_tile(it + 2), 0, lane);
-      consume(fb, it + 1);
+      load_mfrag<FP4G_MXFP4>(fb, item_tile(it + 1), item_half(it + 1), lane);
+      consume(fa, it, acc[0]);
+      load_mfrag<FP4G_MXFP4>(fa, item_tile(it + 2), item_half(it + 2), lane);
+      consume(fb, it + 1, acc[NMAT - 1]);
     }
     if (it + 1 < n_items) {
-      load_mfrag<FP4G_MXFP4>(fb, item_tile(it + 1), 1, lane);
-      consume(fa, it);
-      consume(fb, it + 1);
+      load_mfrag<FP4G_MXFP4>(fb, item_tile(it + 1), item_half(it + 1), lane);
+      consume(fa, it, acc[0]);
+      consume(fb, it + 1, acc[NMAT - 1]);
     } else {
-      consume(fa, it);
+      consume(fa, it, acc[0]);
     }
   }
 
   __syncthreads();  // every wave is past its last read of the staging area
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int a = 0; a < NMAT; ++a)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][r * 4 + v][lane] = acc[r][v];
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][(a * 4 + r) * 4 + v][lane] = acc[a][r][v];
   __syncthreads();
   if (wave != 0) return;
   float val[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) val[i] = ((red[0][i][lane] + red[1][i][lane]) + red[2][i][lane]) + red[3][i][lane];
 
-  constexpr int NU = 8;  // (vector 4 kg + 2 w, + 1) of row block r: unit 2 r + w
+  // units: EPI_SILU (gate, up) of (row block r, vector 4 kg + v), unit 4 r + v;
+  // EPI_STORE vectors (4 kg + 2 w, + 1) of row block r, unit 2 r + w
+  constexpr int NU = EPI == EPI_SILU ? 16 : 8;
   float ua[NU], ub[NU];
   bool live[NU];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
-    ua[u] = val[2 * u];
-    ub[u] = val[2 * u + 1];
-    live[u] = 4 * kg + 2 * (u & 1) < M;
+    if constexpr (EPI == EPI_SILU) {
+      ua[u] = val[u];
+      ub[u] = val[16 + u];
+      live[u] = 4 * kg + (u & 3) < M;
+    } else {
+      ua[u] = val[2 * u];
+      ub[u] = val[2 * u + 1];
+      live[u] = 4 * kg + 2 * (u & 1) < M;
+    }
   }
   exchange_tree<NU>(p.slots, (int64_t)p.gbase[p.n] * 64, (int64_t)gt * 64 + lane, p.S, s, ua, ub, live);
   const int d_out = p.d_out[mem];
 #pragma unroll
   for (int u = 0; u < NU; ++u) {
     if (!live[u]) continue;
-    const int r = u / 2, w = u % 2;
-    const int m = 4 * kg + 2 * w, row = g * 64 + 16 * r + cl;
-    if (row < d_out) {
-      float* y = p.y[mem] + row;
-      if (m < M) y[(int64_t)m * d_out] = ua[u] * p.tscale[mem];
-      if (m + 1 < M) y[(int64_t)(m + 1) * d_out] = ub[u] * p.tscale[mem];
+    if constexpr (EPI == EPI_SILU) {
+      const int r = u / 4, m = 4 * kg + (u & 3), row = g * 64 + 16 * r + cl;
+      if (m < M && row < d_out)
+        p.h[(int64_t)m * d_out + row] = f32_to_bf16_rne(silu_f32(ua[u] * p.tscale[0]) * (ub[u] * p.tscale[1]));
+    } else {
+      const int r = u / 2, w = u % 2;
+      const int m = 4 * kg + 2 * w, row = g * 64 + 16 * r + cl;
+      if (row < d_out) {
+        float* y = p.y[mem] + row;
+        if (m < M) y[(int64_t)m * d_out] = ua[u] * p.tscale[mem];
+        if (m + 1 < M) y[(int64_t)(m + 1) * d_out] = ub[u] * p.tscale[mem];
+      }
     }
   }
 }
 
-inline hipError_t launch_a8(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s) {
+template <int NMAT, int EPI>
+hipError_t launch_a8(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s) {
   switch (M) {
 #define FP4G_CASE(MM)                                        \
   case MM:                                                   \
-    k_gemv_a8<MM><<<grid, kThreads, lds, s>>>(p);            \
+    k_gemv_a8<MM, NMAT, EPI><<<grid, kThreads, lds, s>>>(p); \
     break;
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
     FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)

@@ -87,13 +87,13 @@ typedef enum { FP4G_NVFP4 = 1, FP4G_MXFP4 = 2, FP4G_FP8_ROW = 3 } fp4g_format;
  * tokens per weight read"); VALU with more than 8 is FP4G_E_PATH.  FP8 rows have
  * only the VALU kernel: MFMA is refused there with FP4G_E_PATH.  Both paths give
  * the same results up to the order of the FP32 additions.
- * A8 (W4A8; fp4_skinny_gemm and fp4_gemv_grouped on MXFP4 weights only, M in
- * 1..16, else FP4G_E_PATH): the input is first quantised per vector and 32
- * columns to E4M3 with an E8M0 scale, the smallest 2^e with amax / 2^e <= 448,
- * round to nearest even (the Ling-3.0 article measures MXFP4 experts with 8-bit
- * activations, sec. 5-6); the product of those activations is then exact up
- * to the order of the FP32 additions (scaled FP4 x FP8 matrix cores).  x must
- * be finite on this path. */
+ * A8 (W4A8; fp4_skinny_gemm, fp4_gemv_grouped and fp4_gate_up_silu on MXFP4
+ * weights only, M in 1..16, else FP4G_E_PATH): the input is first quantised per
+ * vector and 32 columns to E4M3 with an E8M0 scale, the smallest 2^e with
+ * amax / 2^e <= 448, round to nearest even (the Ling-3.0 article measures MXFP4
+ * experts with 8-bit activations, sec. 5-6); the product of those activations
+ * is then exact up to the order of the FP32 additions (scaled FP4 x FP8 matrix
+ * cores).  x must be finite on this path. */
 typedef enum { FP4G_PATH_AUTO = 0, FP4G_PATH_VALU = 1, FP4G_PATH_MFMA = 2, FP4G_PATH_A8 = 3 } fp4g_path;
 
 /* Operation ids for fp4g_workspace_bytes. */
@@ -276,7 +276,9 @@ int32_t fp4_gemv_grouped(const fp4g_group* G_host, const uint16_t* X_dev, int32_
  * gate and up projections are 17408 x 5120 in the dense model), or two FP8_ROW
  * matrices, each with its own row scales (the FP8 MLPs of the last layers in the
  * feed's mixed checkpoint, section "Fewer bytes per weight: NVFP4"; VALU path,
- * M in 1..8).  X_dev: bf16 [M][hidden]; H_dev: bf16 [M][d_ff]. */
+ * M in 1..8).  With FP4G_PATH_A8 (MXFP4 pairs) g and u are the W4A8 products of
+ * the input quantised once for both.  X_dev: bf16 [M][hidden]; H_dev: bf16
+ * [M][d_ff]. */
 int32_t fp4_gate_up_silu(const fp4g_weight* Wg_host, const fp4g_weight* Wu_host,
                          const uint16_t* X_dev, int32_t M, uint16_t* H_dev, int32_t path,
                          void* ws_dev, uint64_t ws_bytes, void* stream);

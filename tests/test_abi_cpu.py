@@ -217,13 +217,14 @@ def test_gate_up_error_paths():
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u2), X, 1, H, 0, None, 0, None) == E_SHAPE
     u3 = good_desc(fmt=fg.MXFP4)
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u3), X, 1, H, 0, None, 0, None) == E_FORMAT
-    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, 3, None, 0, None) == E_PATH
+    assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 1, H, fg.PATH_A8, None, 0, None) == E_PATH  # A8: MXFP4 only
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 17, H, 0, None, 0, None) == E_SHAPE
     assert L.fp4_gate_up_silu(ctypes.byref(g), ctypes.byref(u), X, 9, H, fg.PATH_VALU, None, 0, None) == E_PATH
     # FP8 row pairs (a mixed layout's FP8 MLPs): VALU only, up to 8 vectors, one format per pair
     g8, u8 = good_desc(fg.FP8_ROW), good_desc(fg.FP8_ROW); u8.packed = FAKE + (8 << 30)
     assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u), X, 1, H, 0, None, 0, None) == E_FORMAT
     assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u8), X, 1, H, fg.PATH_MFMA, None, 0, None) == E_PATH
+    assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u8), X, 1, H, fg.PATH_A8, None, 0, None) == E_PATH
     assert L.fp4_gate_up_silu(ctypes.byref(g8), ctypes.byref(u8), X, 9, H, 0, None, 0, None) == E_SHAPE
     big8 = good_desc(fg.FP8_ROW, 17408, 5120)
     assert fg.workspace_bytes(fg.OP_GATE_UP, big8, 8) > 0 and fg.workspace_bytes(fg.OP_GATE_UP, big8, 9) == 0

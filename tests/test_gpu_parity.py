@@ -763,7 +763,10 @@ def test_a8_matches_w4a8_oracle(M):
         W, host = make(fg.MXFP4, *shape, seed=60)
         X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("a8X", M, shape), device=DEV)
         X[0, :32] = 0.0           # an all-zero block
-        X[-1, 32:64] *= 1e-6      # tiny values (E4M3 subnormals of their block)
+        X[-1, 32:64] *= 1e-6      # tiny values (the block's scale follows them)
+        X[0, 64] = 100.0          # block scale 2^-2: below it E4M3 subnormals and,
+        X[0, 65:80] = -1e-3       # under half the smallest step, negatives that
+        X[0, 80:96] = -1e-5       # round to zero (the -0 code on the device)
         check_a8(fg.fp4_skinny_gemm(W, X, path=fg.PATH_A8), host, bits(X))
 
 
@@ -795,6 +798,26 @@ def test_a8_grouped_and_refusals():
     Wn, _ = make(fg.NVFP4, 64, 256, seed=61)
     with pytest.raises(fg.Fp4gError):
         fg.fp4_skinny_gemm(Wn, datagen.bf16_normal((2, 256), 1, device=DEV), path=fg.PATH_A8)
-    Wg, _ = make(fg.MXFP4, 64, 256, seed=62)
     with pytest.raises(fg.Fp4gError):
-        fg.fp4_gate_up_silu(Wg, Wg, datagen.bf16_normal((2, 256), 1, device=DEV), path=fg.PATH_A8)
+        fg.fp4_gate_up_silu(Wn, Wn, datagen.bf16_normal((2, 256), 1, device=DEV), path=fg.PATH_A8)
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+def test_a8_gate_up_silu_matches_oracle(M):
+    """Fused gate/up on the W4A8 path: both products of the once-quantised
+    input, then bf16(SiLU(g) u), within the bound of the bf16 path with the W4A8
+    oracle's products and magnitude sums."""
+    log("a8 gate_up", M)
+    for shape in ((200, 1056), (70, 288), (96, 5120)):
+        Wg, hg = make(fg.MXFP4, *shape, seed=("a8gu", 0))
+        Wu, hu = make(fg.MXFP4, *shape, seed=("a8gu", 1))
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("a8guX", M, shape), device=DEV)
+        X[0, 64] = 100.0
+        X[0, 65:96] = -1e-5
+        H = fg.fp4_gate_up_silu(Wg, Wu, X, path=fg.PATH_A8)
+        g, Ag = oracle_a8.gemv(fg.MXFP4, hg["codes"], hg["scales"], hg["tensor_scale"], bits(X))
+        u, Au = oracle_a8.gemv(fg.MXFP4, hu["codes"], hu["scales"], hu["tensor_scale"], bits(X))
+        r = {"h": oracle.silu_mul(g, u), "g": g, "u": u, "Ag": Ag, "Au": Au}
+        h = H.detach().float().cpu().double().numpy().reshape(M, -1)
+        bad = np.abs(h - r["h"]) > h_bound(r, r["h"])
+        assert not bad.any(), f"{bad.sum()} h values out of bound ({shape})"
