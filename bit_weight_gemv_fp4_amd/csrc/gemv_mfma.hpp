@@ -136,8 +136,19 @@ struct MfmaMoe {
   int cd, dff;           // down: chunks per slot; d_ff
 };
 
+// Waves per SIMD the register allocation aims for.  VGPRs and AGPRs share one
+// file of 512 per lane, so four waves leave 128 registers: enough, without
+// spills, for the plain and gate/up forms up to 8 vectors, the plain form up to
+// 16 and the MoE gate/up (measured 5-25% faster than at three waves).  Gate/up
+// above 8 vectors and the MoE down would spill at that budget: no target there.
+template <int M, int NMAT, int MODE>
+constexpr int mfma_waves_per_eu() {
+  return (NMAT == 2 && M > kMaxM) || MODE == 2 ? 1 : 4;
+}
+
 template <uint32_t FMT, int M, int NMAT, int EPI, int MODE = 0>
-__global__ __launch_bounds__(kThreads) void k_gemv_mfma(GemvParams p, MfmaMoe q) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<M, NMAT, MODE>())))
+void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   constexpr bool MOE = MODE == 1, MOED = MODE == 2;
   // NVFP4 with up to 8 vectors: both blocks of a slot in one MFMA (A rows 8..15
   // carry the second block); the outputs of lanes i and i + 32 then add up
