@@ -35,8 +35,9 @@ inline size_t a8_lds_bytes(const Plan& pl, int M, int nmat) {
   return staged > red ? staged : red;
 }
 
+// Four waves per SIMD (128 registers per lane): every form fits without spills.
 template <int M, int NMAT, int EPI>
-__global__ __launch_bounds__(kThreads) void k_gemv_a8(GemvParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_a8(GemvParams p) {
   static_assert((NMAT == 1 && EPI == EPI_STORE) || (NMAT == 2 && EPI == EPI_SILU), "A8: plain or gate/up");
   // values per lane at the end: matrix a, rows 16 r + cl, vectors 4 kg + v
   constexpr int NV = 16 * NMAT;
