@@ -368,12 +368,19 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(GemvParams p) {
     } else {
       tile_dot<FMT, M, false>(f, xc, xstride, tail_pieces, part);
     }
-    if (NMAT == 1 || it % NMAT == 0) {
+    if constexpr (NMAT == 1) {
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[0][m] += part[m];
     } else {
+      // branch-free (item it belongs to matrix it % 2): the compiler merges two
+      // branches into a store through a chosen pointer, which keeps the
+      // accumulators in private memory
+      const bool up = it % NMAT != 0;
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[NMAT - 1][m] += part[m];
+      for (int m = 0; m < M; ++m) {
+        acc[0][m] += up ? 0.0f : part[m];
+        acc[1][m] += up ? part[m] : 0.0f;
+      }
     }
   };
   stream_items<FMT>(n_items, lane, item_tile, consume);

@@ -265,12 +265,11 @@ __global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
       tile_dot<FMT, M, true>(f, xc, xstride, kPiecesNv, part);
     else
       tile_dot<FMT, M, false>(f, xc, xstride, tail_pieces, part);
-    if ((it & 1) == 0) {
+    const bool up = (it & 1) != 0;  // branch-free, as in the dense kernel
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[0][m] += part[m];
-    } else {
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[1][m] += part[m];
+    for (int m = 0; m < M; ++m) {
+      acc[0][m] += up ? 0.0f : part[m];
+      acc[1][m] += up ? part[m] : 0.0f;
     }
   };
   stream_items<FMT>((c1 - c0) * 2, lane, tile_of, eat);
