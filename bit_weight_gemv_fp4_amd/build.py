@@ -44,12 +44,23 @@ def _compile(src: Path, verbose: bool) -> Path:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> Path:
+def _stale(src: Path, newest_header: float) -> bool:
+    obj = BUILD / (src.stem + ".o")
+    return not obj.exists() or obj.stat().st_mtime < max(src.stat().st_mtime, newest_header)
+
+
+def build(verbose: bool = False, jobs: int | None = None, incremental: bool = False) -> Path:
+    """Compile every source (incremental: only those older than their object or
+    than any header of the package) and link the library."""
     BUILD.mkdir(exist_ok=True)
     srcs = sorted(CSRC.glob("*.hip"))
-    jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
+    headers = list(CSRC.glob("*.hpp")) + list((PKG.parent / "include").glob("*.h"))
+    newest = max((h.stat().st_mtime for h in headers), default=0.0)
+    todo = [s for s in srcs if not incremental or _stale(s, newest)]
+    jobs = jobs or min(max(len(todo), 1), max(1, min(16, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    objs = [BUILD / (s.stem + ".o") for s in srcs]
     tmp = LIB.with_suffix(".so.tmp")
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
     if verbose:
@@ -60,4 +71,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> Path:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

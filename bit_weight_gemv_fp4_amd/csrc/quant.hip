@@ -8,8 +8,11 @@
 // block code = E4M3_RNE(amax_b / (6 s_T)); element = E2M1_RNE(w / (s_b s_T)).
 // MXFP4: the smallest power of two 2^e with amax_b / 2^e <= 6 (E8M0 code
 // e + 127); FP8 rows: s_row = amax_row / 448.  Rounding is to nearest, ties to
-// the even code, saturating; zero magnitudes get the positive-zero code.  The
-// scale arithmetic is FP32, one rounding per operation.
+// the even code, saturating; zero magnitudes get the positive-zero code.  s_T
+// and s_row are the FP32 values nearest to their quotients (IEEE division);
+// every code is then the grid value nearest to the EXACT quotient: a first
+// guess from the FP32 quotient (at most one code off) is corrected by the sign
+// of fma(-mid * k, s, a) = a - mid * k * s rounded once, whose sign is exact.
 #include <algorithm>
 
 #include "common.hpp"
@@ -40,6 +43,31 @@ __device__ __forceinline__ uint32_t e2m1_rne(float q) {
 }
 
 __device__ __forceinline__ float bf16_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Midpoint between the magnitudes of codes c and c + 1 (exact in FP32).
+__device__ __forceinline__ float e2m1_mid(uint32_t c) {
+  constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  return kMid[c];
+}
+__device__ __forceinline__ float e4m3_mid(uint32_t c) { return (e4m3_val(c) + e4m3_val(c + 1)) * 0.5f; }
+
+// The code nearest to the exact quotient a / (k s) (a >= 0, k s > 0), given a
+// guess c at most one code away: the sign of a - mid * k * s decides each
+// neighbouring midpoint exactly (mid * k is exact in FP32: at most 5 + 4
+// significant bits; the fma rounds once, which keeps the sign).  At a midpoint
+// the even code wins; cmax saturates.
+template <class Mid>
+__device__ __forceinline__ uint32_t exact_code(uint32_t c, uint32_t cmax, float a, float k, float s, Mid mid) {
+  if (c < cmax) {
+    const float r = __builtin_fmaf(-(mid(c) * k), s, a);
+    if (r > 0.0f || (r == 0.0f && ((c + 1) & 1u) == 0)) return c + 1;
+  }
+  if (c > 0) {
+    const float r = __builtin_fmaf(-(mid(c - 1) * k), s, a);
+    if (r < 0.0f || (r == 0.0f && ((c - 1) & 1u) == 0)) return c - 1;
+  }
+  return c;
+}
 
 // Largest |w| of the tensor as the bit pattern of a non-negative bf16 (ordered
 // like the value), into *amax (zeroed by k_zero_u32 first).
@@ -83,12 +111,15 @@ __global__ __launch_bounds__(256) void k_quant_fp4(const uint16_t* w, int d_out,
   }
   uint32_t el[BLK];
   if constexpr (FMT == FP4G_NVFP4) {
-    const uint32_t sc = e4m3_rne_pos(amax / six_st);
+    const uint32_t sc = exact_code(e4m3_rne_pos(amax / six_st), 126u, amax, 6.0f, s_t, e4m3_mid);
     scales[b] = (uint8_t)sc;
     const float sb = e4m3_val(sc);
     const float den = sb * s_t;
 #pragma unroll
-    for (int k = 0; k < BLK; ++k) el[k] = sb > 0.0f ? e2m1_rne(v[k] / den) : 0u;
+    for (int k = 0; k < BLK; ++k) {
+      const uint32_t c = exact_code(e2m1_rne(fabsf(v[k]) / den), 7u, fabsf(v[k]), sb, s_t, e2m1_mid);
+      el[k] = sb > 0.0f ? ((v[k] < 0.0f && c != 0) ? (c | 8u) : c) : 0u;
+    }
   } else {
     int code = 127;
     if (amax > 0.0f) {
@@ -122,9 +153,9 @@ __global__ __launch_bounds__(256) void k_quant_fp8(const uint16_t* w, int d_out,
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (lane == 0) row_scale[r] = s;
   for (int k = lane; k < d_in; k += 64) {
-    const float q = bf16_f32(src[k]) / s;
-    const uint32_t c = e4m3_rne_pos(fabsf(q));
-    codes[r * d_in + k] = (uint8_t)((q < 0.0f && c != 0) ? (c | 0x80u) : c);
+    const float v = bf16_f32(src[k]);
+    const uint32_t c = exact_code(e4m3_rne_pos(fabsf(v) / s), 126u, fabsf(v), 1.0f, s, e4m3_mid);
+    codes[r * d_in + k] = (uint8_t)((v < 0.0f && c != 0) ? (c | 0x80u) : c);
   }
 }
 

@@ -211,8 +211,10 @@ int32_t fp4g_pack(uint32_t format, int32_t d_out, int32_t d_in, const void* code
  *   FP8_ROW: per row s = amax_row / 448 (1 if all zero) as the FP32 row scale;
  *            element = E4M3(w / s).
  * Rounding: nearest, ties to the even code, saturating (E2M1 at 6, E4M3 at 448);
- * a value that rounds to zero gets the +0 code.  Scale arithmetic in FP32, one
- * rounding per operation in the order written.
+ * a value that rounds to zero gets the +0 code.  s_T and s are the FP32 values
+ * nearest to their quotients; every code is the grid value nearest to the exact
+ * quotient of the bf16 input and the stored FP32 scales (no intermediate
+ * rounding decides a code).
  *   codes_dev   NVFP4/MXFP4: u8[d_out][d_in/2]; FP8_ROW: u8[d_out][d_in].
  *   scales_dev  u8[d_out][d_in/16] (NVFP4), u8[d_out][d_in/32] (MXFP4), f32[d_out].
  *   tensor_scale_dev  NULL or one f32: s_T (NVFP4), 1.0 otherwise.

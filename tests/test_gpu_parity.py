@@ -21,12 +21,11 @@ import torch
 import bit_weight_gemv_fp4_amd as fg
 import datagen
 import oracle
+from gpu_common import (DEV, TOL, bits, build_moe, check_h, check_moe, check_product, h_bound, log, make,
+                        sample_rows)
 from oracle import layout
 
 pytestmark = pytest.mark.gpu
-
-DEV = "cuda"
-TOL = 2e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -36,41 +35,6 @@ def _gpu_and_native_library():
     fg.lib()
     yield
     torch.cuda.synchronize()
-
-
-def log(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def bits(x_bf16: torch.Tensor) -> np.ndarray:
-    return x_bf16.detach().cpu().view(torch.int16).numpy().view(np.uint16)
-
-
-def make(fmt, d_out, d_in, seed):
-    mat = datagen.matrix(fmt, d_out, d_in, datagen.tensor_seed("gpu", fmt, d_out, d_in, seed), device=DEV)
-    W = fg.pack(fmt, mat["codes"], mat["scales"], mat["tensor_scale"])
-    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in mat.items()}
-    return W, host
-
-
-def sample_rows(d_out, n=192, seed=0):
-    rng = np.random.default_rng(seed)
-    fixed = {0, 1, 63, 64, d_out - 1, d_out // 2}
-    rows = sorted(fixed | set(rng.integers(0, d_out, n).tolist()))
-    return np.array([r for r in rows if 0 <= r < d_out], dtype=np.int64)
-
-
-def check_product(y_gpu, host, X_bits, rows=None, tol=TOL):
-    Y, A = oracle.gemv(host["format"], host["codes"], host["scales"], host["tensor_scale"], X_bits, rows=rows)
-    y = y_gpu.detach().cpu().double().numpy().reshape(Y.shape[0], -1)
-    if rows is not None:
-        y = y[:, rows]
-    err = np.abs(y - Y)
-    bound = tol * A
-    bad = err > bound
-    assert not bad.any(), f"{bad.sum()} outputs out of bound; worst ratio {np.max(err / np.maximum(bound, 1e-300)):.3g}"
-    return float(np.max(err / np.maximum(A, 1e-300)))
 
 
 # ---- packing -------------------------------------------------------------------------
@@ -217,22 +181,6 @@ def test_lmhead_argmax_full_vocabulary(M):
     assert np.all(Y[np.arange(M), i] >= Y.max(axis=1) - 2 * TOL * A.max(axis=1))
 
 
-def h_bound(r, h_ref):
-    tg, tu = TOL * r["Ag"], TOL * r["Au"]
-    silu_g = r["g"] / (1.0 + np.exp(-r["g"]))
-    return 1.1 * tg * (np.abs(r["u"]) + tu) + np.abs(silu_g) * tu + 2.0 ** -8 * np.abs(h_ref)
-
-
-def check_h(H_gpu, gate, up, X_bits, rows=None):
-    r = oracle.gate_up_silu(gate, up, X_bits, rows=rows)
-    h = H_gpu.detach().float().cpu().double().numpy().reshape(r["h"].shape[0], -1)
-    if rows is not None:
-        h = h[:, rows]
-    err = np.abs(h - r["h"])
-    bad = err > h_bound(r, r["h"])
-    assert not bad.any(), f"{bad.sum()} h values out of bound"
-
-
 @pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("M", [1, 2, 4, 5, 8])
 @pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
@@ -262,38 +210,108 @@ def quant_inputs(d_out, d_in, seed):
     return w.to(torch.bfloat16)
 
 
+def check_quant_exact(fmt, w_bf16, label):
+    """The kernel's codes, scales and tensor scale against the exact-decision
+    oracle, bit for bit.  The oracle's marks (decisions within 2^-22 of a
+    midpoint, where an FP32-quotient order could differ) are counted and
+    reported: the kernel decides those exactly too, so none may differ."""
+    codes, scales, ts = fg.quantize(fmt, w_bf16.to(DEV))
+    ref = oq.quantize_detail(fmt, w_bf16.cpu().view(torch.int16).numpy().view(np.uint16))
+    n_marked = int(ref["el_amb"].sum()) + int(ref.get("scale_amb", np.zeros(1, bool)).sum())
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    n_diff = int((oq.elements_of(fmt, gc) != ref["el"]).sum())
+    n_diff += int((gs.view(np.uint32) != np.asarray(ref["scales"]).view(np.uint32)).sum()) if fmt == fg.FP8_ROW \
+        else int((gs != ref["scales"]).sum())
+    log(f"quantize {label} fmt={fmt}: {ref['el'].size} elements, {n_marked} decisions near a midpoint, {n_diff} differ")
+    assert np.float32(ts).view(np.uint32) == np.float32(ref["tensor_scale"]).view(np.uint32)
+    assert n_diff == 0
+    assert np.array_equal(gc, ref["codes"])
+    return codes, scales, ts
+
+
 @pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4, fg.FP8_ROW])
 @pytest.mark.parametrize("shape", [(130, 544), (256, 2048)])
-def test_quantize_matches_oracle_bit_exact(fmt, shape):
+def test_quantize_matches_exact_oracle(fmt, shape):
     log("quantize", fmt, shape)
-    w = quant_inputs(*shape, seed=shape[0] + fmt)
-    codes, scales, ts = fg.quantize(fmt, w.to(DEV))
-    rc, rs, rts = oq.quantize(fmt, w.view(torch.int16).numpy().view(np.uint16))
-    assert ts == rts
-    assert np.array_equal(codes.cpu().numpy(), rc)
-    assert np.array_equal(scales.cpu().numpy(), rs)
+    check_quant_exact(fmt, quant_inputs(*shape, seed=shape[0] + fmt), shape)
+
+
+def midpoint_inputs(fmt, seed, d_out=64, d_in=512):
+    """Weights placed exactly on rounding midpoints of the decoded scale (a
+    power-of-two tensor / row scale makes every quotient exact in FP32 too) and
+    one bf16 step either side of them, mixed with normal weights."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((d_out, d_in))
+    mids2 = oq._MID_E2M1
+    mids8 = oq._MID_E4M3
+    if fmt == fg.FP8_ROW:
+        for r in range(d_out):
+            s = 2.0 ** int(rng.integers(-8, 3))
+            w[r, 0] = 448.0 * s
+            k = 1 + np.arange(128)
+            w[r, k] = mids8[rng.integers(0, 125, 128)] * s * np.where(rng.random(128) < .5, -1, 1)
+    else:
+        blk = 16 if fmt == fg.NVFP4 else 32
+        s_t = 2.0 ** -6 if fmt == fg.NVFP4 else 1.0
+        for r in range(d_out):
+            for b in range(d_in // blk):
+                sb = oq._E4M3[int(rng.integers(48, 110))] if fmt == fg.NVFP4 else 2.0 ** int(rng.integers(-8, 8))
+                w[r, blk * b] = 6.0 * sb * s_t
+                k = blk * b + 1 + np.arange(blk // 2)
+                w[r, k] = mids2[rng.integers(0, 7, blk // 2)] * sb * s_t * np.where(rng.random(blk // 2) < .5, -1, 1)
+        if fmt == fg.NVFP4:
+            w[0, 0] = 2688.0 * s_t
+    wt = torch.from_numpy(w.astype(np.float32)).to(torch.bfloat16)
+    # one bf16 step up or down on a quarter of the entries
+    nudge = torch.from_numpy(rng.integers(-1, 2, w.shape).astype(np.int16)) * torch.from_numpy(rng.random(w.shape) < 0.25)
+    bits = (wt.view(torch.int16).to(torch.int32) + nudge.to(torch.int32)).to(torch.int16)
+    bits[0, 0] = wt.view(torch.int16)[0, 0]
+    bits[:, 0] = wt.view(torch.int16)[:, 0]
+    return bits.view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4, fg.FP8_ROW])
+def test_quantize_midpoints_ties_to_even(fmt):
+    """Exact midpoints go to the even code and their bf16 neighbours to the
+    nearer side, bit-exact against the exact oracle."""
+    log("quantize midpoints", fmt)
+    check_quant_exact(fmt, midpoint_inputs(fmt, 20 + fmt), "midpoints")
 
 
 def test_quantize_then_product():
-    """Quantise -> pack -> product: equals the oracle's product of the quantised
-    matrix, and stays near the bf16 matrix's product."""
+    """Quantise -> pack -> product: within the product bound of the oracle's
+    GEMV of the quantised matrix, and within the quantisation error of the bf16
+    matrix's exact product: |y - W x| <= sum_k |x_k| e_k + bound, with e_k the
+    largest rounding error of element k: half the widest E2M1 step (1) times the
+    decoded block scale, or, where the block scale rounded down far enough that
+    the block maximum saturates (a zero or subnormal E4M3 scale), the block
+    maximum's excess over 6 times it; MXFP4 never saturates; for FP8 rows
+    2^-4 |w| + half the smallest E4M3 step times the row scale."""
     log("quantize -> gemv")
     w = quant_inputs(192, 1024, 7).to(DEV)
     x = datagen.bf16_normal((1024,), 8, device=DEV)
-    exact = (w.double() @ x.double()).cpu().numpy()
-    for fmt in (fg.NVFP4, fg.MXFP4):
-        codes, scales, ts = fg.quantize(fmt, w)
+    wd = w.double().cpu().numpy()
+    xd = x.double().cpu().numpy()
+    exact = wd @ xd
+    for fmt in (fg.NVFP4, fg.MXFP4, fg.FP8_ROW):
+        codes, scales, ts = check_quant_exact(fmt, w, "product")
         W = fg.pack(fmt, codes, scales, ts)
-        y = fg.fp4_gemv(W, x)
+        y = (fg.fp8_lmhead_gemv(W, x) if fmt == fg.FP8_ROW else fg.fp4_gemv(W, x)).reshape(-1)
         host = {"format": fmt, "codes": codes.cpu(), "scales": scales.cpu(), "tensor_scale": ts}
         check_product(y, host, bits(x)[None, :])
-        rel = np.linalg.norm(y.cpu().double().numpy() - exact) / np.linalg.norm(exact)
-        assert rel < 0.2, (fmt, rel)
-    codes, scales, _ = fg.quantize(fg.FP8_ROW, w)
-    W = fg.pack(fg.FP8_ROW, codes, scales)
-    y = fg.fp8_lmhead_gemv(W, x)
-    rel = np.linalg.norm(y.cpu().double().numpy().ravel() - exact) / np.linalg.norm(exact)
-    assert rel < 0.05, rel
+        sc = scales.cpu().numpy()
+        if fmt == fg.NVFP4:
+            sb = oq._E4M3[sc] * ts
+            amax_b = np.abs(wd).reshape(wd.shape[0], -1, 16).max(-1)
+            e = np.repeat(np.maximum(sb, amax_b - 6.0 * sb), 16, axis=1)
+        elif fmt == fg.MXFP4:
+            e = np.repeat(np.exp2(sc.astype(np.float64) - 127), 32, axis=1)
+        else:
+            e = 2.0 ** -4 * np.abs(wd) + 2.0 ** -10 * sc.astype(np.float64)[:, None]
+        _, A = oracle.gemv(fmt, codes.cpu(), scales.cpu(), ts, bits(x)[None, :])
+        bound = e @ np.abs(xd) + TOL * A[0]
+        err = np.abs(y.cpu().double().numpy() - exact)
+        assert np.all(err <= bound), (fmt, float(np.max(err / bound)))
 
 
 # ---- special cases: bit-exact ------------------------------------------------------------------
@@ -473,83 +491,6 @@ def test_config3_lm_head():
 
 
 # ---- MoE --------------------------------------------------------------------------------------
-
-
-def build_moe(fmt, E, k, hidden, dff, seed, shared=True):
-    pg = fg.packed_bytes(fmt, dff, hidden)
-    pd = fg.packed_bytes(fmt, hidden, dff)
-    bufs = {n: torch.empty(E * (pd if n == "down" else pg), dtype=torch.uint8, device=DEV) for n in ("gate", "up", "down")}
-    logical = {}
-    descs = {}
-    for n, (o, i) in (("gate", (dff, hidden)), ("up", (dff, hidden)), ("down", (hidden, dff))):
-        mats = datagen.matrix(fmt, o, i, datagen.tensor_seed("moe", seed, n), device=DEV, batch=E)
-        stride = pd if n == "down" else pg
-        first = None
-        for e in range(E):
-            w = fg.pack(fmt, mats["codes"][e], mats["scales"][e], 1.0, out=bufs[n], offset=e * stride)
-            if first is None:
-                first = w
-        first.desc.packed_bytes = bufs[n].numel()
-        descs[n] = first
-        logical[n] = mats
-    sh = None
-    sh_host = None
-    if shared:
-        sh, sh_host = [], {}
-        for n, (o, i) in (("gate", (dff, hidden)), ("up", (dff, hidden)), ("down", (hidden, dff))):
-            W, host = make(fmt, o, i, seed=("shared", seed, n))
-            sh.append(W)
-            sh_host[n] = host
-    layer = fg.moe_layer(descs["gate"], descs["up"], descs["down"], E, k, pg, pg, pd, shared=sh)
-    layer.keep.append(bufs)
-
-    def expert(e):
-        return {n: {"format": fmt, "codes": logical[n]["codes"][e].cpu(), "scales": logical[n]["scales"][e].cpu(),
-                    "tensor_scale": 1.0} for n in ("gate", "up", "down")}
-
-    return layer, expert, sh_host
-
-
-def check_moe(layer, expert, sh_host, X, logits, k, has_shared=True):
-    M = X.shape[0]
-    dff = layer.desc.d_ff
-    nh = k + (1 if has_shared else 0)
-    H = torch.empty((M, nh, dff), dtype=torch.bfloat16, device=DEV)
-    Y, ids, w = fg.moe_route_gemv(layer, X, logits, H=H)
-    torch.cuda.synchronize()
-    rid, rw = oracle.topk_softmax(logits.cpu().numpy(), k)
-    assert np.array_equal(ids.cpu().numpy(), rid), "top-k ids differ"
-    wg = w.cpu().double().numpy()
-    assert np.all(np.abs(wg - rw) <= 1e-5 * rw), "gate weights"
-    Xb = bits(X)
-    Hb = bits(H.view(M * nh, dff)).reshape(M, nh, dff)
-    # stage 1: every (token, expert) intermediate
-    for m in range(M):
-        for j in range(nh):
-            ex = expert(int(rid[m, j])) if j < k else sh_host
-            r = oracle.gate_up_silu(ex["gate"], ex["up"], Xb[m][None, :])
-            h = H[m, j].float().cpu().double().numpy()[None, :]
-            assert np.all(np.abs(h - r["h"]) <= h_bound(r, r["h"])), (m, j)
-    # stage 2: combine given the GPU's own h and gate weights
-    yg = Y.cpu().double().numpy()
-    e2e = 0.0
-    for m in range(M):
-        ref = np.zeros(layer.desc.hidden)
-        tol = np.zeros(layer.desc.hidden)
-        for j in range(nh):
-            ex = expert(int(rid[m, j])) if j < k else sh_host
-            d, Ad = oracle.gemv(ex["down"]["format"], ex["down"]["codes"], ex["down"]["scales"], 1.0,
-                                Hb[m, j][None, :])
-            c = wg[m, j] if j < k else 1.0
-            ref += c * d[0]
-            tol += c * Ad[0]
-        assert np.all(np.abs(yg[m] - ref) <= TOL * tol), m
-    # end to end against the pure FP64 oracle (reported)
-    full = oracle.moe(expert, sh_host if has_shared else None, Xb, logits.cpu().numpy(), k)
-    e2e = float(np.max(np.abs(yg - full["y"]) / np.maximum(full["tol"], 1e-300)))
-    log(f"moe end-to-end max |y - y_oracle| / sum(g A_down) = {e2e:.3g}")
-    assert e2e < 0.05
-    return ids
 
 
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
