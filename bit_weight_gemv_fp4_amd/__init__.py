@@ -18,7 +18,7 @@ __all__ = [
     "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_A8",
     "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "MAX_M", "MAX_M_WIDE", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
-    "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
+    "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_skinny_gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
     "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH", "Stream",
 ]
 
@@ -107,6 +107,7 @@ _SIGNATURES = {
     "fp4g_workspace_bytes": (_U64, [_I32, _VP, _I32]),
     "fp4_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP, _VP, _U64, _VP]),
     "fp4_skinny_gemm": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32, _VP, _U64, _VP]),
+    "fp4_skinny_gemm_noalloc": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32, _VP]),
     "fp4_gemv_grouped": (_I32, [ctypes.POINTER(GroupDesc), _VP, _I32, ctypes.POINTER(_VP), _I32, _VP, _U64, _VP]),
     "fp4_gate_up_silu": (_I32, [ctypes.POINTER(WeightDesc), ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32,
                                 _VP, _U64, _VP]),
@@ -327,6 +328,19 @@ def fp4_skinny_gemm(W: PackedWeight, X: torch.Tensor, Y: torch.Tensor | None = N
     wsb, need = _workspace(OP_GEMV, W, M, X.device, ws)
     _check(lib().fp4_skinny_gemm(ctypes.byref(W.desc), _bits(X), M, Y.data_ptr(), path, _ptr(wsb),
                                  wsb.numel() if wsb is not None else 0, _stream(stream)), "fp4_skinny_gemm")
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fp4_skinny_gemm_noalloc(W: PackedWeight, X: torch.Tensor, Y: torch.Tensor, path: int = PATH_AUTO,
+                            stream=None) -> torch.Tensor:
+    """fp4_skinny_gemm with the library's fixed scratch array as its workspace: no
+    device memory is allocated (Y must be given).  Calls on one GPU must be
+    ordered with each other."""
+    _check(lib().fp4_skinny_gemm_noalloc(ctypes.byref(W.desc), _bits(X), X.shape[0], Y.data_ptr(), path,
+                                         _stream(stream)), "fp4_skinny_gemm_noalloc")
     return Y
 
 

@@ -1,6 +1,8 @@
 // gemv.hip -- launch planning, host-side validation and the product entry points
 // fp4_gemv, fp4_skinny_gemm, fp4_gemv_grouped, fp4_gate_up_silu and
 // fp8_lmhead_gemv.  The kernel itself is in gemv_kernel.hpp.
+#include <mutex>
+
 #include "gemv_a8.hpp"
 
 namespace fp4g {
@@ -52,10 +54,44 @@ static fp4g_status check_ws(const void* ws, uint64_t ws_bytes, uint64_t need) {
   return FP4G_OK;
 }
 
+// ---- the library's own scratch (fp4_skinny_gemm_noalloc) -----------------------
+// A fixed device array that stands in for the caller's workspace, for callers
+// that cannot allocate.  Each GPU the library runs on holds its own copy (at its
+// own address) until the process ends; host code never uses the array's name as
+// an address, only the pointer hipGetSymbolAddress returned for that device.
+constexpr uint64_t kStaticScratchBytes = FP4G_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The scratch array's device address on the device `stream` belongs to (looked up
+// once per device, with that device current).
+static fp4g_status static_scratch(void* stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FP4G_E_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return FP4G_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FP4G_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FP4G_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return FP4G_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4G_OK;
+}
+
 // Validation + launch of n products of one input (n = 1: fp4_gemv,
 // fp4_skinny_gemm, fp8_lmhead_gemv).  Members share format and d_in.
+// use_static: take the library's scratch array instead of (ws, ws_bytes).
 static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, const uint16_t* X, int32_t M,
-                         float* const* Y, int32_t path, void* ws, uint64_t ws_bytes, void* stream) {
+                         float* const* Y, int32_t path, void* ws, uint64_t ws_bytes, void* stream,
+                         bool use_static = false) {
   if (n < 1 || n > kMaxGroup) return FP4G_E_SHAPE;
   for (int i = 0; i < n; ++i) {
     const fp4g_status st = check_weight(W[i], want_fp4);
@@ -80,6 +116,12 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   if (a8 && W[0]->format != FP4G_MXFP4) return FP4G_E_PATH;
   const bool mfma = a8 || use_mfma(path, W[0]->format, M);
   const uint64_t need = gemv_ws_bytes_any(R_total, C, 1, M);
+  if (use_static) {  // every host check above is done; the first HIP call follows
+    if (need > kStaticScratchBytes) return FP4G_E_WORKSPACE;
+    const fp4g_status sst = static_scratch(stream, &ws);
+    if (sst != FP4G_OK) return sst;
+    ws_bytes = kStaticScratchBytes;
+  }
   const fp4g_status wst = check_ws(ws, ws_bytes, need);
   if (wst != FP4G_OK) return wst;
   const size_t xbytes = (size_t)M * W[0]->d_in * 2;
@@ -176,6 +218,12 @@ int32_t fp4_gemv(const fp4g_weight* W, const uint16_t* x, float* y, void* ws, ui
 int32_t fp4_skinny_gemm(const fp4g_weight* W, const uint16_t* X, int32_t M, float* Y, int32_t path, void* ws,
                         uint64_t ws_bytes, void* stream) {
   return run_gemv(W, true, X, M, Y, path, ws, ws_bytes, stream);
+}
+
+int32_t fp4_skinny_gemm_noalloc(const fp4g_weight* W, const uint16_t* X, int32_t M, float* Y, int32_t path,
+                                void* stream) {
+  if (!W) return FP4G_E_NULL;
+  return run_group(&W, 1, true, X, M, &Y, path, nullptr, 0, stream, true);
 }
 
 int32_t fp4_gemv_grouped(const fp4g_group* G, const uint16_t* X, int32_t M, float* const* Y, int32_t path,

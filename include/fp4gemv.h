@@ -260,6 +260,24 @@ int32_t fp4_gemv(const fp4g_weight* W_host, const uint16_t* x_dev, float* y_dev,
 int32_t fp4_skinny_gemm(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M, float* Y_dev,
                         int32_t path, void* ws_dev, uint64_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): fp4_skinny_gemm with
+ * the split-K workspace taken from a fixed device array inside the library
+ * instead of ws_dev.  Same arguments, kernels and results as fp4_skinny_gemm
+ * (bit for bit, same plan).  The array holds FP4G_NOALLOC_SCRATCH_BYTES; a call
+ * whose fp4g_workspace_bytes(FP4G_OP_GEMV, W, M) exceeds it returns
+ * FP4G_E_WORKSPACE (every dense product of the feed's model fits up to M = 16:
+ * the largest, 5120 x 17408, needs 5 MiB).  Each GPU holds one array until the
+ * process ends, shared by every call on that GPU: it starts zero-filled and
+ * every call leaves it as it found it, so calls must be ordered (one stream, or
+ * streams synchronised with each other); calls that overlap in time on one GPU
+ * race on it and give unspecified results.  The first call on a device looks up
+ * the array's address there (a HIP call that allocates nothing); nothing calls
+ * hipMalloc, hipFree or any allocating routine. */
+#define FP4G_NOALLOC_SCRATCH_BYTES (16ull << 20)
+int32_t fp4_skinny_gemm_noalloc(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M, float* Y_dev,
+                                int32_t path, void* stream);
+
 /* Several products of one input in one launch: Y_dev[i][m][r] = sum_k
  * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..16 (above 8 on
  * the matrix-core path only).  Members share format and d_in: NVFP4 or MXFP4,

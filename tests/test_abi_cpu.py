@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     L = fg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -96,6 +96,23 @@ def test_gemv_error_paths():
     assert call_gemv(big, ws=None, wsb=0) == E_NULL
     assert call_gemv(big, ws=FAKE + (3 << 30), wsb=need - 1) == E_WORKSPACE
     assert call_gemv(big, ws=FAKE + (3 << 30) + 16, wsb=need) == E_ALIGN
+
+
+def test_noalloc_error_paths_before_any_hip_call():
+    """The allocation-free variant validates like fp4_skinny_gemm and refuses a
+    product whose workspace would exceed its fixed scratch, all on the host."""
+    L = fg.lib()
+    X, Y = FAKE, FAKE + (1 << 30)
+    assert L.fp4_skinny_gemm_noalloc(None, X, 1, Y, 0, None) == E_NULL
+    d = good_desc()
+    assert L.fp4_skinny_gemm_noalloc(ctypes.byref(d), None, 1, Y, 0, None) == E_NULL
+    assert L.fp4_skinny_gemm_noalloc(ctypes.byref(d), X, 0, Y, 0, None) == E_SHAPE
+    assert L.fp4_skinny_gemm_noalloc(ctypes.byref(d), X, 9, Y, fg.PATH_VALU, None) == E_PATH
+    big = good_desc(fg.NVFP4, 248320, 5120)
+    assert fg.workspace_bytes(fg.OP_GEMV, big, 12) > fg.NOALLOC_SCRATCH_BYTES
+    assert L.fp4_skinny_gemm_noalloc(ctypes.byref(big), X, 12, Y, 0, None) == E_WORKSPACE
+    f8 = good_desc(fg.FP8_ROW)
+    assert L.fp4_skinny_gemm_noalloc(ctypes.byref(f8), X, 1, Y, 0, None) == E_FORMAT
 
 
 def test_skinny_and_lmhead_error_paths():
