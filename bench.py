@@ -81,8 +81,6 @@ def parse():
     ap.add_argument("--M", type=int, default=None, help="vectors per step for c4/c5")
     ap.add_argument("--router", action="store_true",
                     help="c5: compute each layer's router logits with an FP8 512x2560 product of x")
-    ap.add_argument("--cpu-sample-layers", type=int, default=24,
-                    help="full layers the CPU oracle runs for cpu_baseline (about 0.45 s each on 16 threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "a8"],
@@ -424,55 +422,200 @@ def build_other(name, M, fg, datagen, torch, path=0, router=False, fmt=None):
 
 
 # ---- CPU oracle baseline ------------------------------------------------------------------------
+# The FP64 oracle (oracle/, test infrastructure) timed on the host as a baseline:
+# bounded samples of the workload, each run three times (median), at the box's
+# thread share and at one thread.  The oracle is plain C in FP64 and is not
+# tuned for speed: the ratio to the GPU says nothing about the kernels' quality.
 
 
-def cpu_baseline_dense(fg, datagen, torch, sample_layers, bytes_per_token):
-    """The FP64 oracle on `sample_layers` full layers plus the same fraction of the
-    LM head's rows, scaled to one token."""
+def host_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"nproc": os.cpu_count(), "affinity_cpus": aff, "model": model}
+
+
+def box_threads():
+    """Threads for the multi-threaded baseline: the CPU share this process may use
+    (OMP_NUM_THREADS when set, else the affinity mask), at most 16."""
+    aff = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    n = int(env) if env.isdigit() and int(env) > 0 else aff
+    return max(1, min(16, n, aff))
+
+
+def median3(fn):
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    ts.sort()
+    return ts[1], ts
+
+
+def baseline_entry(bytes_per_step, legs, per_token=True):
+    """legs: list of (threads, seconds per step, sample text, run times).  The
+    first leg (the box's thread share) is the reported value."""
+    th, sec, sample, runs = legs[0]
+    out = {"value": round(bytes_per_step / sec / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+           "sample": sample, "stat": "median of 3 runs", "host": host_info(), "legs": []}
+    for th, sec, sample, runs in legs:
+        leg = {"threads": th, "GB/s": round(bytes_per_step / sec / 1e9, 4), "s_per_step": round(sec, 3),
+               "sample": sample, "sample_run_s": [round(t, 3) for t in runs]}
+        if per_token:
+            leg["implied_tok_s"] = round(1.0 / sec, 5)
+        out["legs"].append(leg)
+    return out
+
+
+def cpu_baseline_dense(fg, datagen, torch, bytes_per_token, mt_layers=8, st_layers=1):
+    """C3: mt_layers full layers + every 8th LM-head row at the box's thread
+    share, st_layers + every 256th head row at one thread; scaled to one token."""
     import numpy as np
 
     import oracle
 
-    threads = max(1, min(16, os.cpu_count() or 1))
     H, F = datagen.HIDDEN, datagen.FFN
     x = datagen.bf16_normal((1, H), datagen.tensor_seed("c3", "x"), device="cuda")
     xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
     xa = datagen.bf16_normal((1, 12288), datagen.tensor_seed("c3", "x12288"), device="cuda")
     xab = xa.cpu().view(torch.int16).numpy().view(np.uint16)
-    t_total = 0.0
-    for L in range(sample_layers):
+    layers = []
+    for L in range(max(mt_layers, st_layers)):
         mats = []
         for name, (o, i) in [("gate", (F, H)), ("up", (F, H)), ("down", (H, F))] + [
-                (f"attn{j}", s) for j, s in enumerate(datagen.ATTN_SHAPES)]:
+                (f"attn{j}", sh) for j, sh in enumerate(datagen.ATTN_SHAPES)]:
             m = datagen.matrix(fg.NVFP4, o, i, datagen.tensor_seed("c3", L, name), device="cuda")
-            mats.append((name, i, m["codes"].cpu().numpy(), m["scales"].cpu().numpy()))
+            mats.append((i, m["codes"].cpu().numpy(), m["scales"].cpu().numpy()))
             del m
-        t0 = time.perf_counter()
-        g, _ = oracle.gemv(1, mats[0][2], mats[0][3], 1.0, xb, nthreads=threads)
-        u, _ = oracle.gemv(1, mats[1][2], mats[1][3], 1.0, xb, nthreads=threads)
-        hh = oracle.silu_mul(g, u)
-        oracle.gemv(1, mats[2][2], mats[2][3], 1.0, hh, nthreads=threads)
-        for name, i, c, s in mats[3:]:
-            oracle.gemv(1, c, s, 1.0, xb if i == H else xab, nthreads=threads)
-        t_total += time.perf_counter() - t0
+        layers.append(mats)
     V = datagen.VOCAB
-    rows = np.arange(0, V, max(1, datagen.LAYERS // sample_layers), dtype=np.int64)
     m = datagen.matrix(fg.FP8_ROW, V, H, datagen.tensor_seed("c3", "head"), device="cuda")
-    c, s = m["codes"].cpu().numpy(), m["scales"].cpu().numpy()
+    hc, hs = m["codes"].cpu().numpy(), m["scales"].cpu().numpy()
     del m
-    t0 = time.perf_counter()
-    oracle.gemv(3, c, s, 1.0, xb, rows=rows, nthreads=threads)
-    t_head = (time.perf_counter() - t0) * V / len(rows)
-    t_token = t_total * datagen.LAYERS / sample_layers + t_head
-    return {
-        "value": round(bytes_per_token / t_token / 1e9, 4),
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{sample_layers} of 64 layers in full + every {max(1, datagen.LAYERS // sample_layers)}th LM-head row, "
-                  f"scaled to one token ({t_total + t_head * len(rows) / V:.1f} s of CPU work); implied "
-                  f"{1.0 / t_token:.4f} tok/s",
-    }
+
+    def run(n_layers, head_every, th):
+        for mats in layers[:n_layers]:
+            g, _ = oracle.gemv(1, mats[0][1], mats[0][2], 1.0, xb, nthreads=th)
+            u, _ = oracle.gemv(1, mats[1][1], mats[1][2], 1.0, xb, nthreads=th)
+            oracle.gemv(1, mats[2][1], mats[2][2], 1.0, oracle.silu_mul(g, u), nthreads=th)
+            for i, c, sc in mats[3:]:
+                oracle.gemv(1, c, sc, 1.0, xb if i == H else xab, nthreads=th)
+        rows = np.arange(0, V, head_every, dtype=np.int64)
+        oracle.gemv(3, hc, hs, 1.0, xb, rows=rows, nthreads=th)
+
+    legs = []
+    for th, nl, every in ((box_threads(), mt_layers, 8), (1, st_layers, 256)):
+        med, runs = median3(lambda: run(nl, every, th))
+        # the sample's share of one token: nl / 64 of the layers' weights, 1/every of the head's
+        Wl = 2 * F * H + H * F + sum(o * i for o, i in datagen.ATTN_SHAPES)
+        frac_l, head_w = nl * Wl, V * H / every
+        tok_w = datagen.LAYERS * Wl + V * H
+        legs.append((th, med * tok_w / (frac_l + head_w), f"{nl} of 64 layers + every {every}th LM-head row "
+                     f"({(frac_l + head_w) / tok_w:.3f} of a token's weights), scaled to one token", runs))
+    return baseline_entry(bytes_per_token, legs)
+
+
+def cpu_baseline_moe(fg, datagen, torch, bytes_per_step, M, mt_layers=4, st_layers=1):
+    """C5: the oracle's MoE layer (routing, the picked experts and the shared
+    one) on the bench's own logits for the first layers, plus every 8th (16th at
+    one thread) LM-head row; scaled to one step of 40 layers."""
+    import numpy as np
+
+    import oracle
+
+    E, K, Hm, Fm = datagen.MOE_EXPERTS, datagen.MOE_TOPK, datagen.MOE_HIDDEN, datagen.MOE_FF
+    X = datagen.bf16_normal((M, Hm), datagen.tensor_seed("c5", "x", M), device="cuda")
+    Xb = X.cpu().view(torch.int16).numpy().view(np.uint16)
+    cases = []
+    for L in range(max(mt_layers, st_layers)):
+        lg = datagen.router_logits(M, E, datagen.tensor_seed("c5", "logits", 0, L), device="cuda").cpu().numpy()
+        ids, _ = oracle.topk_softmax(lg, K)
+        experts = {}
+        for e in sorted(set(ids.ravel().tolist()) | {E}):   # expert E is the shared one
+            e0 = (e // 64) * 64
+            ex = {}
+            for nm, (o, i) in (("gate", (Fm, Hm)), ("up", (Fm, Hm)), ("down", (Hm, Fm))):
+                m = datagen.matrix(fg.MXFP4, o, i, datagen.tensor_seed("c5", L, nm, e0), device="cuda",
+                                   batch=min(64, E + 1 - e0))
+                ex[nm] = {"format": fg.MXFP4, "codes": m["codes"][e - e0].cpu().numpy(),
+                          "scales": m["scales"][e - e0].cpu().numpy(), "tensor_scale": 1.0}
+                del m
+            experts[e] = ex
+        cases.append((lg, experts))
+    V = datagen.MOE_VOCAB
+    m = datagen.matrix(fg.FP8_ROW, V, Hm, datagen.tensor_seed("c5", "head"), device="cuda")
+    hc, hs = m["codes"].cpu().numpy(), m["scales"].cpu().numpy()
+    del m
+
+    def run(n_layers, head_every, th):
+        for lg, experts in cases[:n_layers]:
+            oracle.moe(lambda e: experts[e], experts[E], Xb, lg, K, nthreads=th)
+        oracle.gemv(3, hc, hs, 1.0, Xb, rows=np.arange(0, V, head_every, dtype=np.int64), nthreads=th)
+
+    legs = []
+    for th, nl, every in ((box_threads(), mt_layers, 8), (1, st_layers, 16)):
+        med, runs = median3(lambda: run(nl, every, th))
+        # layer time and head time measured together: scale each part by its weights
+        w_layer = (len(cases[0][1])) * 3 * Fm * Hm
+        frac = nl * w_layer + V * Hm / every
+        step_w = datagen.MOE_LAYERS * w_layer + V * Hm
+        legs.append((th, med * step_w / frac, f"MoE layers 0..{nl - 1} at M={M} (oracle routing on the bench's "
+                     f"logits, {len(cases[0][1])} experts read in layer 0) + every {every}th LM-head row, "
+                     f"scaled to one step", runs))
+    return baseline_entry(bytes_per_step, legs, per_token=M == 1)
+
+
+def cpu_baseline_products(fg, datagen, torch, name, M, bytes_per_step):
+    """C1 (one 5120x5120 GEMV), C2 / C4 (the MLP at M vectors): the oracle on one
+    copy of the workload's matrices; the one-thread leg on every 8th output row
+    of each product (the MLP's down on the oracle's own h), scaled."""
+    import numpy as np
+
+    import oracle
+
+    H, F = datagen.HIDDEN, datagen.FFN
+    if name == "c1":
+        m = datagen.matrix(fg.NVFP4, H, H, datagen.tensor_seed("c1", 0), device="cuda")
+        mats = [("gemv", m["codes"].cpu().numpy(), m["scales"].cpu().numpy())]
+        x = datagen.bf16_normal((H,), datagen.tensor_seed("c1", "x"), device="cuda")
+        X = x.view(1, -1).cpu().view(torch.int16).numpy().view(np.uint16)
+    else:
+        mats = []
+        for nm, (o, i) in (("gate", (F, H)), ("up", (F, H)), ("down", (H, F))):
+            m = datagen.matrix(fg.NVFP4, o, i, datagen.tensor_seed(name, 0, nm), device="cuda")
+            mats.append((nm, m["codes"].cpu().numpy(), m["scales"].cpu().numpy()))
+        X = datagen.bf16_normal((M, H), datagen.tensor_seed(name, "x", M), device="cuda").cpu().view(
+            torch.int16).numpy().view(np.uint16)
+
+    def run(th, every):
+        rows = lambda n: None if every == 1 else np.arange(0, n, every, dtype=np.int64)  # noqa: E731
+        if name == "c1":
+            oracle.gemv(1, mats[0][1], mats[0][2], 1.0, X, rows=rows(H), nthreads=th)
+            return
+        g, _ = oracle.gemv(1, mats[0][1], mats[0][2], 1.0, X, rows=rows(F), nthreads=th)
+        u, _ = oracle.gemv(1, mats[1][1], mats[1][2], 1.0, X, rows=rows(F), nthreads=th)
+        h = oracle.silu_mul(g, u)
+        if every != 1:  # down needs the whole h: the sampled rows' h, zeros elsewhere
+            hf = np.zeros((X.shape[0], F))
+            hf[:, ::every] = h
+            h = hf
+        oracle.gemv(1, mats[2][1], mats[2][2], 1.0, h, rows=rows(H), nthreads=th)
+
+    legs = []
+    for th, every in ((box_threads(), 1), (1, 8)):
+        med, runs = median3(lambda: run(th, every))
+        legs.append((th, med * every, "the whole product" if every == 1 else
+                     f"every {every}th output row of each product, scaled", runs))
+    return baseline_entry(bytes_per_step, legs, per_token=False)
 
 
 # ---- main ---------------------------------------------------------------------------------------
@@ -533,16 +676,19 @@ def main():
     for _ in range(args.warmup):
         g.replay()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one HIP event between consecutive replays (on the replay stream) gives each
+    # step's own time for the statistics; the wall clock around all of them gives
+    # the headline rate
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         g.replay()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) / step.steps_per_replay for i in range(args.steps))
+    gpu_ms = evs[0].elapsed_time(evs[-1]) / args.steps
     # The dominant kernel: a graph of only its launches (same weights, same order),
     # timed with HIP events on the replay stream; the average per launch includes
     # the gaps between back-to-back launches, so it is a lower bound on the
@@ -572,6 +718,14 @@ def main():
         "data": "synthetic (seeded; weights and activations resident in HBM)",
         "config": {"workload": workload, "M": M, "engine": engine, "path": args.path, "bytes_per_step": bytes_per_step,
                    "launches_per_step": len(step.calls), "setup_s": round(setup_s, 1)},
+        "step_stats": {
+            "runs": args.steps,
+            "median_ms": round(per_step[len(per_step) // 2], 4),
+            "min_ms": round(per_step[0], 4),
+            "p90_ms": round(per_step[min(len(per_step) - 1, int(0.9 * len(per_step)))], 4),
+            "median_GBps": round(bytes_per_step / (per_step[len(per_step) // 2] * 1e-3) / 1e9, 1),
+            "timed_by": "HIP events between consecutive graph replays",
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": dominant,
@@ -594,8 +748,13 @@ def main():
             sys.exit(3)
     if args.breakdown:
         out["breakdown"] = breakdown(step_launches if engine == "stream" else step, torch)
-    if not args.no_cpu_baseline and args.workload == "c3":
-        out["cpu_baseline"] = cpu_baseline_dense(fg, datagen, torch, args.cpu_sample_layers, bytes_per_step)
+    if not args.no_cpu_baseline:
+        if args.workload == "c3":
+            out["cpu_baseline"] = cpu_baseline_dense(fg, datagen, torch, bytes_per_step)
+        elif args.workload == "c5" and not args.router:
+            out["cpu_baseline"] = cpu_baseline_moe(fg, datagen, torch, bytes_per_step, M)
+        elif args.workload in ("c1", "c2", "c4") and args.fmt == "nvfp4":
+            out["cpu_baseline"] = cpu_baseline_products(fg, datagen, torch, args.workload, M, bytes_per_step)
     print(json.dumps(out), flush=True)
 
 

@@ -95,6 +95,48 @@ __device__ __forceinline__ void load_frag(Frag<FMT>& f, const uint8_t* tile, int
   }
 }
 
+// One 32-column piece j of an NVFP4/MXFP4 tile against x values xv[m][0..15]
+// (bf16 pairs of the piece's columns, per vector).
+template <uint32_t FMT, int M>
+__device__ __forceinline__ void piece_dot(const Frag<FMT>& f, int j, const uint32_t (&xv)[M][16], float (&acc)[M]) {
+  bf16x2 w[16];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    w[4 * d + 0] = e2m1x2_bf16<0>(f.q[j][d]);
+    w[4 * d + 1] = e2m1x2_bf16<1>(f.q[j][d]);
+    w[4 * d + 2] = e2m1x2_bf16<2>(f.q[j][d]);
+    w[4 * d + 3] = e2m1x2_bf16<3>(f.q[j][d]);
+  }
+  if constexpr (FMT == FP4G_NVFP4) {
+    const uint32_t sdw = f.s[j >> 1];
+    const float s0 = (j & 1) ? e4m3_f32<2>(sdw) : e4m3_f32<0>(sdw);
+    const float s1 = (j & 1) ? e4m3_f32<3>(sdw) : e4m3_f32<1>(sdw);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p0 = dot2(w[i], xv[m][i], p0);
+        p1 = dot2(w[8 + i], xv[m][8 + i], p1);
+      }
+      acc[m] = __builtin_fmaf(p0, s0, acc[m]);
+      acc[m] = __builtin_fmaf(p1, s1, acc[m]);
+    }
+  } else {
+    const int e = (int)((f.s[j >> 2] >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p0 = dot2(w[i], xv[m][i], p0);
+        p1 = dot2(w[8 + i], xv[m][8 + i], p1);
+      }
+      acc[m] += __builtin_amdgcn_ldexpf(p0 + p1, e - 127);
+    }
+  }
+}
+
 // Accumulate one tile (columns 256c .. 256c+255, or its first `npieces` 32-column
 // pieces when FULL is false) of one matrix into acc[0..M).  xc points at the bf16
 // pairs of column 256c of token 0; token m is xc + m * xstride (in u32 units).
@@ -125,10 +167,27 @@ __device__ __forceinline__ void tile_dot(const Frag<FMT>& f, const uint32_t* __r
         acc[m] += p0 + p1;
       }
     }
+  } else if constexpr (FULL) {
+    // x is read with scalar loads, which may return out of order, so each use
+    // waits for all of them: read the x of XG pieces together and wait once per
+    // group (a wait per piece put eight round trips in every tile)
+    constexpr int XG = M >= 4 ? 1 : 4 / M;
+#pragma unroll
+    for (int j0 = 0; j0 < kPiecesNv; j0 += XG) {
+      uint32_t xv[XG][M][16];
+#pragma unroll
+      for (int jj = 0; jj < XG; ++jj)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xv[jj][m][i] = xc[m * xstride + (j0 + jj) * 16 + i];
+#pragma unroll
+      for (int jj = 0; jj < XG; ++jj) piece_dot<FMT, M>(f, j0 + jj, xv[jj], acc);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < kPiecesNv; ++j) {
-      if (!FULL && j >= npieces) continue;
+      if (j >= npieces) continue;
       // 32 weights: dwords 0,1 = block 0 (16 weights), dwords 2,3 = block 1
       bf16x2 w[16];
 #pragma unroll
@@ -485,10 +544,16 @@ inline int tree_depth(int64_t S) {
 // imbalance, times 1 + 3% per level of the split-K tree (one device-scope round
 // trip each), times 1 + 15% per extra round of waves beyond what the CUs hold at
 // once (16 waves per CU while the kernel needs at most 128 VGPRs: NMAT * M up to
-// 5 for plain products, M up to 3 fused; 12 above).  No more than a quarter of a
-// workgroup's waves may be left without a chunk; ties go to more waves.  (The
-// weights are fitted to timings of the dense-model shapes on MI355X.)  A kernel
-// with more registers passes its own waves_per_cu.
+// 5 for plain products, M up to 3 fused; 12 above), times 1 + half the excess of
+// the busiest wave of a workgroup over its average (ceil(chunks / waves) against
+// chunks / waves: a workgroup ends with its slowest wave, and a per-wave timeline
+// showed the short waves idle for up to half the launch).  No more than a
+// quarter of a workgroup's waves may be left without a chunk; ties go to more
+// waves.  (The weights are fitted to timings of the dense-model shapes on
+// MI355X: the balance term moved the fused 17408x5120 gate/up from 4 to 5
+// workgroups of 4 waves per row group and a 16384-row one from one 16-wave to
+// one 4-wave workgroup per row group.)  A kernel with more registers passes its
+// own waves_per_cu.
 constexpr int kCUs = 256;
 inline Plan plan_for(int64_t R, int64_t C, int nmat, int M, int waves_per_cu = 0) {
   if (waves_per_cu == 0) waves_per_cu = (nmat == 1 ? M <= 5 : M <= 3) ? 16 : 12;
@@ -505,7 +570,9 @@ inline Plan plan_for(int64_t R, int64_t C, int nmat, int M, int waves_per_cu = 0
       const int64_t wgs = R * S, waves = wgs * nw;
       const double imbalance = (double)((wgs + kCUs - 1) / kCUs) * kCUs / (double)wgs;
       const double rounds = (double)waves / ((double)kCUs * waves_per_cu);
-      const double cost = imbalance * (1.0 + 0.03 * tree_depth(S)) * (1.0 + 0.15 * (rounds > 1.0 ? rounds - 1.0 : 0.0));
+      const double intra = (double)((wg_chunks + nw - 1) / nw) * nw / (double)wg_chunks;
+      const double cost = imbalance * (1.0 + 0.03 * tree_depth(S)) * (1.0 + 0.15 * (rounds > 1.0 ? rounds - 1.0 : 0.0)) *
+                          (1.0 + 0.5 * (intra - 1.0));
       if (cost < best_cost - 1e-9 || (cost < best_cost + 1e-9 && waves > best_waves)) {
         best = Plan{(int)S, (int)wg_chunks, nw};
         best_cost = cost;

@@ -174,10 +174,10 @@ def silu_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     return h
 
 
-def gate_up_silu(gate: dict, up: dict, X, rows=None):
+def gate_up_silu(gate: dict, up: dict, X, rows=None, nthreads=None):
     """Fused MLP front half in FP64: returns dict(h, g, u, Ag, Au), each [M][nrows]."""
-    g, Ag = gemv(gate["format"], gate["codes"], gate["scales"], gate["tensor_scale"], X, rows)
-    u, Au = gemv(up["format"], up["codes"], up["scales"], up["tensor_scale"], X, rows)
+    g, Ag = gemv(gate["format"], gate["codes"], gate["scales"], gate["tensor_scale"], X, rows, nthreads)
+    u, Au = gemv(up["format"], up["codes"], up["scales"], up["tensor_scale"], X, rows, nthreads)
     return {"h": silu_mul(g, u), "g": g, "u": u, "Ag": Ag, "Au": Au}
 
 
@@ -194,27 +194,28 @@ def topk_softmax(logits, k: int):
     return ids, w
 
 
-def moe_expert(expert: dict, x_row, h_in=None):
+def moe_expert(expert: dict, x_row, h_in=None, nthreads=None):
     """One expert on one token: d = down(SiLU(gate x) * (up x)).
 
     expert: {"gate","up","down"} logical matrices.  x_row: bf16 bits [hidden].
     h_in: optional given intermediate (bf16 bits or float64 [d_ff]) to feed the
     down projection instead of the FP64 one (stage-wise checking).
     Returns dict(h, d, Ad, hg) with hg the gate/up result dict."""
-    hg = gate_up_silu(expert["gate"], expert["up"], x_row)
+    hg = gate_up_silu(expert["gate"], expert["up"], x_row, nthreads=nthreads)
     h = hg["h"][0] if h_in is None else h_in
     dn = expert["down"]
-    d, Ad = gemv(dn["format"], dn["codes"], dn["scales"], dn["tensor_scale"], np.asarray(h)[None, :])
+    d, Ad = gemv(dn["format"], dn["codes"], dn["scales"], dn["tensor_scale"], np.asarray(h)[None, :],
+                 nthreads=nthreads)
     return {"h": hg["h"][0], "d": d[0], "Ad": Ad[0], "hg": hg}
 
 
-def moe(get_expert, shared, X, logits, k: int, h_given=None):
+def moe(get_expert, shared, X, logits, k: int, h_given=None, nthreads=None):
     """MoE layer in FP64 (article sec. 3 / sec. 4 flowchart).
 
     get_expert(e) -> {"gate","up","down"}; shared: same or None.
     X bf16 bits [M][hidden]; logits f32 [M][E].
     h_given: optional callable (m, slot) -> intermediate to feed down (slot k is
-    the shared expert).  Returns dict(ids, w, y, tol) with tol[m] the per-output
+    the shared expert).  nthreads: host threads per product (default: all).  Returns dict(ids, w, y, tol) with tol[m] the per-output
     tolerance scale sum_j w_j A_down,j + A_down,shared."""
     X = _np(X)
     ids, w = topk_softmax(logits, k)
@@ -226,14 +227,14 @@ def moe(get_expert, shared, X, logits, k: int, h_given=None):
         for j in range(k):
             ex = get_expert(int(ids[m, j]))
             hin = None if h_given is None else h_given(m, j)
-            r = moe_expert(ex, X[m], hin)
+            r = moe_expert(ex, X[m], hin, nthreads)
             contrib = w[m, j] * r["d"]
             t = w[m, j] * r["Ad"]
             y = contrib if y is None else y + contrib
             tol = t if tol is None else tol + t
         if shared is not None:
             hin = None if h_given is None else h_given(m, k)
-            r = moe_expert(shared, X[m], hin)
+            r = moe_expert(shared, X[m], hin, nthreads)
             y = y + r["d"]
             tol = tol + r["Ad"]
         ys.append(y)

@@ -389,6 +389,75 @@ def test_exact_sums_with_mixed_scales(fmt, path):
             assert np.array_equal(got.cpu().double().numpy(), Y), (shape, M)
 
 
+# ---- full-size shapes on the VALU kernel, exact sums ---------------------------------------------
+# The dense shapes and a few ragged and narrow ones: the launch plans they get
+# (one to five workgroups per row group, 4 to 16 waves, ragged rows and columns,
+# 18 workgroups on one row group for 1088x17408 at the wider vector counts)
+# must all return the exact sums.
+
+
+FULL_SHAPES = [(5120, 5120), (4160, 4096), (1088, 17408), (5152, 5152), (5120, 17408), (17408, 5120)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 8])
+@pytest.mark.parametrize("fmt", [fg.NVFP4, fg.MXFP4])
+def test_full_size_exact_sums_valu(fmt, M):
+    """Power-of-two block scales and x in {-1, 0, 1}: every row equals the oracle
+    bit for bit on the VALU kernel (a row group summed by the wrong workgroups or
+    waves, a partial added twice or lost breaks this), and a second call repeats
+    the bits."""
+    log("full-size exact", fmt, M)
+    for shape in FULL_SHAPES:
+        gen = torch.Generator(DEV).manual_seed(shape[0] * 7 + shape[1] + M)
+        mat = datagen.matrix(fmt, *shape, datagen.tensor_seed("even", fmt, shape), device=DEV)
+        sc = exact_scales(fmt, shape, gen)
+        W = fg.pack(fmt, mat["codes"], sc)
+        X = torch.randint(-1, 2, (M, shape[1]), generator=gen, device=DEV).to(torch.bfloat16)
+        Y, _ = oracle.gemv(fmt, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
+        got = fg.fp4_skinny_gemm(W, X, path=fg.PATH_VALU).clone()
+        assert np.array_equal(got.cpu().double().numpy(), Y), shape
+        assert torch.equal(fg.fp4_skinny_gemm(W, X, path=fg.PATH_VALU), got), shape
+
+
+@pytest.mark.parametrize("M", [1, 2, 3])
+def test_grouped_exact_sums_ragged_members(M):
+    """Members of 4000, 70 and 1000 rows in one launch (ragged member ends),
+    exact sums bit for bit."""
+    log("grouped exact", M)
+    shapes = [(4000, 5120), (70, 5120), (1000, 5120)]
+    gen = torch.Generator(DEV).manual_seed(91 + M)
+    mats, Ws = [], []
+    for j, shape in enumerate(shapes):
+        mat = datagen.matrix(fg.NVFP4, *shape, datagen.tensor_seed("evg", j), device=DEV)
+        sc = exact_scales(fg.NVFP4, shape, gen)
+        mats.append((mat, sc))
+        Ws.append(fg.pack(fg.NVFP4, mat["codes"], sc))
+    X = torch.randint(-1, 2, (M, 5120), generator=gen, device=DEV).to(torch.bfloat16)
+    Ys = fg.fp4_gemv_grouped(fg.Group(Ws), X, path=fg.PATH_VALU)
+    for (mat, sc), Yg in zip(mats, Ys):
+        Y, _ = oracle.gemv(fg.NVFP4, mat["codes"].cpu(), sc.cpu(), 1.0, bits(X))
+        assert np.array_equal(Yg.cpu().double().numpy(), Y)
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_gate_up_and_fp8_ragged_full_size(M):
+    """Fused gate/up (NVFP4 and FP8 pairs) and FP8 row products on the VALU
+    kernel, against the oracle's bounds, on shapes with ragged rows and columns;
+    repeated calls give the same bits."""
+    log("gate/up, fp8 ragged", M)
+    for fmt, shape in ((fg.NVFP4, (5152, 2080)), (fg.FP8_ROW, (2080, 2080))):
+        Wg, hg = make(fmt, *shape, seed=("evgu", 0))
+        Wu, hu = make(fmt, *shape, seed=("evgu", 1))
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("evguX", M, fmt), device=DEV)
+        H = fg.fp4_gate_up_silu(Wg, Wu, X, path=fg.PATH_VALU)
+        check_h(H, hg, hu, bits(X))
+        assert torch.equal(fg.fp4_gate_up_silu(Wg, Wu, X, path=fg.PATH_VALU), H)
+    for shape in ((5120, 5120), (5152, 2080)):
+        W, host = make(fg.FP8_ROW, *shape, seed="ev8")
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("ev8X", M), device=DEV)
+        check_product(fg.fp8_lmhead_gemv(W, X), host, bits(X))
+
+
 # ---- split-K exchange tree and grouped launches ----------------------------------------------
 
 
