@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "NVFP4", "MXFP4", "FP8_ROW", "PATH_AUTO", "PATH_VALU", "PATH_MFMA", "PATH_A8",
-    "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "MAX_M", "MAX_M_WIDE", "Fp4gError", "PackedWeight", "MoeLayer",
+    "ACT_BF16", "ACT_MXFP8", "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "MAX_M", "MAX_M_WIDE", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
     "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_skinny_gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
     "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH", "Stream",
@@ -62,7 +62,7 @@ class MoeDesc(ctypes.Structure):
         ("stride_up", ctypes.c_uint64),
         ("stride_down", ctypes.c_uint64),
         ("has_shared", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("act", ctypes.c_int32),
         ("sh_gate", WeightDesc),
         ("sh_up", WeightDesc),
         ("sh_down", WeightDesc),
@@ -426,11 +426,17 @@ class MoeLayer:
     keep: list = field(default_factory=list)
 
 
+ACT_BF16, ACT_MXFP8 = 0, 1
+
+
 def moe_layer(gate: PackedWeight, up: PackedWeight, down: PackedWeight, num_experts: int, top_k: int,
-              stride_gate: int, stride_up: int, stride_down: int, shared: tuple | None = None) -> MoeLayer:
+              stride_gate: int, stride_up: int, stride_down: int, shared: tuple | None = None,
+              act: int = ACT_BF16) -> MoeLayer:
     """Describe a layer whose expert e is at gate/up/down + e * stride (bytes);
-    `gate`, `up`, `down` describe expert 0 and span all experts' bytes."""
+    `gate`, `up`, `down` describe expert 0 and span all experts' bytes.  act:
+    ACT_BF16, or ACT_MXFP8 (W4A8: MXFP8 activations, MXFP4 experts)."""
     d = MoeDesc()
+    d.act = act
     d.num_experts, d.top_k = num_experts, top_k
     d.hidden, d.d_ff = gate.d_in, gate.d_out
     d.gate, d.up, d.down = gate.desc, up.desc, down.desc

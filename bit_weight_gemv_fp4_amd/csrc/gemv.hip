@@ -37,11 +37,12 @@ static bool use_mfma(int32_t path, uint32_t format, int M) {
   return M >= kMfmaMinM;
 }
 
-// A path the call can run: MFMA only for NVFP4/MXFP4; VALU only up to kMaxM
-// vectors (wider verify blocks run on the matrix cores alone).
+// A path the call can run: MFMA only for NVFP4/MXFP4; VALU up to kMaxM vectors
+// for NVFP4/MXFP4 (their wider verify blocks run on the matrix cores alone) and
+// up to kMaxMWide for FP8 rows (which have only the VALU kernel).
 static bool valid_path(int32_t path, bool fp4, int M) {
   if (path == FP4G_PATH_AUTO) return true;
-  if (path == FP4G_PATH_VALU) return M <= kMaxM;
+  if (path == FP4G_PATH_VALU) return M <= kMaxM || !fp4;
   return (path == FP4G_PATH_MFMA || path == FP4G_PATH_A8) && fp4;
 }
 
@@ -104,7 +105,7 @@ static int32_t run_group(const fp4g_weight* const* W, int n, bool want_fp4, cons
   if (!X) return FP4G_E_NULL;
   for (int i = 0; i < n; ++i)
     if (!Y[i]) return FP4G_E_NULL;
-  if (M < 1 || M > (want_fp4 ? kMaxMWide : kMaxM)) return FP4G_E_SHAPE;
+  if (M < 1 || M > kMaxMWide) return FP4G_E_SHAPE;
   if (!aligned(X, 16)) return FP4G_E_ALIGN;
   for (int i = 0; i < n; ++i)
     if (!aligned(Y[i], 16)) return FP4G_E_ALIGN;
@@ -186,18 +187,18 @@ __global__ void k_argmax_finish(unsigned long long* amax, int M, int32_t* top_id
   if (lane < M) {
     uint64_t best = 0;
     for (int j = 0; j < kArgSlots; ++j) {
-      const uint64_t k = amax[(int64_t)j * kMaxM + lane];
+      const uint64_t k = amax[(int64_t)j * kMaxMWide + lane];
       best = k > best ? k : best;
     }
     top_idx[lane] = key_index(best);
     top_val[lane] = key_value(best);
   }
   __syncthreads();
-  for (int i = lane; i < kArgSlots * kMaxM; i += 64) amax[i] = 0ull;
+  for (int i = lane; i < kArgSlots * kMaxMWide; i += 64) amax[i] = 0ull;
 }
 
 // The greedy pick's slots (zero between calls).
-static uint64_t argmax_ws_bytes() { return align256((uint64_t)kArgSlots * kMaxM * 8); }
+static uint64_t argmax_ws_bytes() { return align256((uint64_t)kArgSlots * kMaxMWide * 8); }
 
 static fp4g_status check_group(const fp4g_group* G) {
   if (!G) return FP4G_E_NULL;
@@ -248,7 +249,7 @@ int32_t fp8_lmhead_argmax(const fp4g_weight* W, const uint16_t* X, int32_t M, in
   fp4g_status st = check_weight(W, false);
   if (st != FP4G_OK) return st;
   if (!X || !top_idx || !top_val) return FP4G_E_NULL;
-  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
+  if (M < 1 || M > kMaxMWide) return FP4G_E_SHAPE;
   if (row_begin < 0 || row_begin % kRowsPerGroup || n_rows < 1 || (int64_t)row_begin + n_rows > W->d_out)
     return FP4G_E_SHAPE;
   if (!aligned(X, 16) || (logits && !aligned(logits, 16)) || !aligned(top_idx, 4) || !aligned(top_val, 4))
@@ -362,14 +363,12 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
 
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
   if (!desc || M < 1 || M > kMaxMWide) return 0;
-  if (M > kMaxM && op != FP4G_OP_GEMV && op != FP4G_OP_GATE_UP && op != FP4G_OP_GROUPED) return 0;
   if (op == FP4G_OP_MOE) return moe_ws_bytes((const fp4g_moe*)desc, M);
   if (op == FP4G_OP_LMHEAD_ARGMAX) return check_weight((const fp4g_weight*)desc, false) == FP4G_OK ? argmax_ws_bytes() : 0;
   if (op == FP4G_OP_GROUPED) {
     const fp4g_group* G = (const fp4g_group*)desc;
     if (check_group(G) != FP4G_OK) return 0;
     const bool fp4 = G->w[0].format != FP4G_FP8_ROW;
-    if (!fp4 && M > kMaxM) return 0;
     int64_t R = 0;
     for (int i = 0; i < G->n; ++i) {
       if (check_weight(&G->w[i], fp4) != FP4G_OK) return 0;
@@ -380,10 +379,11 @@ uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {
   }
   const fp4g_weight* W = (const fp4g_weight*)desc;
   if (op != FP4G_OP_GEMV && op != FP4G_OP_GATE_UP && op != FP4G_OP_LMHEAD) return 0;
-  // FP8 rows: the head, or a gate/up pair of a mixed layout (up to kMaxM vectors)
+  // FP8 rows: the head (up to kMaxMWide vectors), or a gate/up pair of a mixed
+  // layout (up to kMaxM)
   const bool fp4 = op == FP4G_OP_GEMV || (op == FP4G_OP_GATE_UP && W->format != FP4G_FP8_ROW);
   if (check_weight(W, fp4) != FP4G_OK) return 0;
-  if (!fp4 && M > kMaxM) return 0;
+  if (!fp4 && op == FP4G_OP_GATE_UP && M > kMaxM) return 0;
   return gemv_ws_bytes_any(row_groups(W->d_out), chunks(W->d_in), op == FP4G_OP_GATE_UP ? 2 : 1, M);
 }
 

@@ -19,6 +19,13 @@
 //    place: no conversion and no scale arithmetic on the VALU.
 //  * Gate and up (NMAT = 2, the fused SiLU epilogue): one staging serves both
 //    matrices; the items alternate matrices as in the bf16 matrix-core kernel.
+//  * Mixture-of-experts modes (the article's measured W4A8 MoE, Table 1 and
+//    sec. 3), as in the bf16 matrix-core kernel: MODE 1, gate/up over the
+//    union's slots (the slot's expert from the routing table); MODE 2, down with
+//    K over the union's (slot, chunk)s, each slot's h quantised to MXFP8 in the
+//    staging like any input, each chunk's product weighted per token by the
+//    slot's coefficient (the MFMA's result is added to the accumulators through
+//    one FMA per value, since a coefficient is no power of two).
 // The split-K tree and the epilogues are those of the other kernels.
 #pragma once
 #include "gemv_mfma.hpp"
@@ -36,9 +43,11 @@ inline size_t a8_lds_bytes(const Plan& pl, int M, int nmat) {
 }
 
 // Four waves per SIMD (128 registers per lane): every form fits without spills.
-template <int M, int NMAT, int EPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_a8(GemvParams p) {
+template <int M, int NMAT, int EPI, int MODE = 0>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_a8(GemvParams p, MfmaMoe q) {
   static_assert((NMAT == 1 && EPI == EPI_STORE) || (NMAT == 2 && EPI == EPI_SILU), "A8: plain or gate/up");
+  constexpr bool MOE = MODE == 1, MOED = MODE == 2;
+  static_assert((!MOE || NMAT == 2) && (!MOED || NMAT == 1), "MoE modes: gate/up, down");
   // values per lane at the end: matrix a, rows 16 r + cl, vectors 4 kg + v
   constexpr int NV = 16 * NMAT;
   constexpr int TILE = kTileMx;
@@ -49,19 +58,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int wave = wave_id();
   const int gt = uniform(blockIdx.x / p.S);
   const int s = uniform(blockIdx.x % p.S);
-  const int mem = member_of(p, gt);
-  const int g = gt - p.gbase[mem];
+  const int mem = MOE ? 0 : member_of(p, gt);
+  int g = gt - p.gbase[mem];
   const uint8_t* w0 = p.w[mem];
   const uint8_t* w1 = p.w[NMAT - 1];  // up (NMAT = 2; the group has one member)
+  int slot = 0, expert = 0;
+  if constexpr (MOE) {
+    slot = uniform(gt / q.rg);
+    g = gt - slot * q.rg;
+    if (slot >= q.route[0]) return;  // past the realised union: no byte read
+    expert = q.route[1 + slot];
+    w0 = expert >= 0 ? p.w[0] + (uint64_t)expert * q.stride[0] : q.sh[0];
+    w1 = expert >= 0 ? p.w[1] + (uint64_t)expert * q.stride[1] : q.sh[1];
+  }
   const int wg_c0 = s * p.wg_chunks;
   const int wg_c1 = min(p.C, wg_c0 + p.wg_chunks);
   const int per_wave = (wg_c1 - wg_c0 + kWavesPerWg - 1) / kWavesPerWg;
-  const int c0 = min(wg_c1, wg_c0 + wave * per_wave);
-  const int c1 = min(wg_c1, c0 + per_wave);
+  int c0 = min(wg_c1, wg_c0 + wave * per_wave);
+  int c1 = min(wg_c1, c0 + per_wave);
+  int n_valid = p.C;  // chunks that carry data (down: those of the realised union)
+  if constexpr (MOED) {
+    n_valid = uniform(q.route[0]) * q.cd;
+    c1 = min(c1, n_valid);
+    c0 = min(c0, c1);
+  }
   const int cl = lane & 15, kg = lane >> 4;
-  const int64_t tile0 = (int64_t)g * p.C;
+  const int64_t tile0 = (int64_t)g * (MOED ? q.cd : p.C);
   // items (chunk, half, matrix), matrix fastest
-  auto item_tile = [&](int it) { return (it % NMAT ? w1 : w0) + (tile0 + c0 + it / (2 * NMAT)) * TILE; };
+  auto item_tile = [&](int it) {
+    const int cv = c0 + it / (2 * NMAT);
+    if constexpr (MOED) {
+      const int sl = cv / q.cd, e = q.route[1 + sl];
+      const uint8_t* base = e >= 0 ? p.w[0] + (uint64_t)e * q.stride[0] : q.sh[0];
+      return base + (tile0 + (cv - sl * q.cd)) * TILE;
+    }
+    return (it % NMAT ? w1 : w0) + (tile0 + cv) * TILE;
+  };
   auto item_half = [&](int it) { return (it / NMAT) & 1; };
 
   const int n_items = (c1 - c0) * 2 * NMAT;
@@ -76,11 +108,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int nblk = M * p.wg_chunks * 8;  // 32-column blocks
     for (int b = threadIdx.x; b < nblk; b += kThreads) {
       const int m = b / (p.wg_chunks * 8), j = b - m * (p.wg_chunks * 8);
-      const int col = wg_c0 * kChunkK + j * 32;
       u32x4 v[4] = {};
-      if (col < p.d_in) {
+      if constexpr (MOED) {
+        // chunk cv of the union: columns of slot cv / cd's h (zero past d_ff and
+        // past the union)
+        const int cv = wg_c0 + j / 8, sl = cv / q.cd, col = (cv - sl * q.cd) * kChunkK + (j % 8) * 32;
+        if (cv < n_valid && col < q.dff) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.d_in + col + 8 * k);
+          for (int k = 0; k < 4; ++k)
+            v[k] = *reinterpret_cast<const u32x4*>(q.hbuf + ((int64_t)sl * M + m) * q.dff + col + 8 * k);
+        }
+      } else {
+        const int col = wg_c0 * kChunkK + j * 32;
+        if (col < p.d_in) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = *reinterpret_cast<const u32x4*>(p.x + (int64_t)m * p.d_in + col + 8 * k);
+        }
       }
       float amax = 0.0f;
 #pragma unroll
@@ -146,11 +189,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       t[d] = u32x4{f.q[0][d], f.q[1][d], f.q[2][d], f.q[3][d]};
       transpose_slot(t[d]);
     }
+    // MoE down: the chunk's slot's coefficient of each of the lane's vectors
+    float cf[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+    if constexpr (MOED) {
+      const int sl = (cc + wg_c0) / q.cd;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) cf[v] = 4 * kg + v < M ? q.coef[sl * M + 4 * kg + v] : 0.0f;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const i32x8 bv = {(int)t[0][r], (int)t[1][r], (int)t[2][r], (int)t[3][r], 0, 0, 0, 0};
       const int sb = (int)((f.s[r][0] >> (8 * kg)) & 0xffu);  // block 4 h + kg of row 16 r + cl
-      ac[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, ac[r], 0, 4, 0, sa, 0, sb);
+      if constexpr (MOED) {
+        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 4,
+                                                                         0, sa, 0, sb);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ac[r][v] = __builtin_fmaf(d[v], cf[v], ac[r][v]);
+      } else {
+        ac[r] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, ac[r], 0, 4, 0, sa, 0, sb);
+      }
     }
   };
 
@@ -209,8 +266,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (!live[u]) continue;
     if constexpr (EPI == EPI_SILU) {
       const int r = u / 4, m = 4 * kg + (u & 3), row = g * 64 + 16 * r + cl;
-      if (m < M && row < d_out)
-        p.h[(int64_t)m * d_out + row] = f32_to_bf16_rne(silu_f32(ua[u] * p.tscale[0]) * (ub[u] * p.tscale[1]));
+      if (m < M && row < d_out) {
+        const float tg = MOE && expert < 0 ? q.sh_ts[0] : p.tscale[0];
+        const float tu = MOE && expert < 0 ? q.sh_ts[1] : p.tscale[1];
+        const uint16_t hv = f32_to_bf16_rne(silu_f32(ua[u] * tg) * (ub[u] * tu));
+        p.h[((int64_t)slot * M + m) * d_out + row] = hv;
+        if constexpr (MOE) {
+          if (q.hdbg) {
+            if (expert < 0) {
+              q.hdbg[((int64_t)m * q.nh + q.k) * d_out + row] = hv;
+            } else {
+              for (int j = 0; j < q.k; ++j)
+                if (q.ids[m * q.k + j] == expert) q.hdbg[((int64_t)m * q.nh + j) * d_out + row] = hv;
+            }
+          }
+        }
+      }
     } else {
       const int r = u / 2, w = u % 2;
       const int m = 4 * kg + 2 * w, row = g * 64 + 16 * r + cl;
@@ -226,9 +297,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 template <int NMAT, int EPI>
 hipError_t launch_a8(int M, const GemvParams& p, unsigned grid, size_t lds, hipStream_t s) {
   switch (M) {
-#define FP4G_CASE(MM)                                        \
-  case MM:                                                   \
-    k_gemv_a8<MM, NMAT, EPI><<<grid, kThreads, lds, s>>>(p); \
+#define FP4G_CASE(MM)                                                   \
+  case MM:                                                              \
+    k_gemv_a8<MM, NMAT, EPI><<<grid, kThreads, lds, s>>>(p, MfmaMoe{}); \
+    break;
+    FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The W4A8 mixture-of-experts gate/up (MODE 1) and down (MODE 2), M = 1..16.
+template <int MODE>
+hipError_t launch_a8_moe(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds, hipStream_t s) {
+  constexpr int NMAT = MODE == 1 ? 2 : 1;
+  constexpr int EPI = MODE == 1 ? EPI_SILU : EPI_STORE;
+  switch (M) {
+#define FP4G_CASE(MM)                                                     \
+  case MM:                                                                \
+    k_gemv_a8<MM, NMAT, EPI, MODE><<<grid, kThreads, lds, s>>>(p, q);     \
     break;
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
     FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)

@@ -54,7 +54,7 @@ struct GemvParams {
   uint16_t* h;                // EPI_SILU: bf16 [M][d_out[0]]
   unsigned long long* slots;  // split-K exchange slots, zero between calls
   const float* rs[kMaxGroup];  // FP8 rows: member i's row scales (EPI_SILU: gate, up)
-  unsigned long long* amax;   // EPI_ARGMAX: [kArgSlots][kMaxM] keys, zero between calls
+  unsigned long long* amax;   // EPI_ARGMAX: [kArgSlots][kMaxMWide] keys, zero between calls
   int32_t* top_idx;           // EPI_ARGMAX: [M] row of the largest logit (+ row_base)
   float* top_val;             // EPI_ARGMAX: [M] the largest logit
   int row_base;               // EPI_ARGMAX: added to the reported row
@@ -146,6 +146,8 @@ template <uint32_t FMT, int M, bool FULL>
 __device__ __forceinline__ void tile_dot(const Frag<FMT>& f, const uint32_t* __restrict__ xc, int xstride,
                                          int npieces, float (&acc)[M]) {
   if constexpr (FMT == FP4G_FP8_ROW) {
+    // x of up to XV vectors is read together (scalar loads, one wait per group)
+    constexpr int XV = M < 4 ? M : 4;
 #pragma unroll
     for (int j = 0; j < kHalfFp8; ++j) {
       if (!FULL && j >= npieces) continue;
@@ -156,15 +158,23 @@ __device__ __forceinline__ void tile_dot(const Frag<FMT>& f, const uint32_t* __r
         w[2 * d + 1] = e4m3x2_bf16<true>(f.q[j][d]);
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint32_t* xm = xc + m * xstride + j * 8;
-        float p0 = 0.0f, p1 = 0.0f;
+      for (int m0 = 0; m0 < M; m0 += XV) {
+        uint32_t xv[XV][8];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          p0 = dot2(w[i], xm[i], p0);
-          p1 = dot2(w[i + 1], xm[i + 1], p1);
+        for (int mm = 0; mm < XV; ++mm)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[mm][i] = m0 + mm < M ? xc[(m0 + mm) * xstride + j * 8 + i] : 0u;
+#pragma unroll
+        for (int mm = 0; mm < XV; ++mm) {
+          if (m0 + mm >= M) continue;
+          float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            p0 = dot2(w[i], xv[mm][i], p0);
+            p1 = dot2(w[i + 1], xv[mm][i + 1], p1);
+          }
+          acc[m0 + mm] += p0 + p1;
         }
-        acc[m] += p0 + p1;
       }
     }
   } else if constexpr (FULL) {
@@ -362,7 +372,7 @@ __device__ __forceinline__ void argmax_epilogue(const GemvParams& p, int row, in
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) key[m] = wave_max_key(key[m]);
-  unsigned long long* slot = p.amax + (int64_t)(blockIdx.x % kArgSlots) * kMaxM;
+  unsigned long long* slot = p.amax + (int64_t)(blockIdx.x % kArgSlots) * kMaxMWide;
   if (lane == 0) {
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -508,8 +518,21 @@ hipError_t launch_m(int M, int nw, const GemvParams& p, unsigned grid, hipStream
     return launch_nw<FMT, MM, NMAT, EPI>(nw, p, grid, s);
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
 #undef FP4G_CASE
-    default: return hipErrorInvalidValue;
+    default: break;
   }
+  // FP8 rows have no matrix-core kernel: their plain products and greedy pick
+  // take verify blocks of 9..16 vectors on this one (one read of the matrix)
+  if constexpr (FMT == FP4G_FP8_ROW && NMAT == 1) {
+    switch (M) {
+#define FP4G_CASE(MM) \
+  case MM:            \
+    return launch_nw<FMT, MM, NMAT, EPI>(nw, p, grid, s);
+      FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
+#undef FP4G_CASE
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 // ---- launch planning -----------------------------------------------------------

@@ -479,7 +479,7 @@ inline int64_t exchange_units_any(int nmat, int M) {
 // Workspace for either kernel (the caller may choose the path per call).
 inline uint64_t gemv_ws_bytes_any(int64_t R_total, int64_t C, int nmat, int M) {
   const Plan b = plan_mfma(R_total, C, nmat, M);
-  const Plan a = M <= kMaxM ? plan_for(R_total, C, nmat, M) : b;  // wider: matrix cores only
+  const Plan a = plan_for(R_total, C, nmat, M);  // wider FP4: matrix cores only; FP8 rows: VALU up to 16
   const int64_t nodes = tree_nodes(a.S) > tree_nodes(b.S) ? tree_nodes(a.S) : tree_nodes(b.S);
   return (uint64_t)nodes * exchange_units_any(nmat, M) * R_total * 64 * 8;
 }
@@ -523,6 +523,38 @@ hipError_t launch_mfma_moe_down(int M, const GemvParams& p, const MfmaMoe& q, un
     k_gemv_mfma<FMT, MM, 1, EPI_STORE, 2><<<grid, kThreads, lds, s>>>(p, q); \
     break;
     FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The same for verify blocks of 9..16 tokens (instantiated in a translation unit
+// of their own).
+template <uint32_t FMT>
+hipError_t launch_mfma_moe_wide(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds,
+                                hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM)                                                       \
+  case MM:                                                                  \
+    k_gemv_mfma<FMT, MM, 2, EPI_SILU, 1><<<grid, kThreads, lds, s>>>(p, q); \
+    break;
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <uint32_t FMT>
+hipError_t launch_mfma_moe_down_wide(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds,
+                                     hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM)                                                        \
+  case MM:                                                                   \
+    k_gemv_mfma<FMT, MM, 1, EPI_STORE, 2><<<grid, kThreads, lds, s>>>(p, q); \
+    break;
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
 #undef FP4G_CASE
     default: return hipErrorInvalidValue;
   }

@@ -1,4 +1,4 @@
-// moe.hip -- one mixture-of-experts layer at decode batch sizes (M = 1..8):
+// moe.hip -- one mixture-of-experts layer at decode batch sizes (M = 1..16):
 // moe_route_gemv.
 //
 // The Ling-3.0 MoE decode article (magicnetworld.com, sec. 3 and the sec. 4
@@ -32,12 +32,17 @@
 // the matrix-core product (gemv_mfma.hpp) takes each slot's expert from them, and
 // k_moe_down follows as above; from M = 5 on the down half also runs on the
 // matrix-core kernel (its down mode).  Measured crossovers set both thresholds.
+// Verify blocks of 9..16 tokens (feed, "DFlash2: drafting a block in one pass":
+// 11 positions) take the same three launches, the routing workgroup with one
+// wave per token.  With 8-bit activations (W4A8, fp4g_moe.act) every M takes
+// the routing launch and the scaled FP4 x FP8 matrix-core kernel for both
+// halves (gemv_a8.hpp), x and each h quantised to MXFP8 in its staging.
 //
 // The kernels use the tile loop, the split-K tree and the launch planner of the
 // dense product (gemv_kernel.hpp, gemv_mfma.hpp).  Results are deterministic.
 #include <algorithm>
 
-#include "gemv_mfma.hpp"
+#include "gemv_a8.hpp"
 
 namespace fp4g {
 
@@ -50,6 +55,20 @@ extern template hipError_t launch_mfma_moe_down<FP4G_NVFP4>(int, const GemvParam
                                                             hipStream_t);
 extern template hipError_t launch_mfma_moe_down<FP4G_MXFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
                                                             hipStream_t);
+// W4A8 gate/up and down, in gemv_a8_moe.hip.
+hipError_t launch_a8_moe_up_ext(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds,
+                                hipStream_t s);
+hipError_t launch_a8_moe_down_ext(int M, const GemvParams& p, const MfmaMoe& q, unsigned grid, size_t lds,
+                                  hipStream_t s);
+// 9..16 tokens, in gemv_mfma_moe_wide.hip.
+extern template hipError_t launch_mfma_moe_wide<FP4G_NVFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
+                                                            hipStream_t);
+extern template hipError_t launch_mfma_moe_wide<FP4G_MXFP4>(int, const GemvParams&, const MfmaMoe&, unsigned, size_t,
+                                                            hipStream_t);
+extern template hipError_t launch_mfma_moe_down_wide<FP4G_NVFP4>(int, const GemvParams&, const MfmaMoe&, unsigned,
+                                                                 size_t, hipStream_t);
+extern template hipError_t launch_mfma_moe_down_wide<FP4G_MXFP4>(int, const GemvParams&, const MfmaMoe&, unsigned,
+                                                                 size_t, hipStream_t);
 
 namespace {
 
@@ -400,16 +419,19 @@ struct MoeLayout {
 constexpr int kUpWavesPerCu = 12;
 inline Plan plan_up(int64_t R, int64_t C) { return plan_latency(R, C, kUpWavesPerCu, {4, 8, 12}); }
 inline Plan plan_dn(int64_t R, int64_t C, int M) { return plan_latency(R, C, M <= 5 ? 16 : 12, {4, 8, 16}); }
-// gate/up plan and exchange units per lane for M vectors (either kernel)
-inline Plan plan_gu(int64_t R, int64_t C, int M) { return M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C); }
-inline int units_gu(int M) { return M >= kMoeMfmaMinM ? kMoeMfmaUnits : M; }
-// down plan and units: C counts the union's slots x d_ff chunks
-inline Plan plan_down(int64_t R, int64_t C, int M) {
-  return M >= kMoeMfmaDnMinM ? plan_mfma(R, C, 1, M) : plan_dn(R, C, M);
+// gate/up plan and exchange units per lane for M vectors (either kernel; the
+// W4A8 path always runs on the matrix cores, planned like the bf16 ones)
+inline Plan plan_gu(int64_t R, int64_t C, int M, bool a8) {
+  return a8 || M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C);
 }
-inline int units_dn(int M) { return M >= kMoeMfmaDnMinM ? kMoeMfmaUnitsDn : (M + 1) / 2; }
+inline int units_gu(int M, bool a8) { return a8 || M >= kMoeMfmaMinM ? kMoeMfmaUnits : M; }
+// down plan and units: C counts the union's slots x d_ff chunks
+inline Plan plan_down(int64_t R, int64_t C, int M, bool a8) {
+  return a8 || M >= kMoeMfmaDnMinM ? plan_mfma(R, C, 1, M) : plan_dn(R, C, M);
+}
+inline int units_dn(int M, bool a8) { return a8 || M >= kMoeMfmaDnMinM ? kMoeMfmaUnitsDn : (M + 1) / 2; }
 
-// Workspace: exchange slots first, sized for the largest need over M = 1..8
+// Workspace: exchange slots first, sized for the largest need over M = 1..16
 // (they must start zero-filled and every call leaves them zero), then the
 // routing tables and h at an offset that does not depend on M: calls of any M on
 // one layer shape can share a workspace without their tables ever landing in
@@ -425,26 +447,29 @@ MoeLayout moe_layout(const fp4g_moe* mo, int M) {
   L.Cg = chunks(mo->hidden);
   L.Rd = row_groups(mo->hidden);
   L.Cd = chunks(mo->d_ff);
-  L.up = plan_gu(L.Rg * L.n_slots_max, L.Cg, M);
-  L.dn = plan_down(L.Rd, L.Cd * L.n_slots_max, M);
-  uint64_t slot_bytes = 0;
-  for (int m = 1; m <= kMaxM; ++m) {
+  const bool a8 = mo->act == FP4G_ACT_MXFP8;
+  L.up = plan_gu(L.Rg * L.n_slots_max, L.Cg, M, a8);
+  L.dn = plan_down(L.Rd, L.Cd * L.n_slots_max, M, a8);
+  uint64_t slot_bytes = 0;  // the largest need of either activation format
+  for (int m = 1; m <= kMaxMWide; ++m) {
     const int ns = n_slots_for(mo, m);
-    const Plan up = plan_gu(L.Rg * ns, L.Cg, m), dn = plan_down(L.Rd, L.Cd * ns, m);
-    const uint64_t b = align256(8ull * tree_nodes(up.S) * units_gu(m) * ns * L.Rg * 64) +
-                       align256(8ull * tree_nodes(dn.S) * units_dn(m) * L.Rd * 64);
-    slot_bytes = std::max(slot_bytes, b);
+    for (bool q8 : {false, true}) {
+      const Plan up = plan_gu(L.Rg * ns, L.Cg, m, q8), dn = plan_down(L.Rd, L.Cd * ns, m, q8);
+      const uint64_t b = align256(8ull * tree_nodes(up.S) * units_gu(m, q8) * ns * L.Rg * 64) +
+                         align256(8ull * tree_nodes(dn.S) * units_dn(m, q8) * L.Rd * 64);
+      slot_bytes = std::max(slot_bytes, b);
+    }
   }
   L.off_x_up = 0;
-  L.off_x_dn = align256(8ull * tree_nodes(L.up.S) * units_gu(M) * L.n_slots_max * L.Rg * 64);
-  const int ns8 = n_slots_for(mo, kMaxM);
+  L.off_x_dn = align256(8ull * tree_nodes(L.up.S) * units_gu(M, a8) * L.n_slots_max * L.Rg * 64);
+  const int nsw = n_slots_for(mo, kMaxMWide);
   uint64_t o = slot_bytes;
   L.off_route = o;
-  o = align256(o + 4ull * (1 + ns8));
+  o = align256(o + 4ull * (1 + nsw));
   L.off_coef = o;
-  o = align256(o + 4ull * ns8 * kMaxM);
+  o = align256(o + 4ull * nsw * kMaxMWide);
   L.off_hbuf = o;
-  o = align256(o + 2ull * ns8 * kMaxM * mo->d_ff);
+  o = align256(o + 2ull * nsw * kMaxMWide * mo->d_ff);
   L.total = o;
   return L;
 }
@@ -454,6 +479,7 @@ fp4g_status check_moe(const fp4g_moe* mo) {
   if (mo->num_experts < 1 || mo->num_experts > kMaxExperts || mo->top_k < 1 || mo->top_k > kMaxTopK ||
       mo->top_k > mo->num_experts || mo->hidden < 32 || mo->d_ff < 32 || (mo->has_shared != 0 && mo->has_shared != 1))
     return FP4G_E_SHAPE;
+  if (mo->act != FP4G_ACT_BF16 && mo->act != FP4G_ACT_MXFP8) return FP4G_E_PATH;
   const fp4g_weight* ws[6] = {&mo->gate, &mo->up, &mo->down, &mo->sh_gate, &mo->sh_up, &mo->sh_down};
   const int nw = mo->has_shared ? 6 : 3;
   for (int i = 0; i < nw; ++i) {
@@ -464,6 +490,7 @@ fp4g_status check_moe(const fp4g_moe* mo) {
     if (ws[i]->d_out != (is_down ? mo->hidden : mo->d_ff) || ws[i]->d_in != (is_down ? mo->d_ff : mo->hidden))
       return FP4G_E_SHAPE;
   }
+  if (mo->act == FP4G_ACT_MXFP8 && mo->gate.format != FP4G_MXFP4) return FP4G_E_PATH;  // W4A8: MXFP4 experts
   const uint64_t pg = packed_bytes_of(mo->gate.format, mo->d_ff, mo->hidden);
   const uint64_t pd = packed_bytes_of(mo->gate.format, mo->hidden, mo->d_ff);
   if (mo->stride_gate < pg || mo->stride_up < pg || mo->stride_down < pd) return FP4G_E_SHAPE;
@@ -489,7 +516,9 @@ hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, c
   if constexpr (M >= kMoeMfmaMinM) {
     k_moe_route<M><<<1, route_waves<M>() * 64, 0, s>>>(p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    if (launch_mfma_moe<FMT>(M, mf.gp, mf.q, grid_up, mf.lds, s) != hipSuccess) return hipErrorLaunchFailure;
+    const hipError_t eu = M > kMaxM ? launch_mfma_moe_wide<FMT>(M, mf.gp, mf.q, grid_up, mf.lds, s)
+                                    : launch_mfma_moe<FMT>(M, mf.gp, mf.q, grid_up, mf.lds, s);
+    if (eu != hipSuccess) return hipErrorLaunchFailure;
   } else {
     switch (up.nw) {
       case 4: k_moe_up<FMT, M, 4><<<grid_up, 256, 0, s>>>(p); break;
@@ -500,7 +529,8 @@ hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, c
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if constexpr (M >= kMoeMfmaDnMinM) {
-    return launch_mfma_moe_down<FMT>(M, mf.gpd, mf.qd, grid_dn, mf.lds_d, s);
+    return M > kMaxM ? launch_mfma_moe_down_wide<FMT>(M, mf.gpd, mf.qd, grid_dn, mf.lds_d, s)
+                     : launch_mfma_moe_down<FMT>(M, mf.gpd, mf.qd, grid_dn, mf.lds_d, s);
   } else {
     switch (dn.nw) {
       case 4: k_moe_down<FMT, M, 4><<<grid_dn, 256, 0, s>>>(p); break;
@@ -517,6 +547,28 @@ hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, c
   return hipGetLastError();
 }
 
+// W4A8: routing once, then gate/up and down on the scaled FP4 x FP8 matrix cores.
+template <int M>
+hipError_t launch_moe_a8_m(const MoeParams& p, const MoeMfma& mf, unsigned grid_up, unsigned grid_dn, hipStream_t s) {
+  k_moe_route<M><<<1, route_waves<M>() * 64, 0, s>>>(p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (launch_a8_moe_up_ext(M, mf.gp, mf.q, grid_up, mf.lds, s) != hipSuccess) return hipErrorLaunchFailure;
+  return launch_a8_moe_down_ext(M, mf.gpd, mf.qd, grid_dn, mf.lds_d, s);
+}
+
+hipError_t launch_moe_a8(int M, const MoeParams& p, const MoeMfma& mf, unsigned grid_up, unsigned grid_dn,
+                         hipStream_t s) {
+  switch (M) {
+#define FP4G_CASE(MM) \
+  case MM:            \
+    return launch_moe_a8_m<MM>(p, mf, grid_up, grid_dn, s);
+    FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
+#undef FP4G_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <uint32_t FMT>
 hipError_t launch_moe(int M, const MoeParams& p, const MoeMfma& mf, const Plan& up, const Plan& dn, unsigned grid_up,
                       unsigned grid_dn, hipStream_t s) {
@@ -525,6 +577,7 @@ hipError_t launch_moe(int M, const MoeParams& p, const MoeMfma& mf, const Plan& 
   case MM:            \
     return launch_moe_m<FMT, MM>(p, mf, up, dn, grid_up, grid_dn, s);
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
+    FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
 #undef FP4G_CASE
     default: return hipErrorInvalidValue;
   }
@@ -533,7 +586,7 @@ hipError_t launch_moe(int M, const MoeParams& p, const MoeMfma& mf, const Plan& 
 }  // namespace
 
 uint64_t moe_ws_bytes(const fp4g_moe* mo, int M) {
-  if (check_moe(mo) != FP4G_OK || M < 1 || M > kMaxM) return 0;
+  if (check_moe(mo) != FP4G_OK || M < 1 || M > kMaxMWide) return 0;
   return moe_layout(mo, M).total;
 }
 
@@ -547,7 +600,7 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   fp4g_status st = check_moe(mo);
   if (st != FP4G_OK) return st;
   if (!X || !logits || !Y || !topk_ids || !topk_w || !ws) return FP4G_E_NULL;
-  if (M < 1 || M > kMaxM) return FP4G_E_SHAPE;
+  if (M < 1 || M > kMaxMWide) return FP4G_E_SHAPE;
   if (!aligned(X, 16) || !aligned(logits, 16) || !aligned(Y, 16) || !aligned(topk_ids, 16) ||
       !aligned(topk_w, 16) || (H && !aligned(H, 16)))
     return FP4G_E_ALIGN;
@@ -617,8 +670,9 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   p.S_dn = L.dn.S;
   const unsigned grid_up = (unsigned)(L.n_slots_max * L.Rg * L.up.S);
   const unsigned grid_dn = (unsigned)(L.Rd * L.dn.S);
+  const bool a8 = mo->act == FP4G_ACT_MXFP8;
   MoeMfma mf{};
-  if (M >= kMoeMfmaMinM) {
+  if (a8 || M >= kMoeMfmaMinM) {
     GemvParams& gp = mf.gp;
     gp.n = 1;
     gp.w[0] = p.gate;
@@ -648,7 +702,7 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
     q.ids = topk_ids;
     q.k = mo->top_k;
     q.nh = nh;
-    mf.lds = mfma_lds_bytes(L.up, mo->gate.format, 2, M);
+    mf.lds = a8 ? a8_lds_bytes(L.up, M, 2) : mfma_lds_bytes(L.up, mo->gate.format, 2, M);
     GemvParams& gd = mf.gpd;
     gd.n = 1;
     gd.w[0] = p.down;
@@ -670,10 +724,11 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
     qd.hbuf = p.hbuf;
     qd.cd = (int)L.Cd;
     qd.dff = mo->d_ff;
-    mf.lds_d = mfma_lds_bytes(L.dn, mo->gate.format, 1, M);
+    mf.lds_d = a8 ? a8_lds_bytes(L.dn, M, 1) : mfma_lds_bytes(L.dn, mo->gate.format, 1, M);
   }
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = mo->gate.format == FP4G_NVFP4
+  const hipError_t e = a8 ? launch_moe_a8(M, p, mf, grid_up, grid_dn, s)
+                       : mo->gate.format == FP4G_NVFP4
                            ? launch_moe<FP4G_NVFP4>(M, p, mf, L.up, L.dn, grid_up, grid_dn, s)
                            : launch_moe<FP4G_MXFP4>(M, p, mf, L.up, L.dn, grid_up, grid_dn, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;

@@ -84,8 +84,10 @@ typedef enum { FP4G_NVFP4 = 1, FP4G_MXFP4 = 2, FP4G_FP8_ROW = 3 } fp4g_format;
  * weights; block scales applied per block in FP32).  AUTO takes MFMA from M = 3
  * on and VALU below.  The VALU kernel takes up to 8 vectors, the MFMA kernel up
  * to 16 (FP4G_MAX_M_WIDE: a verify block of up to 15 drafts, feed section "More
- * tokens per weight read"); VALU with more than 8 is FP4G_E_PATH.  FP8 rows have
- * only the VALU kernel: MFMA is refused there with FP4G_E_PATH.  Both paths give
+ * tokens per weight read"); VALU with more than 8 NVFP4/MXFP4 vectors is
+ * FP4G_E_PATH.  FP8 rows have only the VALU kernel, up to 16 vectors for plain
+ * products and the greedy pick (8 for a fused gate/up pair): MFMA is refused
+ * there with FP4G_E_PATH.  Both paths give
  * the same results up to the order of the FP32 additions.
  * A8 (W4A8; fp4_skinny_gemm, fp4_gemv_grouped and fp4_gate_up_silu on MXFP4
  * weights only, M in 1..16, else FP4G_E_PATH): the input is first quantised per
@@ -108,9 +110,8 @@ typedef enum {
 
 /* Most matrices one fp4_gemv_grouped call takes. */
 #define FP4G_MAX_GROUP 4
-/* Vectors per call: 1..FP4G_MAX_M everywhere, up to FP4G_MAX_M_WIDE for the
- * NVFP4/MXFP4 products (fp4_skinny_gemm, fp4_gemv_grouped, fp4_gate_up_silu) on
- * the matrix-core path. */
+/* Vectors per call: 1..FP4G_MAX_M_WIDE, except the VALU path of the
+ * NVFP4/MXFP4 products and the FP8 gate/up pair (1..FP4G_MAX_M). */
 #define FP4G_MAX_M 8
 #define FP4G_MAX_M_WIDE 16
 
@@ -141,9 +142,18 @@ typedef struct {
   fp4g_weight gate, up, down;
   uint64_t stride_gate, stride_up, stride_down; /* bytes, multiples of 256 */
   int32_t has_shared;   /* 0 or 1 */
-  int32_t reserved;
+  int32_t act;          /* FP4G_ACT_BF16, or FP4G_ACT_MXFP8 (MXFP4 experts only) */
   fp4g_weight sh_gate, sh_up, sh_down;          /* used when has_shared == 1 */
 } fp4g_moe;
+
+/* Activations of a MoE layer.  BF16: the products take x and h as bf16.
+ * MXFP8 (W4A8, the Ling-3.0 article's measured configuration, Table 1 and
+ * sec. 3): x and each expert's bf16 h are quantised per vector and 32 columns to
+ * E4M3 with an E8M0 scale as FP4G_PATH_A8 does, and the products run on the
+ * scaled FP4 x FP8 matrix cores; other values are FP4G_E_PATH, and so is MXFP8
+ * with NVFP4 experts. */
+#define FP4G_ACT_BF16 0
+#define FP4G_ACT_MXFP8 1
 
 /* Matrices that multiply the same input: the query, key and value projections of
  * an attention layer, all read by one decode step (feed, section "Decode speed is
@@ -282,7 +292,7 @@ int32_t fp4_skinny_gemm_noalloc(const fp4g_weight* W_host, const uint16_t* X_dev
  * w_i[r][k] * X_dev[m][k] for each member i of G, m < M in 1..16 (above 8 on
  * the matrix-core path only).  Members share format and d_in: NVFP4 or MXFP4,
  * or FP8_ROW with each member's own row scales (the FP8 projections of a mixed
- * layout; VALU path, M in 1..8).  X_dev: bf16 [M][d_in]; Y_dev: host array of
+ * layout; VALU path, M in 1..16).  X_dev: bf16 [M][d_in]; Y_dev: host array of
  * G->n device pointers, each f32 [M][w_i.d_out], 16-B aligned and disjoint.
  * path: fp4g_path.  Each member's results are those of fp4_skinny_gemm (FP8:
  * fp8_lmhead_gemv) on it alone up to the order of the FP32 additions. */
@@ -303,7 +313,7 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg_host, const fp4g_weight* Wu_host,
                          const uint16_t* X_dev, int32_t M, uint16_t* H_dev, int32_t path,
                          void* ws_dev, uint64_t ws_bytes, void* stream);
 
-/* One MoE layer for M in 1..8 tokens (article sec. 3 and the sec. 4 flowchart:
+/* One MoE layer for M in 1..16 tokens (article sec. 3 and the sec. 4 flowchart:
  * route to top_k of num_experts, read only the chosen experts, accumulate back to
  * the hidden size; sec. 8 notes that M tokens touch the union of their experts).
  * Per token m:
@@ -315,7 +325,9 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg_host, const fp4g_weight* Wu_host,
  * Only the union of the M tokens' experts is read from memory; routing never
  * leaves the device.  Two launches for M = 1, 2 (every gate/up workgroup routes
  * the tokens itself); three from M = 3 on (routing once, gate/up on the matrix
- * cores, then down: on the VALU up to M = 4, on the matrix cores from M = 5).
+ * cores, then down: on the VALU up to M = 4, on the matrix cores from M = 5;
+ * verify blocks of 9..16 tokens the same way, e.g. the feed's 11 positions in
+ * section "DFlash2: drafting a block in one pass").
  *   X_dev       bf16 [M][hidden];  logits_dev f32 [M][num_experts];
  *   Y_dev       f32  [M][hidden];
  *   topk_ids_dev i32 [M][top_k];  topk_w_dev f32 [M][top_k];
@@ -327,7 +339,9 @@ int32_t moe_route_gemv(const fp4g_moe* moe_host, const uint16_t* X_dev, const fl
 
 /* FP8 output layer (article sec. 7; feed, section "MTP: the drafter inside the
  * checkpoint" -- the layer scores the whole vocabulary): logits_dev[m][r] =
- * s_row[r] * sum_k e4m3(c[r][k]) * X_dev[m][k] for M in 1..8.  W must be FP8_ROW.
+ * s_row[r] * sum_k e4m3(c[r][k]) * X_dev[m][k] for M in 1..16 (a verify block
+ * of up to 15 drafts is scored with one read of the layer: feed, section "DFlash2:
+ * drafting a block in one pass", verifies 11 positions).  W must be FP8_ROW.
  * X_dev: bf16 [M][d_in]; logits_dev: f32 [M][d_out]. */
 int32_t fp8_lmhead_gemv(const fp4g_weight* W_host, const uint16_t* X_dev, int32_t M,
                         float* logits_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
@@ -336,7 +350,7 @@ int32_t fp8_lmhead_gemv(const fp4g_weight* W_host, const uint16_t* X_dev, int32_
  * the vocabulary and decoding keeps its best token: feed, sections "MTP: the
  * drafter inside the checkpoint" and "Shaving the step"), over the rows
  * [row_begin, row_begin + n_rows) -- the whole vocabulary, or a draft head that
- * scores a leading part of it.  For m < M in 1..8:
+ * scores a leading part of it.  For m < M in 1..16:
  *   logit[m][r] = s_row[r] * sum_k e4m3(c[r][k]) * X_dev[m][k] as fp8_lmhead_gemv,
  *   top_idx_dev[m] = the row r (absolute, row_begin <= r < row_begin + n_rows)
  *     with the largest FP32 logit, the lower row on equal logits (-0 == +0),

@@ -82,3 +82,45 @@ def gemv(fmt, w_codes, w_scales, tensor_scale, x_bf16_bits):
     codes, scales = quantize_mxfp8(x_bf16_bits)
     Xq = dequant_mxfp8(codes, scales)
     return Xq @ W.T, np.abs(Xq) @ np.abs(W).T
+
+
+def _bf16_bits_of(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of FP64 values: FP32 round to nearest even, then bf16
+    round to nearest even (the intermediate h between the two halves of a
+    layer is bf16 on every path)."""
+    f = np.asarray(v, np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (f + 0x7FFF + ((f >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def moe(get_expert, shared, X_bits, logits, k: int):
+    """W4A8 mixture-of-experts layer in FP64 (the Ling-3.0 article's measured
+    configuration: MXFP4 experts, 8-bit activations): the routing of oracle.moe
+    (top-k by logit, ties to the lower index, softmax over the k picks), each
+    expert's gate and up on x quantised to MXFP8, h = bf16(SiLU(g) u), down on h
+    quantised to MXFP8, y = sum_j g_j d_j + d_shared.  Returns dict(ids, w, y,
+    tol) with tol the sum of the gate-weighted magnitude sums of the downs."""
+    from . import silu_mul, topk_softmax
+
+    X_bits = np.asarray(X_bits, np.uint16)
+    ids, w = topk_softmax(logits, k)
+    M = X_bits.shape[0]
+    ys, tols = [], []
+    for m in range(M):
+        picks = [(int(ids[m, j]), w[m, j]) for j in range(k)] + ([(None, 1.0)] if shared is not None else [])
+        y = 0.0
+        tol = 0.0
+        for e, c in picks:
+            ex = shared if e is None else get_expert(e)
+            g, _ = gemv(ex["gate"]["format"], ex["gate"]["codes"], ex["gate"]["scales"], ex["gate"]["tensor_scale"],
+                        X_bits[m][None, :])
+            u, _ = gemv(ex["up"]["format"], ex["up"]["codes"], ex["up"]["scales"], ex["up"]["tensor_scale"],
+                        X_bits[m][None, :])
+            h = _bf16_bits_of(silu_mul(g, u))
+            dn = ex["down"]
+            d, Ad = gemv(dn["format"], dn["codes"], dn["scales"], dn["tensor_scale"], h)
+            y = y + c * d[0]
+            tol = tol + c * Ad[0]
+        ys.append(y)
+        tols.append(tol)
+    return {"ids": ids, "w": w, "y": np.stack(ys), "tol": np.stack(tols)}

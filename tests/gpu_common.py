@@ -66,7 +66,7 @@ def check_h(H_gpu, gate, up, X_bits, rows=None):
 
 
 def build_moe(fmt, E, k, hidden, dff, seed, shared=True, tscales=(1.0, 1.0, 1.0), sh_tscales=(1.0, 1.0, 1.0),
-              scales=None, sh_scales=None):
+              scales=None, sh_scales=None, act=0):
     """An MoE layer of E routed experts (and a shared one if `shared`), packed
     back to back.  tscales: the routed gate/up/down tensor scales (one per kind,
     as the layer descriptor holds them; NVFP4 only); sh_tscales: the shared
@@ -109,7 +109,7 @@ def build_moe(fmt, E, k, hidden, dff, seed, shared=True, tscales=(1.0, 1.0, 1.0)
                 W, host = make(fmt, o, i, seed=("shared", seed, n), tensor_scale=sh_tscales[j])
             sh.append(W)
             sh_host[n] = host
-    layer = fg.moe_layer(descs["gate"], descs["up"], descs["down"], E, k, pg, pg, pd, shared=sh)
+    layer = fg.moe_layer(descs["gate"], descs["up"], descs["down"], E, k, pg, pg, pd, shared=sh, act=act)
     layer.keep.append(bufs)
 
     def expert(e):
@@ -123,7 +123,16 @@ def check_moe(layer, expert, sh_host, X, logits, k, e2e_max=0.05):
     """Stage-wise MoE parity: ids exact, gate weights to 1e-5, every (token,
     chosen expert) intermediate within the h bound, the output given the GPU's own
     h and gate weights within the product bound; end to end against the pure FP64
-    oracle reported (and held under e2e_max of the tolerance scale)."""
+    oracle reported (and held under e2e_max of the tolerance scale).  A layer with
+    8-bit activations is checked against the W4A8 oracle: each product's input
+    quantised to MXFP8 (x for gate and up, the GPU's own bf16 h for down)."""
+    from oracle import w4a8
+    a8 = layer.desc.act == fg.ACT_MXFP8
+
+    def product(mat, xbits):
+        if a8:
+            return w4a8.gemv(mat["format"], mat["codes"], mat["scales"], mat["tensor_scale"], xbits)
+        return oracle.gemv(mat["format"], mat["codes"], mat["scales"], mat["tensor_scale"], xbits)
     M = X.shape[0]
     has_shared = sh_host is not None
     dff = layer.desc.d_ff
@@ -141,7 +150,9 @@ def check_moe(layer, expert, sh_host, X, logits, k, e2e_max=0.05):
     for m in range(M):
         for j in range(nh):
             ex = expert(int(rid[m, j])) if j < k else sh_host
-            r = oracle.gate_up_silu(ex["gate"], ex["up"], Xb[m][None, :])
+            g, Ag = product(ex["gate"], Xb[m][None, :])
+            u, Au = product(ex["up"], Xb[m][None, :])
+            r = {"h": oracle.silu_mul(g, u), "g": g, "u": u, "Ag": Ag, "Au": Au}
             h = H[m, j].float().cpu().double().numpy()[None, :]
             assert np.all(np.abs(h - r["h"]) <= h_bound(r, r["h"])), (m, j)
     # stage 2: combine given the GPU's own h and gate weights
@@ -152,14 +163,13 @@ def check_moe(layer, expert, sh_host, X, logits, k, e2e_max=0.05):
         tol = np.zeros(layer.desc.hidden)
         for j in range(nh):
             ex = expert(int(rid[m, j])) if j < k else sh_host
-            dn = ex["down"]
-            d, Ad = oracle.gemv(dn["format"], dn["codes"], dn["scales"], dn["tensor_scale"], Hb[m, j][None, :])
+            d, Ad = product(ex["down"], Hb[m, j][None, :])
             c = wg[m, j] if j < k else 1.0
             ref += c * d[0]
             tol += c * Ad[0]
         assert np.all(np.abs(yg[m] - ref) <= TOL * tol), m
     # end to end against the pure FP64 oracle (reported)
-    full = oracle.moe(expert, sh_host, Xb, logits.cpu().numpy(), k)
+    full = (w4a8.moe if a8 else oracle.moe)(expert, sh_host, Xb, logits.cpu().numpy(), k)
     e2e = float(np.max(np.abs(yg - full["y"]) / np.maximum(full["tol"], 1e-300)))
     log(f"moe end-to-end max |y - y_oracle| / sum(g A_down) = {e2e:.3g}")
     assert e2e < e2e_max

@@ -129,7 +129,7 @@ def test_skinny_and_lmhead_error_paths():
     assert L.fp4_skinny_gemm(ctypes.byref(d), X, 4, Y, fg.PATH_A8, None, 0, None) == E_PATH  # A8: MXFP4 only
     assert L.fp8_lmhead_gemv(ctypes.byref(d), X, 1, Y, None, 0, None) == E_FORMAT  # NVFP4 given
     f8 = good_desc(fmt=fg.FP8_ROW)
-    assert L.fp8_lmhead_gemv(ctypes.byref(f8), X, 9, Y, None, 0, None) == E_SHAPE
+    assert L.fp8_lmhead_gemv(ctypes.byref(f8), X, 17, Y, None, 0, None) == E_SHAPE  # 1..16
     assert L.fp8_lmhead_gemv(ctypes.byref(f8), None, 1, Y, None, 0, None) == E_NULL
 
 
@@ -164,7 +164,7 @@ def test_grouped_error_paths():
     f8 = good_desc(fg.FP8_ROW); f8b = good_desc(fg.FP8_ROW, d_out=64); f8b.packed = FAKE + (8 << 30)
     assert call_grouped(group_desc(f8, k)) == E_FORMAT                 # FP8 rows with NVFP4
     assert call_grouped(group_desc(f8, f8b), path=fg.PATH_MFMA) == E_PATH  # FP8 rows: VALU only
-    assert call_grouped(group_desc(f8, f8b), M=9) == E_SHAPE
+    assert call_grouped(group_desc(f8, f8b), M=17) == E_SHAPE
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), 0]) == E_NULL
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (3 << 30) + 4]) == E_ALIGN
     assert call_grouped(group_desc(q, k), ys=[FAKE + (2 << 30), FAKE + (2 << 30) + 256]) == E_ALIAS
@@ -187,13 +187,14 @@ def test_lmhead_argmax_error_paths():
     X, I, V, LG = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), FAKE + (4 << 30)
     need = L.fp4g_workspace_bytes(fg.OP_LMHEAD_ARGMAX, ctypes.byref(f8), 1)
     assert 0 < need <= 8192
+    assert L.fp4g_workspace_bytes(fg.OP_LMHEAD_ARGMAX, ctypes.byref(f8), 16) == need
     WS = FAKE + (5 << 30)
 
     def call(d=f8, M=1, rb=0, n=300, lg=LG, i=I, v=V, ws=WS, wsb=need):
         return L.fp8_lmhead_argmax(ctypes.byref(d), X, M, rb, n, lg, i, v, ws, wsb, None)
 
     assert call(d=good_desc()) == E_FORMAT        # NVFP4 is not a head format here
-    assert call(M=9) == E_SHAPE
+    assert call(M=17) == E_SHAPE
     assert call(rb=32) == E_SHAPE                 # row_begin not a multiple of 64
     assert call(n=0) == E_SHAPE
     assert call(rb=64, n=237) == E_SHAPE          # past d_out
@@ -283,9 +284,9 @@ def call_moe(m, M=1, ws=FAKE + (9 << 32), wsb=None, **kw):
 def test_moe_error_paths():
     m = moe_desc()
     assert fg.workspace_bytes(fg.OP_MOE, m, 1) > 0
-    assert fg.workspace_bytes(fg.OP_MOE, m, 9) == 0
+    assert fg.workspace_bytes(fg.OP_MOE, m, 16) > 0 and fg.workspace_bytes(fg.OP_MOE, m, 17) == 0
     assert call_moe(m, M=0) == E_SHAPE
-    assert call_moe(m, M=9) == E_SHAPE
+    assert call_moe(m, M=17) == E_SHAPE
     m2 = moe_desc(); m2.top_k = 9
     assert call_moe(m2, wsb=1 << 30) == E_SHAPE
     m2 = moe_desc(); m2.top_k = 17; m2.num_experts = 16
@@ -299,6 +300,11 @@ def test_moe_error_paths():
     m2 = moe_desc(); m2.stride_up += 16
     assert call_moe(m2, wsb=1 << 30) in (E_ALIGN, E_SHAPE)
     assert call_moe(m, ws=None) == E_NULL
+    m2 = moe_desc(); m2.act = 2                                   # unknown activation format
+    assert call_moe(m2, wsb=1 << 30) == E_PATH
+    assert fg.workspace_bytes(fg.OP_MOE, m2, 1) == 0
+    m2 = moe_desc(); m2.act = fg.ACT_MXFP8                        # W4A8 takes the same workspace
+    assert fg.workspace_bytes(fg.OP_MOE, m2, 4) == fg.workspace_bytes(fg.OP_MOE, moe_desc(), 4)
     assert call_moe(m, wsb=fg.workspace_bytes(fg.OP_MOE, m, 1) - 1) == E_WORKSPACE
     assert call_moe(m, Y=FAKE + (6 << 32)) == E_ALIAS          # output on top of X
     assert call_moe(m, ids=FAKE + (8 << 32)) == E_ALIAS        # two outputs overlap
@@ -343,8 +349,10 @@ def test_workspace_queries():
     assert fg.workspace_bytes(fg.OP_GATE_UP, good_desc(d_out=17408, d_in=5120), 16) > 0
     assert fg.workspace_bytes(fg.OP_GEMV, big, 17) == 0
     assert fg.workspace_bytes(fg.OP_LMHEAD, good_desc(fg.FP8_ROW, 5120, 17408), 8) > 0
-    assert fg.workspace_bytes(fg.OP_LMHEAD, good_desc(fg.FP8_ROW, 5120, 17408), 9) == 0
-    assert fg.workspace_bytes(fg.OP_MOE, moe_desc(), 9) == 0
+    assert fg.workspace_bytes(fg.OP_LMHEAD, good_desc(fg.FP8_ROW, 5120, 17408), 16) > 0  # FP8 rows: up to 16
+    assert fg.workspace_bytes(fg.OP_LMHEAD, good_desc(fg.FP8_ROW, 5120, 17408), 17) == 0
+    assert fg.workspace_bytes(fg.OP_GATE_UP, good_desc(fg.FP8_ROW, 5120, 17408), 9) == 0  # FP8 pairs: up to 8
+    assert fg.workspace_bytes(fg.OP_MOE, moe_desc(), 16) > 0 and fg.workspace_bytes(fg.OP_MOE, moe_desc(), 17) == 0
     assert fg.MAX_M == 8 and fg.MAX_M_WIDE == 16
     bad = good_desc(); bad.layout_tag = 0
     assert fg.workspace_bytes(fg.OP_GEMV, bad, 1) == 0

@@ -695,6 +695,102 @@ def test_wide_verify_refuses_the_valu_path():
         fg.fp4_skinny_gemm(W, datagen.bf16_normal((17, 1056), 5, device=DEV))
 
 
+# ---- wider verify blocks on the FP8 head and the MoE layer ---------------------------------------
+
+
+@pytest.mark.parametrize("M", [9, 11, 16])
+def test_wide_verify_lmhead(M):
+    """FP8 rows at a verify block of 9..16 positions in one read of the matrix
+    (ragged shapes and the dense head's sampled rows)."""
+    log("wide lmhead", M)
+    for shape in ((300, 544), (1, 32), (2048, 2560)):
+        W, host = make(fg.FP8_ROW, *shape, seed=4)
+        X = datagen.bf16_normal((M, shape[1]), datagen.tensor_seed("Xhw", M, shape), device=DEV)
+        check_product(fg.fp8_lmhead_gemv(W, X), host, bits(X))
+    W, host = make(fg.FP8_ROW, datagen.VOCAB, datagen.HIDDEN, seed=310)
+    X = datagen.bf16_normal((M, datagen.HIDDEN), datagen.tensor_seed("Xhw", M), device=DEV)
+    check_product(fg.fp8_lmhead_gemv(W, X), host, bits(X), rows=sample_rows(datagen.VOCAB, 200, seed=M))
+
+
+@pytest.mark.parametrize("M", [11, 16])
+def test_wide_verify_lmhead_argmax_full_vocabulary(M):
+    """The greedy pick for 11 and 16 positions over the MoE model's whole
+    157184-row head: logits within the bound on every row, the pick the FP32
+    arg-max of those logits, the oracle's best row within twice the bound; and a
+    row range (a draft head)."""
+    log("wide lmhead argmax", M)
+    V, d = datagen.MOE_VOCAB, datagen.MOE_HIDDEN
+    W, host = make(fg.FP8_ROW, V, d, seed=44)
+    X = datagen.bf16_normal((M, d), datagen.tensor_seed("amw", M), device=DEV)
+    idx, val, L = fg.fp8_lmhead_argmax(W, X, logits=True)
+    Lh = L.cpu().numpy()
+    assert np.array_equal(idx.cpu().numpy(), f32_argmax(Lh))
+    assert np.array_equal(val.cpu().numpy(), Lh[np.arange(M), idx.cpu().numpy()])
+    Y, A = oracle.gemv(fg.FP8_ROW, host["codes"], host["scales"], 1.0, bits(X))
+    assert np.all(np.abs(Lh.astype(np.float64) - Y) <= TOL * A)
+    i = idx.cpu().numpy().astype(np.int64)
+    assert np.all(Y[np.arange(M), i] >= Y.max(axis=1) - 2 * TOL * A.max(axis=1))
+    idx2, _, _ = fg.fp8_lmhead_argmax(W, X, 64 * 100, 100032)
+    sub = Lh[:, 6400:6400 + 100032]
+    assert np.array_equal(idx2.cpu().numpy(), f32_argmax(sub) + 6400)
+
+
+@pytest.mark.parametrize("M", [9, 12, 16])
+def test_wide_verify_moe_small(M):
+    log("wide moe small", M)
+    for fmt, shared in ((fg.MXFP4, True), (fg.NVFP4, False)):
+        layer, expert, sh = build_moe(fmt, 16, 4, 256, 128, seed=("wide", M), shared=shared,
+                                      tscales=(1.0, 1.0, 1.0) if fmt == fg.MXFP4 else (0.5, 2.0, 1.5))
+        X = datagen.bf16_normal((M, 256), datagen.tensor_seed("mxw", M), device=DEV)
+        logits = datagen.router_logits(M, 16, datagen.tensor_seed("mlw", M), device=DEV)
+        check_moe(layer, expert, sh, X, logits, 4)
+
+
+@pytest.mark.parametrize("M", [11, 16])
+def test_wide_verify_config5_moe_layer(M):
+    """The Ling-3.0-flash-shaped MoE layer (512 MXFP4 experts, top-8 + shared) at
+    11 and 16 tokens: up to 129 experts in the union."""
+    log("wide C5 moe", M)
+    layer, expert, sh = build_moe(fg.MXFP4, 512, 8, 2560, 768, seed=5)
+    X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("C5xw", M), device=DEV)
+    logits = datagen.router_logits(M, 512, datagen.tensor_seed("C5lw", M), device=DEV)
+    check_moe(layer, expert, sh, X, logits, 8)
+
+
+# ---- W4A8 mixture-of-experts layer (8-bit activations, MXFP4 experts) -----------------------------
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 8, 16])
+def test_moe_a8_small(M):
+    log("moe a8 small", M)
+    for shared in (True, False):
+        layer, expert, sh = build_moe(fg.MXFP4, 16, 4, 256, 128, seed=("a8moe", M), shared=shared, act=fg.ACT_MXFP8)
+        X = datagen.bf16_normal((M, 256), datagen.tensor_seed("a8mx", M), device=DEV)
+        logits = datagen.router_logits(M, 16, datagen.tensor_seed("a8ml", M), device=DEV)
+        check_moe(layer, expert, sh, X, logits, 4)
+
+
+@pytest.mark.parametrize("M", [4, 8, 11, 16])
+def test_moe_a8_config5_layer(M):
+    """The Ling-3.0-flash-shaped layer on the article's measured W4A8
+    configuration (Table 1, sec. 3): 512 MXFP4 experts 768x2560 / 2560x768,
+    top-8 + shared, x and h quantised to MXFP8, at 4, 8, 11 and 16 tokens."""
+    log("moe a8 C5", M)
+    layer, expert, sh = build_moe(fg.MXFP4, 512, 8, 2560, 768, seed=5, act=fg.ACT_MXFP8)
+    X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("C5x8", M), device=DEV)
+    logits = datagen.router_logits(M, 512, datagen.tensor_seed("C5l8", M), device=DEV)
+    check_moe(layer, expert, sh, X, logits, 8)
+
+
+def test_moe_a8_refuses_nvfp4_experts():
+    layer, _, _ = build_moe(fg.NVFP4, 16, 4, 256, 128, seed=("a8nv",), act=fg.ACT_MXFP8)
+    X = datagen.bf16_normal((2, 256), 1, device=DEV)
+    logits = datagen.router_logits(2, 16, 2, device=DEV)
+    with pytest.raises(fg.Fp4gError) as e:
+        fg.moe_route_gemv(layer, X, logits)
+    assert e.value.status == 6  # FP4G_E_PATH
+
+
 # ---- mixed layout: FP8 row-scaled MLPs and projections, the MoE router ---------------------
 
 
