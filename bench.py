@@ -85,8 +85,6 @@ def parse():
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "a8"],
                     help="kernel path of the NVFP4/MXFP4 products (auto: MFMA from M = 3 on)")
-    ap.add_argument("--engine", default="launches", choices=["stream", "launches"],
-                    help="stream: one persistent launch per step (fp4_stream_run); launches: one launch per product")
     return ap.parse_args()
 
 
@@ -123,14 +121,11 @@ class Step:
 
 
 def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
-    """The dense decode chain; returns (step of separate launches, keep, stream ops).
-    In the stream every op waits for the one before it (the order of a decoder
-    layer: projections, gate/up, down, next layer), as the separate launches do."""
+    """The dense decode chain; returns (step of separate launches, keep)."""
     dev = "cuda"
     H, F = datagen.HIDDEN, datagen.FFN
     step = Step()
     keep = []
-    sops = []
     x = datagen.bf16_normal((M, H), datagen.tensor_seed("c3", "x"), device=dev)
     x_attn_in = datagen.bf16_normal((M, 12288), datagen.tensor_seed("c3", "x12288"), device=dev)
     h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
@@ -149,26 +144,6 @@ def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
         keep += [Wg, Wu, Wd] + att
         gu_bytes = 2 * fg.packed_bytes(fg.NVFP4, F, H) + M * H * 2 + M * F * 2
         step.add("gate_up_silu", (lambda Wg=Wg, Wu=Wu: fg.fp4_gate_up_silu(Wg, Wu, x, h)), gu_bytes)
-        # stream ops: per layer its own outputs (each buffer is written once per
-        # run), in the order of a decoder layer: the three projections of x run
-        # together after the previous layer, the 5120x12288 output projection
-        # waits for them, then gate/up + SiLU, then down
-        prev = len(sops) - 1
-        for j in (0, 1, 3, 2):
-            o, i = datagen.ATTN_SHAPES[j]
-            out = torch.empty((M, o), dtype=torch.float32, device=dev)
-            keep.append(out)
-            if j == 2:
-                w_op, w_cnt = len(sops) - 1, 3
-            else:
-                w_op, w_cnt = prev, 1
-            sops.append({"kind": fg.OP_GEMV, "w": att[j], "x": x if i == H else x_attn_in, "out": out,
-                         "wait_op": w_op, "wait_count": w_cnt})
-        hl = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
-        yl = torch.empty((M, H), dtype=torch.float32, device=dev)
-        keep += [hl, yl]
-        sops.append({"kind": fg.OP_GATE_UP, "w": Wg, "w_up": Wu, "x": x, "out": hl, "wait_op": len(sops) - 1})
-        sops.append({"kind": fg.OP_GEMV, "w": Wd, "x": hl, "out": yl, "wait_op": len(sops) - 1})
         if M == 1:
             step.add("down", (lambda Wd=Wd: fg.fp4_gemv(Wd, h.view(-1), y.view(-1))),
                      algorithmic_gemv_bytes(fg, fg.NVFP4, H, F, M))
@@ -200,10 +175,7 @@ def build_dense_stream(fg, datagen, torch, layers, with_head=True, M=1):
         keep += [Wh, logits]
         step.add("lm_head", (lambda: fg.fp8_lmhead_gemv(Wh, x, logits)),
                  algorithmic_gemv_bytes(fg, fg.FP8_ROW, datagen.VOCAB, H, M))
-        lg2 = torch.empty((M, datagen.VOCAB), dtype=torch.float32, device=dev)
-        keep.append(lg2)
-        sops.append({"kind": fg.OP_LMHEAD, "w": Wh, "x": x, "out": lg2, "wait_op": len(sops) - 1})
-    return step, keep, sops
+    return step, keep
 
 
 def build_mixed_stream(fg, datagen, torch, M=1):
@@ -639,18 +611,10 @@ def main():
     M = args.M or (4 if args.workload in ("c4", "skinny") else 1)
     t_setup = time.perf_counter()
     if args.workload == "c3":
-        step, keep, sops = build_dense_stream(fg, datagen, torch, datagen.LAYERS, True, M=M)
+        step, keep = build_dense_stream(fg, datagen, torch, datagen.LAYERS, True, M=M)
         workload = "full dense weight stream, M=1: 64 x [NVFP4 attention 12288x5120, 12288x5120, 5120x12288, " \
                    "7680x5120, gate/up 17408x5120 + SiLU*mul, down 5120x17408] + FP8 LM head 248320x5120"
         dominant = "gate_up_silu"
-        if args.engine == "stream":
-            st = fg.Stream(sops, M)
-            keep.append(st)
-            sstep = Step()
-            sstep.add("decode_stream", st.run, step.bytes())
-            step_launches = step
-            step = sstep
-            dominant = "decode_stream"
     elif args.workload == "c3m":
         step, keep = build_mixed_stream(fg, datagen, torch, M=M)
         workload = (f"full dense weight stream in the mixed layout, M={M}: 64 layers of FP8 projections (48 linear "
@@ -662,7 +626,6 @@ def main():
         fmt = {"nvfp4": fg.NVFP4, "mxfp4": fg.MXFP4}[args.fmt]
         step, keep, workload, dominant = build_other(args.workload, M, fg, datagen, torch, path, args.router, fmt)
     bytes_per_step = step.bytes() / step.steps_per_replay
-    engine = args.engine if args.workload == "c3" else "launches"
     # one eager pass allocates the workspace and checks every launch
     step.run()
     torch.cuda.synchronize()
@@ -716,7 +679,7 @@ def main():
         "vs_baseline": None,
         "dtype": "e2m1/e4m3 weights x bf16 -> f32",
         "data": "synthetic (seeded; weights and activations resident in HBM)",
-        "config": {"workload": workload, "M": M, "engine": engine, "path": args.path, "bytes_per_step": bytes_per_step,
+        "config": {"workload": workload, "M": M, "path": args.path, "bytes_per_step": bytes_per_step,
                    "launches_per_step": len(step.calls), "setup_s": round(setup_s, 1)},
         "step_stats": {
             "runs": args.steps,
@@ -740,14 +703,8 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
         },
     }
-    if engine == "stream":
-        err = keep[-1].error()
-        out["stream_error_flag"] = err
-        if err:
-            print(json.dumps({"error": "decode stream reported a time-out; results invalid"}), file=sys.stderr)
-            sys.exit(3)
     if args.breakdown:
-        out["breakdown"] = breakdown(step_launches if engine == "stream" else step, torch)
+        out["breakdown"] = breakdown(step, torch)
     if not args.no_cpu_baseline:
         if args.workload == "c3":
             out["cpu_baseline"] = cpu_baseline_dense(fg, datagen, torch, bytes_per_step)

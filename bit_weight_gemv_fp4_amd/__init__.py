@@ -19,7 +19,7 @@ __all__ = [
     "ACT_BF16", "ACT_MXFP8", "OP_GEMV", "OP_GATE_UP", "OP_MOE", "OP_LMHEAD", "OP_GROUPED", "OP_LMHEAD_ARGMAX", "MAX_GROUP", "MAX_M", "MAX_M_WIDE", "Fp4gError", "PackedWeight", "MoeLayer",
     "lib", "abi_version", "status_string", "packed_bytes", "workspace_bytes", "pack", "unpack",
     "validate", "quantize", "fp4_gemv", "fp4_skinny_gemm", "fp4_skinny_gemm_noalloc", "NOALLOC_SCRATCH_BYTES", "fp4_gemv_grouped", "Group", "fp4_gate_up_silu", "moe_route_gemv",
-    "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH", "Stream",
+    "fp8_lmhead_gemv", "fp8_lmhead_argmax", "LIB_PATH"
 ]
 
 NVFP4, MXFP4, FP8_ROW = 1, 2, 3
@@ -69,32 +69,6 @@ class MoeDesc(ctypes.Structure):
     ]
 
 
-class StreamOpDesc(ctypes.Structure):
-    _fields_ = [
-        ("kind", ctypes.c_int32),
-        ("wait_op", ctypes.c_int32),
-        ("wait_count", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
-        ("w", ctypes.POINTER(WeightDesc)),
-        ("w_up", ctypes.POINTER(WeightDesc)),
-        ("x_dev", ctypes.c_void_p),
-        ("out_dev", ctypes.c_void_p),
-    ]
-
-
-class StreamPlan(ctypes.Structure):
-    _fields_ = [
-        ("magic", ctypes.c_uint32),
-        ("M", ctypes.c_int32),
-        ("n_ops", ctypes.c_int32),
-        ("n_items", ctypes.c_int32),
-        ("grid", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
-        ("ws", ctypes.c_void_p),
-        ("ws_bytes", ctypes.c_uint64),
-    ]
-
-
 _VP, _I32, _U32, _U64, _F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float
 _SIGNATURES = {
     "fp4g_abi_version": (_U32, []),
@@ -114,10 +88,6 @@ _SIGNATURES = {
     "moe_route_gemv": (_I32, [ctypes.POINTER(MoeDesc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _VP, _U64, _VP]),
     "fp8_lmhead_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _VP, _U64, _VP]),
     "fp8_lmhead_argmax": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _U64, _VP]),
-    "fp4g_stream_workspace_bytes": (_U64, [ctypes.POINTER(StreamOpDesc), _I32, _I32]),
-    "fp4g_stream_build": (_I32, [ctypes.POINTER(StreamOpDesc), _I32, _I32, _VP, _U64, ctypes.POINTER(StreamPlan), _VP]),
-    "fp4_stream_run": (_I32, [ctypes.POINTER(StreamPlan), _VP]),
-    "fp4g_stream_error": (_I32, [ctypes.POINTER(StreamPlan), ctypes.POINTER(ctypes.c_int32), _VP]),
 }
 
 _lib = None
@@ -469,43 +439,3 @@ def moe_route_gemv(layer: MoeLayer, X: torch.Tensor, logits: torch.Tensor, Y: to
                                 topk_w.data_ptr(), _ptr(H), _ptr(wsb), wsb.numel() if wsb is not None else 0,
                                 _stream(stream)), "moe_route_gemv")
     return Y, topk_ids, topk_w
-
-
-class Stream:
-    """A decode step's chain of products run by one persistent launch.
-
-    ops: list of dicts {"kind": OP_GEMV | OP_GATE_UP | OP_LMHEAD, "w": PackedWeight,
-    "w_up": PackedWeight (GATE_UP), "x": bf16 tensor [M, d_in], "out": tensor
-    [M, d_out] (float32, or bfloat16 for GATE_UP), "wait_op": index or -1,
-    "wait_count": ops ending at wait_op to wait for (default 1)}."""
-
-    def __init__(self, ops, M: int, stream=None):
-        n = len(ops)
-        self.M = M
-        self.keep = ops
-        self.arr = (StreamOpDesc * n)()
-        for i, o in enumerate(ops):
-            d = self.arr[i]
-            d.kind = o["kind"]
-            d.wait_op = o.get("wait_op", -1)
-            d.wait_count = o.get("wait_count", 1)
-            d.w = ctypes.pointer(o["w"].desc)
-            d.w_up = ctypes.pointer(o["w_up"].desc) if o.get("w_up") is not None else None
-            assert o["x"].dtype == torch.bfloat16 and o["x"].is_contiguous() and o["out"].is_contiguous()
-            d.x_dev = o["x"].data_ptr()
-            d.out_dev = o["out"].data_ptr()
-        nb = lib().fp4g_stream_workspace_bytes(self.arr, n, M)
-        if nb == 0:
-            raise Fp4gError(2, "fp4g_stream_workspace_bytes")
-        self.ws = torch.zeros(nb, dtype=torch.uint8, device=ops[0]["x"].device)
-        self.plan = StreamPlan()
-        _check(lib().fp4g_stream_build(self.arr, n, M, self.ws.data_ptr(), nb, ctypes.byref(self.plan),
-                                       _stream(stream)), "fp4g_stream_build")
-
-    def run(self, stream=None):
-        _check(lib().fp4_stream_run(ctypes.byref(self.plan), _stream(stream)), "fp4_stream_run")
-
-    def error(self, stream=None) -> int:
-        e = ctypes.c_int32(0)
-        _check(lib().fp4g_stream_error(ctypes.byref(self.plan), ctypes.byref(e), _stream(stream)), "fp4g_stream_error")
-        return e.value

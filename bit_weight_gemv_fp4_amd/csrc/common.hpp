@@ -30,12 +30,6 @@ constexpr int kMaxM = 8;       // vectors per call: VALU kernels, MoE, FP8 rows
 constexpr int kMaxMWide = 16;  // NVFP4/MXFP4 products on the matrix-core kernel
 constexpr int kWavesPerWg = 4;
 constexpr int kThreads = 256;
-// Every workspace starts with a fixed region of hand-off counters.  No call ever
-// writes anything else there, so counters left at zero by one call are still zero
-// for the next, whatever the shapes.  Partial sums and tables start after it.
-constexpr uint64_t kCounterBytes = 65536;
-constexpr int kMaxCounters = (int)(kCounterBytes / 4);
-
 __host__ __device__ inline int tile_bytes(uint32_t fmt) {
   return fmt == FP4G_NVFP4 ? kTileNv : fmt == FP4G_MXFP4 ? kTileMx : kTileF8;
 }
@@ -97,30 +91,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
-// ---- split-K hand-off between workgroups ---------------------------------------
-// Partial sums are published with device-scope stores (written through to the
-// point where all XCDs see them) and read back with device-scope loads, so no
-// full-L2 write-back or invalidate is needed.  The s_waitcnt makes this wave's
-// partial stores complete before the arrival counter is incremented; the loads
-// of the last arriver are issued after its atomic returned.
-__device__ __forceinline__ void publish_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// ---- data shared between workgroups of one launch ------------------------------
+// Device-scope (agent) loads and stores: they reach the point where every XCD
+// sees them, so a workgroup can read what another one wrote in the same launch
+// without a cache write-back or invalidate (the split-K tree uses device-scope
+// atomics; the fused MoE layer hands h over with these).
+#define FP4G_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ uint64_t load_dev_u64(const void* p) {
+  return __hip_atomic_load((const FP4G_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float collect_partial(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ unsigned load_dev_u32(const unsigned* p) {
+  return __hip_atomic_load((const FP4G_GLOBAL unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Called by one whole wave after it published its partials; true in the wave of
-// the workgroup that arrives last (`expected_prev` earlier arrivals).
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected_prev) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  unsigned prev = 0;
-  if ((threadIdx.x & 63) == 0) prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0, 64);
-  return prev == expected_prev;
-}
-// The last arriver leaves the counter at zero for the next call.
-__device__ __forceinline__ void reset_counter(unsigned* counter) {
-  if ((threadIdx.x & 63) == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_dev_u16(void* p, uint16_t v) {
+  __hip_atomic_store((FP4G_GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int wave_id() {

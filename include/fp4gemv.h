@@ -364,71 +364,6 @@ int32_t fp8_lmhead_argmax(const fp4g_weight* W_host, const uint16_t* X_dev, int3
                           int32_t n_rows, float* logits_dev, int32_t* top_idx_dev, float* top_val_dev,
                           void* ws_dev, uint64_t ws_bytes, void* stream);
 
-/* --- a whole decode step in one launch --------------------------------------- */
-
-/* One product of a decode step.  Decoding a token runs every matrix of the model
- * once, each on the previous one's output (feed, section "Decode speed is bytes
- * divided by bandwidth"); a stream is that chain, executed by one launch in
- * which each unit of work (op, 64-row group, K split) puts its weight loads in
- * flight before it waits for the ops it depends on.
- *   kind     FP4G_OP_GEMV: NVFP4/MXFP4 matrix, out = f32 [M][d_out];
- *            FP4G_OP_GATE_UP: gate (w) and up (w_up) of one shape, out = bf16
- *            [M][d_out] = bf16(SiLU(gate x) * (up x)) as fp4_gate_up_silu;
- *            FP4G_OP_LMHEAD: FP8_ROW matrix, out = f32 [M][d_out].
- *   wait_op  -1, or the index of an earlier op: this op reads x only after every
- *            output row of ops wait_op-wait_count+1 .. wait_op is written.
- *   wait_count  how many consecutive ops end at wait_op (0 is taken as 1); ops
- *            that read the same input and wait for the same ops run concurrently
- *            (e.g. the projections of one input).  The op's x may overlap the
- *            outputs of the ops it waits for and of no other op.
- *   w, w_up  host pointers to descriptors; d_out % 64 == 0, d_in % 256 == 0.
- *   x_dev    bf16 [M][d_in], 16-B aligned.  out_dev: 256-B aligned; outputs of
- *            different ops must not overlap each other, any weights or any x
- *            except as above. */
-typedef struct {
-  int32_t kind;
-  int32_t wait_op;
-  int32_t wait_count;
-  int32_t reserved;
-  const fp4g_weight* w;
-  const fp4g_weight* w_up;
-  const uint16_t* x_dev;
-  void* out_dev;
-} fp4g_stream_op;
-
-/* Filled in by fp4g_stream_build; passed by value to the calls below. */
-typedef struct {
-  uint32_t magic;
-  int32_t M;        /* vectors per product, 1..8 */
-  int32_t n_ops;
-  int32_t n_items;  /* work units (op, 64-row group, K split) */
-  int32_t grid;     /* workgroups per launch (one per unit) */
-  int32_t reserved; /* set by fp4g_stream_build (LDS bytes per workgroup); do not edit */
-  void* ws;         /* the stream's workspace (device) */
-  uint64_t ws_bytes;
-} fp4g_stream_plan;
-
-/* Workspace bytes for a stream of n_ops ops at M vectors (0 if invalid). */
-uint64_t fp4g_stream_workspace_bytes(const fp4g_stream_op* ops_host, int32_t n_ops, int32_t M);
-
-/* Validate the ops, write the op table into ws_dev, zero its counters, and fill
- * *plan_host.  Synchronises `stream`.  The workspace then belongs to this stream
- * (do not pass it to other calls).  The descriptors and device buffers the ops
- * name must stay valid for every run. */
-int32_t fp4g_stream_build(const fp4g_stream_op* ops_host, int32_t n_ops, int32_t M, void* ws_dev, uint64_t ws_bytes,
-                          fp4g_stream_plan* plan_host, void* stream);
-
-/* Run every op of the stream once, asynchronously (a one-thread launch that
- * counts the run, then the stream's launch; capturable in a HIP graph).  Runs of
- * one plan must be ordered on one stream.  A run that hits an internal time-out
- * sets a sticky error flag (see fp4g_stream_error) instead of hanging; its
- * outputs are then unspecified. */
-int32_t fp4_stream_run(const fp4g_stream_plan* plan_host, void* stream);
-
-/* Read (into *err_host: 0 = every run since the last check was complete) and
- * clear the sticky error flag.  Synchronises `stream`. */
-int32_t fp4g_stream_error(const fp4g_stream_plan* plan_host, int32_t* err_host, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

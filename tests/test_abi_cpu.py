@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 16, names
     L = fg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -356,49 +356,3 @@ def test_workspace_queries():
     assert fg.MAX_M == 8 and fg.MAX_M_WIDE == 16
     bad = good_desc(); bad.layout_tag = 0
     assert fg.workspace_bytes(fg.OP_GEMV, bad, 1) == 0
-
-
-def stream_op(kind=fg.OP_GEMV, wait=-1, d_out=128, d_in=512, fmt=fg.NVFP4, x=FAKE + (20 << 32), out=FAKE + (21 << 32),
-              w_base=0):
-    w = good_desc(fmt, d_out, d_in)
-    w.packed = FAKE + ((30 + w_base) << 32)
-    o = fg.StreamOpDesc()
-    o.kind, o.wait_op = kind, wait
-    o.w = ctypes.pointer(w)
-    o.w_up = ctypes.pointer(good_desc(fmt, d_out, d_in)) if kind == fg.OP_GATE_UP else None
-    if kind == fg.OP_GATE_UP:
-        o.w_up.contents.packed = FAKE + ((60 + w_base) << 32)
-    o.x_dev, o.out_dev = x, out
-    return o, w
-
-
-def build_stream(ops, M=1, ws=FAKE + (50 << 32), wsb=None):
-    arr = (fg.StreamOpDesc * len(ops))(*[o for o, _ in ops])
-    if wsb is None:
-        wsb = fg.lib().fp4g_stream_workspace_bytes(arr, len(ops), M)
-    plan = fg.StreamPlan()
-    return fg.lib().fp4g_stream_build(arr, len(ops), M, ws, wsb, ctypes.byref(plan), None)
-
-
-def test_stream_error_paths():
-    L = fg.lib()
-    ok = [stream_op(), stream_op(wait=0, out=FAKE + (22 << 32), w_base=1)]
-    arr = (fg.StreamOpDesc * 2)(*[o for o, _ in ok])
-    assert L.fp4g_stream_workspace_bytes(arr, 2, 1) > 0
-    assert L.fp4g_stream_workspace_bytes(arr, 2, 9) == 0
-    assert L.fp4g_stream_workspace_bytes(arr, 0, 1) == 0
-    assert build_stream([stream_op(d_in=288)]) == E_SHAPE           # d_in % 256
-    assert build_stream([stream_op(d_out=70)]) == E_SHAPE           # d_out % 64
-    assert build_stream([stream_op(wait=0)]) == E_SHAPE             # waits on itself
-    assert build_stream([stream_op(kind=9)]) == E_FORMAT
-    assert build_stream([stream_op(kind=fg.OP_LMHEAD)]) == E_FORMAT  # NVFP4 given to an FP8 op
-    assert build_stream([stream_op(out=FAKE + (21 << 32) + 16)]) == E_ALIGN
-    assert build_stream([stream_op(), stream_op(wait=0, w_base=1)]) == E_ALIAS  # same output twice
-    # op 1 reads op 0's output without waiting for it
-    assert build_stream([stream_op(), stream_op(x=FAKE + (21 << 32), out=FAKE + (22 << 32), w_base=1)]) == E_ALIAS
-    assert build_stream(ok, ws=None) == E_NULL
-    assert build_stream(ok, wsb=1024) == E_WORKSPACE
-    plan = fg.StreamPlan()
-    assert L.fp4_stream_run(ctypes.byref(plan), None) == E_NULL
-    plan.ws = FAKE
-    assert L.fp4_stream_run(ctypes.byref(plan), None) == E_FORMAT   # not built
