@@ -261,6 +261,8 @@ def _workspace(op, desc, M, device, ws):
     if need == 0:
         return None, 0
     dev = torch.device(device)
+    if dev.type == "cuda" and dev.index is None:  # "cuda" and "cuda:0" name one buffer
+        dev = torch.device("cuda", torch.cuda.current_device())
     key = dev
     if op == OP_MOE:
         # MoE keeps tables after its slots: one workspace per layer shape

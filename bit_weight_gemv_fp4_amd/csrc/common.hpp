@@ -91,22 +91,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
-// ---- data shared between workgroups of one launch ------------------------------
-// Device-scope (agent) loads and stores: they reach the point where every XCD
-// sees them, so a workgroup can read what another one wrote in the same launch
-// without a cache write-back or invalidate (the split-K tree uses device-scope
-// atomics; the fused MoE layer hands h over with these).
-#define FP4G_GLOBAL __attribute__((address_space(1)))
-__device__ __forceinline__ uint64_t load_dev_u64(const void* p) {
-  return __hip_atomic_load((const FP4G_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned load_dev_u32(const unsigned* p) {
-  return __hip_atomic_load((const FP4G_GLOBAL unsigned*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_dev_u16(void* p, uint16_t v) {
-  __hip_atomic_store((FP4G_GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
@@ -151,6 +135,26 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum of a 32-bit value over the 64 lanes, uniform (the same DPP steps).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// Sum of lanes 0..7 (the others must hold 0), uniform: row_shr 1, 2, 4 add
+// pairs, then pairs of pairs, so lane 7 holds ((e7+e6)+(e5+e4))+((e3+e2)+(e1+e0)).
+__device__ __forceinline__ float wave_sum8(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 7));
 }
 
 // ---- host-side validation helpers -----------------------------------------------

@@ -7,19 +7,21 @@
 // sec. 8 notes that M tokens read the union of their experts.  Routing never
 // leaves the device.  For M = 1, 2 two launches:
 //
-//  k_moe_up   Every workgroup first routes all M tokens itself (top-k of the
-//             logits by a wave arg-max per pick, softmax over the k picked, the
-//             sorted union of the picked experts via an LDS bitmap), then takes
-//             the (slot, 64-row group, K split) its block index names.  Slots are
-//             the union's experts in ascending id, then the shared expert.
-//             Workgroups past the realised union exit before reading a byte, so
-//             only the union's gate/up bytes stream.  The K splits of a (slot,
-//             row group) meet in the split-K exchange tree, and the survivor
-//             writes h = bf16(SiLU(gate x) * (up x)) for all M tokens to the
-//             workspace.  Workgroup 0 also writes the routing tables: the slots'
-//             experts and, per (slot, token), the gate weight times the down
-//             matrix's tensor scale (0 for a token that did not pick the expert,
-//             1 x scale for the shared expert).
+//  k_moe_up   Every workgroup first routes the M tokens itself (top-k of the
+//             logits by a wave arg-max per pick, softmax over the k picked),
+//             then takes the (slot, 64-row group, K split) its block index
+//             names.  At M = 1 the slots are the picks in pick order, then the
+//             shared expert, and a workgroup picks only as far as its own slot;
+//             at M = 2 they are the union's experts in ascending id (ranked
+//             lane-parallel), then the shared expert.  Workgroups past the
+//             realised union exit before reading a byte, so only the union's
+//             gate/up bytes stream.  The K splits of a (slot, row group) meet in
+//             the split-K exchange tree, and the survivor writes
+//             h = bf16(SiLU(gate x) * (up x)) for all M tokens to the workspace.
+//             One workgroup also writes the routing tables: the slots' experts
+//             and, per (slot, token), the gate weight times the down matrix's
+//             tensor scale (0 for a token that did not pick the expert, 1 x
+//             scale for the shared expert).
 //  k_moe_down Each workgroup owns one 64-row group of the hidden size and a
 //             share of the (slot, chunk) tiles of that row group over all the
 //             union's experts.  Each tile's dot products with the slot's h are
@@ -28,8 +30,9 @@
 //             tree, whose survivor writes Y.
 //
 // From M = 3 vectors on, the gate/up half runs on the matrix cores instead:
-// k_moe_route (one workgroup) routes the tokens once and writes the tables, then
-// the matrix-core product (gemv_mfma.hpp) takes each slot's expert from them, and
+// k_moe_route (one workgroup; the union through an LDS bitmap) routes the
+// tokens once and writes the tables, then the matrix-core product
+// (gemv_mfma.hpp) takes each slot's expert from them, and
 // k_moe_down follows as above; from M = 5 on the down half also runs on the
 // matrix-core kernel (its down mode).  Measured crossovers set both thresholds.
 // Verify blocks of 9..16 tokens (feed, "DFlash2: drafting a block in one pass":
@@ -79,6 +82,9 @@ constexpr int kMoeMfmaUnitsDn = 8;  // and plain products (at most)
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 8;
+// k_moe_down (up to kMoeMfmaDnMinM - 1 vectors) holds the slot table in one
+// register per lane
+static_assert((kMoeMfmaDnMinM - 1) * kMaxTopK + 1 < 64, "slot table exceeds a wave");
 
 struct MoeParams {
   const uint8_t *gate, *up, *down;  // routed expert 0; expert e at + e * stride
@@ -114,86 +120,206 @@ struct RouteLds {
   int n_slots;
 };
 
+// Compare-exchange for a descending order of 64-bit pick keys.
+__device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
+  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// The K picks of token m from its logits, one wave, E <= 512: each lane holds
+// the pick keys of experts lane + 64 t (t < 8), sorted descending by a 19-
+// comparator network, so the lane's best remaining key is always key[0].  A
+// pick is the wave maximum of the lanes' heads: first of the high words (the
+// logit's order) by DPP; when exactly one lane holds that value (the usual
+// case) it is the winner, otherwise the full 64-bit maximum breaks the tie by
+// the lower expert index.  The winner drops its head.
+template <int M>
+__device__ __forceinline__ void pick_sorted(const MoeParams& p, RouteLds<M>& r, int m, int lane, int npick,
+                                            float& myv, float& v0) {
+  const float* lg = p.logits + (int64_t)m * p.E;
+  uint64_t k[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int e = lane + 64 * t;
+    k[t] = e < p.E ? pick_key(lg[e], e) : 0ull;
+  }
+  cas_desc(k[0], k[2]); cas_desc(k[1], k[3]); cas_desc(k[4], k[6]); cas_desc(k[5], k[7]);
+  cas_desc(k[0], k[4]); cas_desc(k[1], k[5]); cas_desc(k[2], k[6]); cas_desc(k[3], k[7]);
+  cas_desc(k[0], k[1]); cas_desc(k[2], k[3]); cas_desc(k[4], k[5]); cas_desc(k[6], k[7]);
+  cas_desc(k[2], k[4]); cas_desc(k[3], k[5]);
+  cas_desc(k[1], k[4]); cas_desc(k[3], k[6]);
+  cas_desc(k[1], k[2]); cas_desc(k[3], k[4]); cas_desc(k[5], k[6]);
+  for (int j = 0; j < npick; ++j) {
+    const uint32_t hi = (uint32_t)(k[0] >> 32);
+    const uint32_t top = wave_max_u32(hi);
+    const uint64_t tie = __ballot(hi == top);
+    uint64_t best;
+    if (__popcll(tie) == 1) {
+      const int w = __ffsll((unsigned long long)tie) - 1;
+      // readlane returns int: widen it as unsigned, or the low word's top bit
+      // (always set: it holds 0xffffffff - e) would fill the high word
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)k[0], w);
+      best = ((uint64_t)top << 32) | lo;
+    } else {
+      best = wave_max_key(hi == top ? k[0] : 0ull);
+    }
+    if (k[0] == best) {
+#pragma unroll
+      for (int t = 0; t < 7; ++t) k[t] = k[t + 1];
+      k[7] = 0ull;
+    }
+    const float bv = key_value(best);
+    if (j == 0) v0 = bv;  // picks come in descending order
+    if (lane == j) myv = bv;
+    if (lane == 0) {
+      r.ids[m][j] = key_index(best);
+      r.v[m][j] = bv;
+    }
+  }
+}
+
+// The same for up to 1024 experts (16 keys per lane): each pick takes the lane
+// maximum over its keys, then the wave maximum, and clears the picked key.
+template <int M>
+__device__ __forceinline__ void pick_scan(const MoeParams& p, RouteLds<M>& r, int m, int lane, int npick,
+                                          float& myv, float& v0) {
+  const float* lg = p.logits + (int64_t)m * p.E;
+  constexpr int kPer = kMaxExperts / 64;
+  const int per_lane = (p.E + 63) / 64;
+  uint64_t key[kPer];
+#pragma unroll
+  for (int t = 0; t < kPer; ++t) {
+    const int e = lane + 64 * t;
+    key[t] = (t < per_lane && e < p.E) ? pick_key(lg[e], e) : 0ull;
+  }
+  for (int j = 0; j < npick; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int t = 1; t < kPer; ++t) best = key[t] > best ? key[t] : best;
+    best = wave_max_key(best);
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) key[t] = key[t] == best ? 0ull : key[t];
+    const float bv = key_value(best);
+    if (j == 0) v0 = bv;
+    if (lane == j) myv = bv;
+    if (lane == 0) {
+      r.ids[m][j] = key_index(best);
+      r.v[m][j] = bv;
+    }
+  }
+}
+
 // All NW * 64 threads: route the M tokens into `r` (ids, weights, sorted union).
+// One wave per token picks and takes the softmax over its K picks; the union of
+// the M x K picks, in ascending expert id, is ranked lane-parallel for one or
+// two tokens (each pick's rank among the distinct smaller ids: two loops over
+// the picks), else counted through a bitmap in LDS.
 template <int M, int NW>
 __device__ void route_tokens(const MoeParams& p, RouteLds<M>& r) {
+  constexpr bool kByRank = M <= 2;  // measured: the rank loops cost ~45 ns per pick, the bitmap ~1 us in all
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int words = (p.E + 31) / 32;
-  for (int i = threadIdx.x; i < words; i += NW * 64) r.bits[i] = 0u;
-  const int per_lane = (p.E + 63) / 64;  // <= 16
+  if constexpr (!kByRank)
+    for (int i = threadIdx.x; i < words; i += NW * 64) r.bits[i] = 0u;
   for (int m = wave; m < M; m += NW) {
-    const float* lg = p.logits + (int64_t)m * p.E;
-    // the lane's pick keys (experts lane + 64 t) in registers, from one load
-    // round trip; a picked key becomes 0
-    constexpr int kPer = kMaxExperts / 64;
-    uint64_t key[kPer];
-#pragma unroll
-    for (int t = 0; t < kPer; ++t) {
-      const int e = lane + 64 * t;
-      key[t] = (t < per_lane && e < p.E) ? pick_key(lg[e], e) : 0ull;
-    }
-    const bool wide = per_lane > kPer / 2;  // uniform: more than 512 experts
-    float myv = 0.0f, v0 = 0.0f;           // lane j < K: the logit of pick j; the largest
-    for (int j = 0; j < p.K; ++j) {
-      uint64_t best = key[0];
-#pragma unroll
-      for (int t = 1; t < kPer / 2; ++t) best = key[t] > best ? key[t] : best;
-      if (wide) {
-#pragma unroll
-        for (int t = kPer / 2; t < kPer; ++t) best = key[t] > best ? key[t] : best;
-      }
-      best = wave_max_key(best);
-#pragma unroll
-      for (int t = 0; t < kPer; ++t) key[t] = key[t] == best ? 0ull : key[t];
-      const float bv = key_value(best);
-      if (j == 0) v0 = bv;  // picks come in descending order
-      if (lane == j) myv = bv;
-      if (lane == 0) {
-        r.ids[m][j] = key_index(best);
-        r.v[m][j] = bv;
-      }
-    }
-    // softmax over the K picks, one pick per lane (lanes 0..7; K <= 8): the sum
-    // of the exponentials by a butterfly over those lanes
+    float myv = 0.0f, v0 = 0.0f;  // lane j < K: the logit of pick j; the largest
+    if (p.E <= 512)
+      pick_sorted<M>(p, r, m, lane, p.K, myv, v0);
+    else
+      pick_scan<M>(p, r, m, lane, p.K, myv, v0);
+    // softmax over the K picks, one pick per lane (lanes 0..7; K <= 8): the sum of
+    // the exponentials by three DPP steps into lane 7
     const float ej = lane < p.K ? expf(myv - v0) : 0.0f;
-    float z = ej;
-    z += __shfl_xor(z, 1, 64);
-    z += __shfl_xor(z, 2, 64);
-    z += __shfl_xor(z, 4, 64);
+    const float z = wave_sum8(ej);
     if (lane < p.K) r.w[m][lane] = ej / z;
   }
   __syncthreads();
-  if (threadIdx.x < M * p.K) {
-    const int m = threadIdx.x / p.K, j = threadIdx.x % p.K;
-    const int e = r.ids[m][j];
-    atomicOr(&r.bits[e >> 5], 1u << (e & 31));
+  if constexpr (kByRank) {
+    if (wave == 0) {
+      const int n = M * p.K;
+      const int id = lane < n ? r.ids[lane / p.K][lane % p.K] : 0x7fffffff;
+      // the first pick of its expert (for M = 1 the picks are distinct already;
+      // checked anyway, so that every slot below n_slots is written whatever
+      // the picks hold)
+      bool first = lane < n;
+      for (int i = 0; i < n; ++i) {
+        const int o = __builtin_amdgcn_readlane(id, i);
+        first = first && !(i < lane && o == id);
+      }
+      const uint64_t fm = __ballot(first);
+      int rank = 0;
+      for (int i = 0; i < n; ++i) {
+        const int o = __builtin_amdgcn_readlane(id, i);
+        rank += (((fm >> i) & 1ull) != 0 && o < id) ? 1 : 0;
+      }
+      if (first) r.uni[rank] = id;
+      const int nd = __popcll(fm);
+      if (lane == 0) {
+        if (p.has_shared) r.uni[nd] = -1;
+        r.n_slots = nd + (p.has_shared ? 1 : 0);
+      }
+    }
+  } else {
+    if (threadIdx.x < M * p.K) {
+      const int m = threadIdx.x / p.K, j = threadIdx.x % p.K;
+      const int e = r.ids[m][j];
+      atomicOr(&r.bits[e >> 5], 1u << (e & 31));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // ascending expert ids: exclusive scan of the words' popcounts over the lanes
+      int base = 0;
+      for (int w0 = 0; w0 < words; w0 += 64) {
+        const unsigned word = (w0 + lane < words) ? r.bits[w0 + lane] : 0u;
+        const int c = __popc(word);
+        int incl = c;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int o = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += o;
+        }
+        int pos = base + incl - c;
+        unsigned wd = word;
+        while (wd) {
+          const int b = __ffs(wd) - 1;
+          wd &= wd - 1;
+          r.uni[pos++] = (w0 + lane) * 32 + b;
+        }
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) {
+        if (p.has_shared) r.uni[base] = -1;
+        r.n_slots = base + (p.has_shared ? 1 : 0);
+      }
+    }
   }
   __syncthreads();
-  if (wave == 0) {
-    // ascending expert ids: exclusive scan of the words' popcounts over the lanes
-    int base = 0;
-    for (int w0 = 0; w0 < words; w0 += 64) {
-      const unsigned word = (w0 + lane < words) ? r.bits[w0 + lane] : 0u;
-      const int c = __popc(word);
-      int incl = c;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      int pos = base + incl - c;
-      unsigned wd = word;
-      while (wd) {
-        const int b = __ffs(wd) - 1;
-        wd &= wd - 1;
-        r.uni[pos++] = (w0 + lane) * 32 + b;
-      }
-      base += __shfl(incl, 63, 64);
+}
+
+// One token's routing in pick order (k_moe_up at M = 1): slot j is the j-th
+// pick (largest logit first), slot K the shared expert, so a gate/up unit of
+// slot j needs only the first j + 1 picks and the shared slot none.  Wave 0
+// makes `npick` picks; with `weights` (npick = K) it also takes the softmax.
+template <int M>
+__device__ void route_by_pick(const MoeParams& p, RouteLds<M>& r, int npick, bool weights) {
+  const int lane = threadIdx.x & 63;
+  if (wave_id() == 0 && npick > 0) {
+    float myv = 0.0f, v0 = 0.0f;
+    if (p.E <= 512)
+      pick_sorted<M>(p, r, 0, lane, npick, myv, v0);
+    else
+      pick_scan<M>(p, r, 0, lane, npick, myv, v0);
+    if (weights) {
+      const float ej = lane < p.K ? expf(myv - v0) : 0.0f;
+      const float z = wave_sum8(ej);
+      if (lane < p.K) r.w[0][lane] = ej / z;
     }
-    if (lane == 0) {
-      if (p.has_shared) r.uni[base] = -1;
-      r.n_slots = base + (p.has_shared ? 1 : 0);
-    }
+    if (lane < npick) r.uni[lane] = r.ids[0][lane];
+  }
+  if (threadIdx.x == 0) {
+    if (p.has_shared) r.uni[p.K] = -1;
+    r.n_slots = p.K + (p.has_shared ? 1 : 0);
   }
   __syncthreads();
 }
@@ -237,21 +363,18 @@ __global__ __launch_bounds__(route_waves<M>() * 64) void k_moe_route(MoeParams p
   write_route_tables<M, route_waves<M>()>(p, r);
 }
 
-template <uint32_t FMT, int M, int NW>
-__global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
+// Gate/up of unit `blk` = (slot, 64-row group, K split) of the union, after the
+// workgroup routed the tokens into r.  BY_PICK: the slots are in pick order
+// (one token), so slot j's intermediate is column j of H.
+template <uint32_t FMT, int M, int NW, bool BY_PICK>
+__device__ __forceinline__ void moe_up_unit(const MoeParams& p, const RouteLds<M>& r, int blk,
+                                            float (&red)[NW][2 * M][64]) {
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : kTileMx;
-  constexpr int NA = 2 * M;
-  __shared__ RouteLds<M> r;
-  __shared__ float red[NW][NA][64];
-  route_tokens<M, NW>(p, r);
-
   const int lane = threadIdx.x & 63, wave = wave_id();
-  if (blockIdx.x == 0) write_route_tables<M, NW>(p, r);
-
   const int per_slot = p.Rg * p.S_up;
-  const int slot = uniform(blockIdx.x / per_slot);
+  const int slot = uniform(blk / per_slot);
   if (slot >= r.n_slots) return;
-  const int rem = blockIdx.x % per_slot;
+  const int rem = blk % per_slot;
   const int g = uniform(rem / p.S_up), s = uniform(rem % p.S_up);
   const int e = r.uni[slot];
   const uint8_t* wg_ = e >= 0 ? p.gate + (uint64_t)e * p.sg : p.sh_gate;
@@ -316,21 +439,45 @@ __global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
   const int row = g * 64 + lane;
   exchange_tree<M>(p.x_up, (int64_t)p.n_slots_max * p.Rg * 64, ((int64_t)slot * p.Rg + g) * 64 + lane, p.S_up, s,
                    ua, ub, live);
-  if (row >= p.dff) return;
-  const int nh = p.K + p.has_shared;
+  if (row < p.dff) {
+    const int nh = p.K + p.has_shared;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (!live[m]) continue;
-    const uint16_t h = f32_to_bf16_rne(silu_f32(ua[m] * tsg) * (ub[m] * tsu));
-    p.hbuf[((int64_t)slot * M + m) * p.dff + row] = h;
-    if (p.hdbg) {
-      if (e < 0) {
-        p.hdbg[((int64_t)m * nh + p.K) * p.dff + row] = h;
-      } else {
-        for (int j = 0; j < p.K; ++j)
-          if (r.ids[m][j] == e) p.hdbg[((int64_t)m * nh + j) * p.dff + row] = h;
+    for (int m = 0; m < M; ++m) {
+      if (!live[m]) continue;
+      const uint16_t h = f32_to_bf16_rne(silu_f32(ua[m] * tsg) * (ub[m] * tsu));
+      p.hbuf[((int64_t)slot * M + m) * p.dff + row] = h;
+      if (p.hdbg) {
+        if (BY_PICK) {
+          p.hdbg[(int64_t)slot * p.dff + row] = h;  // slot j = pick j, the shared slot last
+        } else if (e < 0) {
+          p.hdbg[((int64_t)m * nh + p.K) * p.dff + row] = h;
+        } else {
+          for (int j = 0; j < p.K; ++j)
+            if (r.ids[m][j] == e) p.hdbg[((int64_t)m * nh + j) * p.dff + row] = h;
+        }
       }
     }
+  }
+}
+
+template <uint32_t FMT, int M, int NW>
+__global__ __launch_bounds__(NW * 64) void k_moe_up(MoeParams p) {
+  __shared__ RouteLds<M> r;
+  __shared__ float red[NW][2 * M][64];
+  if constexpr (M == 1) {
+    // slots in pick order: slot j needs the first j + 1 picks, the shared slot
+    // none; the first unit of the last routed slot makes all K picks and writes
+    // the tables
+    const int per_slot = p.Rg * p.S_up;
+    const int slot = uniform(blockIdx.x / per_slot);
+    const bool tables = blockIdx.x == (p.K - 1) * per_slot;
+    route_by_pick<M>(p, r, slot < p.K ? slot + 1 : 0, tables);
+    if (tables) write_route_tables<M, NW>(p, r);
+    moe_up_unit<FMT, M, NW, true>(p, r, blockIdx.x, red);
+  } else {
+    route_tokens<M, NW>(p, r);
+    if (blockIdx.x == 0) write_route_tables<M, NW>(p, r);
+    moe_up_unit<FMT, M, NW, false>(p, r, blockIdx.x, red);
   }
 }
 
@@ -339,7 +486,10 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down(MoeParams p) {
   constexpr int TILE = FMT == FP4G_NVFP4 ? kTileNv : kTileMx;
   __shared__ float red[NW][M][64];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int n_slots = uniform(p.route[0]);
+  // the slot table in one round trip: lane i holds route[i] (the slot count,
+  // then the slots' experts)
+  const int rt = lane <= p.n_slots_max ? p.route[lane] : 0;
+  const int n_slots = __builtin_amdgcn_readfirstlane(rt);
   const int g = uniform(blockIdx.x / p.S_dn), s = uniform(blockIdx.x % p.S_dn);
   // this workgroup's share of the row group's (slot, chunk) tiles, then the wave's
   const int total = n_slots * p.Cd;
@@ -354,7 +504,7 @@ __global__ __launch_bounds__(NW * 64) void k_moe_down(MoeParams p) {
   for (int m = 0; m < M; ++m) acc[m] = 0.0f;
   auto tile_of = [&](int it) {
     const int q = i0 + it, slot = q / p.Cd, c = q - slot * p.Cd;
-    const int e = p.route[1 + slot];
+    const int e = __builtin_amdgcn_readlane(rt, 1 + slot);
     const uint8_t* wd = e >= 0 ? p.down + (uint64_t)e * p.sd : p.sh_down;
     return wd + (tile0 + c) * TILE;
   };
@@ -409,20 +559,22 @@ struct MoeLayout {
   int n_slots_max;
   int64_t Rg, Cg, Rd, Cd;
   Plan up, dn;
+  uint32_t gate_fmt;
   uint64_t off_route, off_coef, off_hbuf, off_x_up, off_x_dn, total;
 };
 
 // Both kernels stream a few thousand tiles at most and are bound by each wave's
-// chain of round trips (routing, loads, tree): latency plans.  The routing code
-// takes k_moe_up past 128 VGPRs (12 waves per CU): workgroups of 4, 8 or 12
-// waves.  k_moe_down fits 16 waves per CU up to M = 5, like the dense kernel.
-constexpr int kUpWavesPerCu = 12;
-inline Plan plan_up(int64_t R, int64_t C) { return plan_latency(R, C, kUpWavesPerCu, {4, 8, 12}); }
+// chain of round trips (routing, loads, tree): latency plans.  k_moe_up holds
+// two tiles in flight plus the routing state, up to 170 VGPRs (12 waves per CU:
+// workgroups of 4, 8 or 12 waves; at M = 2 the 12-wave form spills a few
+// registers and is still the fastest measured).  k_moe_down fits 16 waves per
+// CU up to M = 5, like the dense kernel.
+inline Plan plan_up(int64_t R, int64_t C, int M) { return plan_latency(R, C, 12, {4, 8, 12}); }
 inline Plan plan_dn(int64_t R, int64_t C, int M) { return plan_latency(R, C, M <= 5 ? 16 : 12, {4, 8, 16}); }
 // gate/up plan and exchange units per lane for M vectors (either kernel; the
 // W4A8 path always runs on the matrix cores, planned like the bf16 ones)
 inline Plan plan_gu(int64_t R, int64_t C, int M, bool a8) {
-  return a8 || M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C);
+  return a8 || M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C, M);
 }
 inline int units_gu(int M, bool a8) { return a8 || M >= kMoeMfmaMinM ? kMoeMfmaUnits : M; }
 // down plan and units: C counts the union's slots x d_ff chunks
@@ -430,6 +582,7 @@ inline Plan plan_down(int64_t R, int64_t C, int M, bool a8) {
   return a8 || M >= kMoeMfmaDnMinM ? plan_mfma(R, C, 1, M) : plan_dn(R, C, M);
 }
 inline int units_dn(int M, bool a8) { return a8 || M >= kMoeMfmaDnMinM ? kMoeMfmaUnitsDn : (M + 1) / 2; }
+
 
 // Workspace: exchange slots first, sized for the largest need over M = 1..16
 // (they must start zero-filled and every call leaves them zero), then the
@@ -443,6 +596,7 @@ int n_slots_for(const fp4g_moe* mo, int M) {
 MoeLayout moe_layout(const fp4g_moe* mo, int M) {
   MoeLayout L{};
   L.n_slots_max = n_slots_for(mo, M);
+  L.gate_fmt = mo->gate.format;
   L.Rg = row_groups(mo->d_ff);
   L.Cg = chunks(mo->hidden);
   L.Rd = row_groups(mo->hidden);
@@ -511,8 +665,10 @@ struct MoeMfma {
 };
 
 template <uint32_t FMT, int M>
-hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const Plan& up, const Plan& dn, unsigned grid_up,
+hipError_t launch_moe_m(const MoeParams& p, const MoeMfma& mf, const MoeLayout& L, unsigned grid_up,
                         unsigned grid_dn, hipStream_t s) {
+  const Plan& up = L.up;
+  const Plan& dn = L.dn;
   if constexpr (M >= kMoeMfmaMinM) {
     k_moe_route<M><<<1, route_waves<M>() * 64, 0, s>>>(p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
@@ -570,12 +726,12 @@ hipError_t launch_moe_a8(int M, const MoeParams& p, const MoeMfma& mf, unsigned 
 }
 
 template <uint32_t FMT>
-hipError_t launch_moe(int M, const MoeParams& p, const MoeMfma& mf, const Plan& up, const Plan& dn, unsigned grid_up,
+hipError_t launch_moe(int M, const MoeParams& p, const MoeMfma& mf, const MoeLayout& L, unsigned grid_up,
                       unsigned grid_dn, hipStream_t s) {
   switch (M) {
 #define FP4G_CASE(MM) \
   case MM:            \
-    return launch_moe_m<FMT, MM>(p, mf, up, dn, grid_up, grid_dn, s);
+    return launch_moe_m<FMT, MM>(p, mf, L, grid_up, grid_dn, s);
     FP4G_CASE(1) FP4G_CASE(2) FP4G_CASE(3) FP4G_CASE(4) FP4G_CASE(5) FP4G_CASE(6) FP4G_CASE(7) FP4G_CASE(8)
     FP4G_CASE(9) FP4G_CASE(10) FP4G_CASE(11) FP4G_CASE(12) FP4G_CASE(13) FP4G_CASE(14) FP4G_CASE(15) FP4G_CASE(16)
 #undef FP4G_CASE
@@ -590,13 +746,20 @@ uint64_t moe_ws_bytes(const fp4g_moe* mo, int M) {
   return moe_layout(mo, M).total;
 }
 
-}  // namespace fp4g
+namespace {
 
-using namespace fp4g;
+// One call's checked parameters: kernel arguments, plans and grids.
+struct MoeCall {
+  MoeParams p;
+  MoeMfma mf;
+  MoeLayout L;
+  unsigned grid_up, grid_dn;
+  bool a8;
+};
 
-extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const float* logits, int32_t M, float* Y,
-                                  int32_t* topk_ids, float* topk_w, uint16_t* H, void* ws, uint64_t ws_bytes,
-                                  void* stream) {
+// Host checks of moe_route_gemv and the set-up of its launches.
+fp4g_status moe_prepare(const fp4g_moe* mo, const uint16_t* X, const float* logits, int32_t M, float* Y,
+                        int32_t* topk_ids, float* topk_w, uint16_t* H, void* ws, uint64_t ws_bytes, MoeCall& c) {
   fp4g_status st = check_moe(mo);
   if (st != FP4G_OK) return st;
   if (!X || !logits || !Y || !topk_ids || !topk_w || !ws) return FP4G_E_NULL;
@@ -604,7 +767,8 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   if (!aligned(X, 16) || !aligned(logits, 16) || !aligned(Y, 16) || !aligned(topk_ids, 16) ||
       !aligned(topk_w, 16) || (H && !aligned(H, 16)))
     return FP4G_E_ALIGN;
-  const MoeLayout L = moe_layout(mo, M);
+  c.L = moe_layout(mo, M);
+  const MoeLayout& L = c.L;
   if (ws_bytes < L.total) return FP4G_E_WORKSPACE;
   if (!aligned(ws, 256)) return FP4G_E_ALIGN;
   const int nh = mo->top_k + mo->has_shared;
@@ -625,7 +789,8 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
          overlap(outs[i], outb[i], mo->sh_down.packed, mo->sh_down.packed_bytes)))
       return FP4G_E_ALIAS;
   }
-  MoeParams p{};
+  c.p = MoeParams{};
+  MoeParams& p = c.p;
   p.gate = (const uint8_t*)mo->gate.packed;
   p.up = (const uint8_t*)mo->up.packed;
   p.down = (const uint8_t*)mo->down.packed;
@@ -668,10 +833,12 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
   p.Rd = (int)L.Rd;
   p.Cd = (int)L.Cd;
   p.S_dn = L.dn.S;
-  const unsigned grid_up = (unsigned)(L.n_slots_max * L.Rg * L.up.S);
-  const unsigned grid_dn = (unsigned)(L.Rd * L.dn.S);
-  const bool a8 = mo->act == FP4G_ACT_MXFP8;
-  MoeMfma mf{};
+  c.grid_up = (unsigned)(L.n_slots_max * L.Rg * L.up.S);
+  c.grid_dn = (unsigned)(L.Rd * L.dn.S);
+  const unsigned grid_up = c.grid_up;
+  const bool a8 = c.a8 = mo->act == FP4G_ACT_MXFP8;
+  c.mf = MoeMfma{};
+  MoeMfma& mf = c.mf;
   if (a8 || M >= kMoeMfmaMinM) {
     GemvParams& gp = mf.gp;
     gp.n = 1;
@@ -726,10 +893,25 @@ extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const f
     qd.dff = mo->d_ff;
     mf.lds_d = a8 ? a8_lds_bytes(L.dn, M, 1) : mfma_lds_bytes(L.dn, mo->gate.format, 1, M);
   }
-  hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = a8 ? launch_moe_a8(M, p, mf, grid_up, grid_dn, s)
-                       : mo->gate.format == FP4G_NVFP4
-                           ? launch_moe<FP4G_NVFP4>(M, p, mf, L.up, L.dn, grid_up, grid_dn, s)
-                           : launch_moe<FP4G_MXFP4>(M, p, mf, L.up, L.dn, grid_up, grid_dn, s);
-  return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
+  return FP4G_OK;
+}
+
+hipError_t moe_launch(int M, const MoeCall& c, hipStream_t s) {
+  if (c.a8) return launch_moe_a8(M, c.p, c.mf, c.grid_up, c.grid_dn, s);
+  return c.L.gate_fmt == FP4G_NVFP4 ? launch_moe<FP4G_NVFP4>(M, c.p, c.mf, c.L, c.grid_up, c.grid_dn, s)
+                                    : launch_moe<FP4G_MXFP4>(M, c.p, c.mf, c.L, c.grid_up, c.grid_dn, s);
+}
+
+}  // namespace
+}  // namespace fp4g
+
+using namespace fp4g;
+
+extern "C" int32_t moe_route_gemv(const fp4g_moe* mo, const uint16_t* X, const float* logits, int32_t M, float* Y,
+                                  int32_t* topk_ids, float* topk_w, uint16_t* H, void* ws, uint64_t ws_bytes,
+                                  void* stream) {
+  MoeCall c;
+  const fp4g_status st = moe_prepare(mo, X, logits, M, Y, topk_ids, topk_w, H, ws, ws_bytes, c);
+  if (st != FP4G_OK) return st;
+  return moe_launch(M, c, (hipStream_t)stream) == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }

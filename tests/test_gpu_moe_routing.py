@@ -1,0 +1,62 @@
+"""MoE routing on the gate/up kernel of M = 1, 2 (every workgroup routes the
+tokens itself; at M = 1 the slots follow the pick order and each workgroup picks
+only as far as its own slot): ties, expert counts on both pick paths (up to 512
+experts: sorted keys per lane; above: a scan per pick), a single pick, and
+repeated calls on one workspace.  Parity as in test_gpu_parity: ids exact,
+stage-wise bounds against the FP64 oracle."""
+import pytest
+import torch
+
+import bit_weight_gemv_fp4_amd as fg
+import datagen
+from gpu_common import DEV, build_moe, check_moe, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_routing_ties(M):
+    """Equal logits (zeros of both signs, repeated values): lower expert index first."""
+    log("routing ties", M)
+    layer, expert, sh = build_moe(fg.MXFP4, 16, 4, 256, 128, seed=21)
+    X = datagen.bf16_normal((M, 256), datagen.tensor_seed("ftx", M), device=DEV)
+    logits = torch.zeros((M, 16), dtype=torch.float32, device=DEV)
+    logits[0, 3] = -0.0
+    logits[0, 9] = 0.75
+    if M > 1:
+        logits[1] = torch.tensor([0.5, -1, 0.5, 0.25] * 4, device=DEV)
+    ids = check_moe(layer, expert, sh, X, logits, 4)
+    assert ids[0].tolist() == [9, 0, 1, 2]
+    if M > 1:
+        assert ids[1].tolist() == [0, 2, 4, 6]
+
+
+@pytest.mark.parametrize("E,k", [(100, 8), (512, 1), (640, 8), (1024, 6)])
+@pytest.mark.parametrize("M", [1, 2])
+def test_routing_expert_counts(E, k, M):
+    """Partial last lane of keys (100), a single pick, and the scan path above 512."""
+    log("routing experts", E, k, M)
+    layer, expert, sh = build_moe(fg.MXFP4, E, k, 256, 128, seed=22)
+    X = datagen.bf16_normal((M, 256), datagen.tensor_seed("fex", E, k, M), device=DEV)
+    logits = datagen.router_logits(M, E, datagen.tensor_seed("fel", E, k, M), device=DEV)
+    check_moe(layer, expert, sh, X, logits, k)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_config5_repeated_calls(M):
+    """The C5 layer three times in a row on one workspace, new inputs each time."""
+    log("C5 repeat", M)
+    layer, expert, sh = build_moe(fg.MXFP4, 512, 8, 2560, 768, seed=23)
+    for rep in range(3):
+        X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("frx", M, rep), device=DEV)
+        logits = datagen.router_logits(M, 512, datagen.tensor_seed("frl", M, rep), device=DEV)
+        check_moe(layer, expert, sh, X, logits, 8)
+
+
+def test_no_shared_expert_pick_order():
+    """M = 1 without a shared expert: the slots are exactly the K picks."""
+    log("no shared, M = 1")
+    layer, expert, sh = build_moe(fg.MXFP4, 64, 8, 256, 128, seed=25, shared=False)
+    X = datagen.bf16_normal((1, 256), 251, device=DEV)
+    logits = datagen.router_logits(1, 64, 252, device=DEV)
+    check_moe(layer, expert, sh, X, logits, 8)
