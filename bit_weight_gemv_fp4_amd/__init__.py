@@ -79,6 +79,7 @@ _SIGNATURES = {
     "fp4g_quantize": (_I32, [_U32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _U64, _VP]),
     "fp4g_validate": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP]),
     "fp4g_workspace_bytes": (_U64, [_I32, _VP, _I32]),
+    "fp4g_workspace_check": (_I32, [_I32, _VP, _I32, _VP, _U64, ctypes.POINTER(_U64), _VP]),
     "fp4_gemv": (_I32, [ctypes.POINTER(WeightDesc), _VP, _VP, _VP, _U64, _VP]),
     "fp4_skinny_gemm": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32, _VP, _U64, _VP]),
     "fp4_skinny_gemm_noalloc": (_I32, [ctypes.POINTER(WeightDesc), _VP, _I32, _VP, _I32, _VP]),
@@ -244,6 +245,16 @@ def validate(W: PackedWeight, stream=None) -> int:
 def workspace_bytes(op: int, desc, M: int) -> int:
     d = desc.desc if isinstance(desc, (PackedWeight, MoeLayer, Group)) else desc
     return lib().fp4g_workspace_bytes(op, ctypes.addressof(d), M)
+
+
+def workspace_check(op: int, desc, M: int, ws: torch.Tensor, stream=None) -> int:
+    """Non-zero 8-byte words in the part of `ws` the call (op, desc, M) needs
+    zero-filled (0: the workspace may be used).  Synchronises the stream."""
+    d = desc.desc if isinstance(desc, (PackedWeight, MoeLayer, Group)) else desc
+    n = ctypes.c_uint64(0)
+    _check(lib().fp4g_workspace_check(op, ctypes.addressof(d), M, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                      ctypes.byref(n), _stream(stream)), "fp4g_workspace_check")
+    return int(n.value)
 
 
 _ws_cache: dict = {}

@@ -173,5 +173,6 @@ fp4g_status check_weight(const fp4g_weight* w, bool want_fp4);
 
 // Workspace bytes of moe_route_gemv (0 for invalid arguments).
 uint64_t moe_ws_bytes(const fp4g_moe* mo, int M);
+uint64_t moe_slot_bytes(const fp4g_moe* mo);  // the part of that workspace that must start zero
 
 }  // namespace fp4g

@@ -87,6 +87,46 @@ static fp4g_status static_scratch(void* stream, void** out) {
   return FP4G_OK;
 }
 
+// ---- workspace check ----------------------------------------------------------------
+// One workgroup counts the non-zero 8-byte words of a region into a device word
+// of the library's own (a region of a few MiB takes well under a millisecond).
+static __device__ unsigned long long ws_check_total;
+static void* g_check_ptr[kMaxDevices];
+
+__global__ __launch_bounds__(1024) void k_count_nonzero(const unsigned long long* __restrict__ w, uint64_t n,
+                                                        unsigned long long* out) {
+  __shared__ unsigned long long part[16];
+  unsigned long long c = 0;
+  for (uint64_t i = threadIdx.x; i < n; i += 1024) c += w[i] != 0ull ? 1ull : 0ull;
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_down(c, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long t = 0;
+    for (int i = 0; i < 16; ++i) t += part[i];
+    *out = t;
+  }
+}
+
+static fp4g_status check_total_ptr(void* stream, void** out) {
+  int cur = 0, dev = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return FP4G_E_HIP;
+  dev = cur;
+  if (stream && hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) return FP4G_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FP4G_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_check_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return FP4G_E_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(ws_check_total));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return FP4G_E_HIP;
+    g_check_ptr[dev] = p;
+  }
+  *out = g_check_ptr[dev];
+  return FP4G_OK;
+}
+
 // Validation + launch of n products of one input (n = 1: fp4_gemv,
 // fp4_skinny_gemm, fp8_lmhead_gemv).  Members share format and d_in.
 // use_static: take the library's scratch array instead of (ws, ws_bytes).
@@ -359,6 +399,24 @@ int32_t fp4_gate_up_silu(const fp4g_weight* Wg, const fp4g_weight* Wu, const uin
   else
     e = launch_m<FP4G_FP8_ROW, 2, EPI_SILU>(M, pl.nw, p, grid, s);
   return e == hipSuccess ? FP4G_OK : FP4G_E_HIP;
+}
+
+int32_t fp4g_workspace_check(int32_t op, const void* desc, int32_t M, const void* ws, uint64_t ws_bytes,
+                             uint64_t* nonzero, void* stream) {
+  if (!desc || !ws || !nonzero) return FP4G_E_NULL;
+  const uint64_t need = fp4g_workspace_bytes(op, desc, M);
+  if (need == 0) return FP4G_E_SHAPE;
+  if (ws_bytes < need) return FP4G_E_WORKSPACE;
+  if (!aligned(ws, 256)) return FP4G_E_ALIGN;
+  const uint64_t region = op == FP4G_OP_MOE ? moe_slot_bytes((const fp4g_moe*)desc) : need;
+  void* total = nullptr;
+  const fp4g_status st = check_total_ptr(stream, &total);
+  if (st != FP4G_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  k_count_nonzero<<<1, 1024, 0, s>>>((const unsigned long long*)ws, region / 8, (unsigned long long*)total);
+  if (hipGetLastError() != hipSuccess) return FP4G_E_HIP;
+  if (hipMemcpyAsync(nonzero, total, sizeof(uint64_t), hipMemcpyDeviceToHost, s) != hipSuccess) return FP4G_E_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? FP4G_OK : FP4G_E_HIP;
 }
 
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc, int32_t M) {

@@ -746,6 +746,11 @@ uint64_t moe_ws_bytes(const fp4g_moe* mo, int M) {
   return moe_layout(mo, M).total;
 }
 
+uint64_t moe_slot_bytes(const fp4g_moe* mo) {
+  if (check_moe(mo) != FP4G_OK) return 0;
+  return moe_layout(mo, 1).off_route;  // the tables follow the slots
+}
+
 namespace {
 
 // One call's checked parameters: kernel arguments, plans and grids.

@@ -232,12 +232,18 @@ int32_t fp4g_pack(uint32_t format, int32_t d_out, int32_t d_in, const void* code
 int32_t fp4g_quantize(uint32_t format, int32_t d_out, int32_t d_in, const uint16_t* w_dev, void* codes_dev,
                       void* scales_dev, float* tensor_scale_dev, void* ws_dev, uint64_t ws_bytes, void* stream);
 
-/* Inverse of fp4g_pack: write the logical codes and scales of W. */
+/* Inverse of fp4g_pack: write the logical codes and scales of W (the formats as
+ * the pages define them: feed, section "Fewer bytes per weight: NVFP4"; Ling-3.0
+ * article, glossary (MXFP4) and sec. 7 (the FP8 output layer)).  A pure byte
+ * permutation, so a pack/unpack round trip is bit-exact. */
 int32_t fp4g_unpack(const fp4g_weight* W_host, void* codes_dev, void* scales_dev, void* stream);
 
 /* Count, into the device int64 at *bad_dev, the scale entries of W that are NaN
  * codes (E4M3 S.1111.111, E8M0 0xFF) or non-finite FP32 row scales.  Callers
- * check it once at load time; the product kernels never test scales. */
+ * check it once at load time; the product kernels never test scales.  (The
+ * Ling-3.0 article, sec. 11, describes weights silently taken in the wrong
+ * format and a service that only got slower; this check and the descriptors'
+ * format and layout tags are the guard against the same with bad scales.) */
 int32_t fp4g_validate(const fp4g_weight* W_host, int64_t* bad_dev, void* stream);
 
 /* --- workspace ---------------------------------------------------------------- */
@@ -245,22 +251,37 @@ int32_t fp4g_validate(const fp4g_weight* W_host, int64_t* bad_dev, void* stream)
 /* Bytes of device workspace the call `op` needs for descriptor `desc_host`
  * (fp4g_weight, fp4g_group or fp4g_moe, see fp4g_op) and M vectors; 0 means none
  * (then ws_dev may be NULL).  A call given less returns FP4G_E_WORKSPACE.  The
- * workspace holds split-K exchange slots, hand-off counters, routing tables and
- * partial sums.  The caller zero-fills a workspace once, before its first use;
- * every call leaves the slots and counters at zero again when its kernels
- * complete, so one zero-filled workspace (of the largest size needed) serves
- * calls of any shape.  moe_route_gemv is the exception: it also keeps its
+ * workspace holds split-K exchange slots, the greedy pick's running maxima and
+ * (moe_route_gemv) routing tables and intermediate vectors.  The caller
+ * zero-fills a workspace once, before its first use; every call leaves the slots
+ * and maxima at zero again when its kernels complete, so one zero-filled
+ * workspace (of the largest size needed) serves calls of any shape.  A slot
+ * left non-zero (a workspace never zero-filled, or a call interrupted, or two
+ * calls overlapping on it) would be taken as a partner's partial sum:
+ * fp4g_workspace_check finds such slots before a call.  moe_route_gemv is the exception: it also keeps its
  * routing tables and intermediate vectors in the workspace, after the slots, so
  * its workspace may be shared only by moe_route_gemv calls on layers of one
  * shape (any M), and by nothing else.  Calls that share a workspace must be
  * ordered on one stream.  Returns 0 also for invalid arguments. */
 uint64_t fp4g_workspace_bytes(int32_t op, const void* desc_host, int32_t M);
 
+/* Count, into *nonzero_host, the 8-byte words of the part of ws_dev that must
+ * be zero before the call (op, desc_host, M): the exchange slots and running
+ * maxima (for FP4G_OP_MOE the slots only, not the tables after them).  0 means
+ * the call may use the workspace; a caller that gets more must zero-fill it
+ * (or refuse the call).  Synchronises `stream`; meant for load time, tests and
+ * debugging, not for the decode loop.  Errors: FP4G_E_NULL, FP4G_E_SHAPE (no
+ * workspace needed, or a bad descriptor), FP4G_E_WORKSPACE (ws_bytes smaller
+ * than fp4g_workspace_bytes), FP4G_E_ALIGN (ws_dev not 256-B aligned). */
+int32_t fp4g_workspace_check(int32_t op, const void* desc_host, int32_t M, const void* ws_dev,
+                             uint64_t ws_bytes, uint64_t* nonzero_host, void* stream);
+
 /* --- products --------------------------------------------------------------- */
 
 /* y_dev[r] = sum_k w[r][k] * x_dev[k] for an NVFP4 or MXFP4 matrix (M = 1, the
- * batch-1 decode GEMV).  x_dev: bf16 bit patterns [d_in], 16-B aligned.
- * y_dev: f32 [d_out], 16-B aligned. */
+ * batch-1 decode GEMV whose speed is the bytes of W over the memory bandwidth:
+ * feed, section "Decode speed is bytes divided by bandwidth").  x_dev: bf16 bit
+ * patterns [d_in], 16-B aligned.  y_dev: f32 [d_out], 16-B aligned. */
 int32_t fp4_gemv(const fp4g_weight* W_host, const uint16_t* x_dev, float* y_dev, void* ws_dev,
                  uint64_t ws_bytes, void* stream);
 

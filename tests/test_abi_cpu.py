@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = fg.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -356,3 +356,23 @@ def test_workspace_queries():
     assert fg.MAX_M == 8 and fg.MAX_M_WIDE == 16
     bad = good_desc(); bad.layout_tag = 0
     assert fg.workspace_bytes(fg.OP_GEMV, bad, 1) == 0
+
+
+def test_workspace_check_error_paths():
+    """The workspace check refuses bad arguments before touching the device."""
+    L = fg.lib()
+    d = good_desc(fg.NVFP4, 5120, 17408)
+    need = L.fp4g_workspace_bytes(fg.OP_GEMV, ctypes.byref(d), 1)
+    assert need > 0
+    n = ctypes.c_uint64(7)
+    assert L.fp4g_workspace_check(fg.OP_GEMV, None, 1, FAKE, need, ctypes.byref(n), None) == E_NULL
+    assert L.fp4g_workspace_check(fg.OP_GEMV, ctypes.byref(d), 1, None, need, ctypes.byref(n), None) == E_NULL
+    assert L.fp4g_workspace_check(fg.OP_GEMV, ctypes.byref(d), 1, FAKE, need, None, None) == E_NULL
+    assert L.fp4g_workspace_check(fg.OP_GEMV, ctypes.byref(d), 1, FAKE, need - 8, ctypes.byref(n), None) == E_WORKSPACE
+    assert L.fp4g_workspace_check(fg.OP_GEMV, ctypes.byref(d), 1, FAKE + 16, need, ctypes.byref(n), None) == E_ALIGN
+    small = good_desc(fg.NVFP4, 64, 256)  # one tile column: no split-K, no workspace
+    assert L.fp4g_workspace_bytes(fg.OP_GEMV, ctypes.byref(small), 1) == 0
+    assert L.fp4g_workspace_check(fg.OP_GEMV, ctypes.byref(small), 1, FAKE, 256, ctypes.byref(n), None) == E_SHAPE
+    assert L.fp4g_workspace_check(fg.OP_MOE, ctypes.byref(moe_desc()), 17, FAKE, 1 << 30, ctypes.byref(n),
+                                  None) == E_SHAPE
+    assert n.value == 7  # untouched
