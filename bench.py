@@ -37,13 +37,15 @@ ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0
+HEAD_DRAFT_ROWS = 100032  # the draft head's reduced vocabulary: the leading rows of the FP8 head
 
 
-# The files the dense and FP8-row product kernels (and their launch planning) are
+# The files the NVFP4 and FP8-row product kernels (and their launch planning) are
 # built from; the committed counter summary is valid only while they are unchanged.
 TRAFFIC_SOURCES = ("bit_weight_gemv_fp4_amd/build.py", "bit_weight_gemv_fp4_amd/csrc/common.hpp",
                    "bit_weight_gemv_fp4_amd/csrc/gemv_kernel.hpp", "bit_weight_gemv_fp4_amd/csrc/gemv_mfma.hpp",
                    "bit_weight_gemv_fp4_amd/csrc/gemv.hip", "bit_weight_gemv_fp4_amd/csrc/gemv_nvfp4.hip",
+                   "bit_weight_gemv_fp4_amd/csrc/gemv_mfma_nvfp4.hip", "bit_weight_gemv_fp4_amd/csrc/gemv_mfma_nvfp4_silu.hip",
                    "bit_weight_gemv_fp4_amd/csrc/gemv_fp8.hip")
 
 
@@ -53,19 +55,32 @@ def traffic_sources_hash():
     return hashlib.sha256(b"".join((ROOT / q).read_bytes() for q in TRAFFIC_SOURCES)).hexdigest()[:16]
 
 
-def counter_traffic(kind):
-    """HBM bytes per launch of `kind` from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary (profiles/counters.json), or None when the kernel sources
-    have changed since the counters were taken."""
+def resolved_path(workload, path, M):
+    """The kernel path a workload's products take: 'valu' or 'mfma' for the
+    NVFP4/MXFP4 products of c4 and skinny ('auto': the matrix cores from M = 3
+    on), 'auto' where the workload has a single kernel choice."""
+    if workload not in ("c4", "skinny"):
+        return "auto"
+    if path == "auto":
+        return "valu" if M <= 2 else "mfma"
+    return path
+
+
+def counter_traffic(workload, M, path, fmt, kind):
+    """HBM bytes per launch of `kind` in this workload from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/counters.json): only for
+    the (workload, M, path, format) the counters were taken on, and only while
+    the kernel sources hash to the value recorded there; otherwise None."""
     p = ROOT / "profiles" / "counters.json"
     if not p.exists():
         return None
     d = json.loads(p.read_text())
-    h = traffic_sources_hash()
-    k = d.get("kernels", {}).get(kind)
-    if d.get("source_sha256_16") != h or not k:
+    if d.get("source_sha256_16") != traffic_sources_hash():
         return None
-    return round(k["fetch_bytes"] + k["write_bytes"])
+    for e in d.get("entries", []):
+        if (e["workload"], e["M"], e["path"], e["fmt"], e["kind"]) == (workload, M, path, fmt, kind):
+            return round(e["fetch_bytes"] + e["write_bytes"])
+    return None
 
 
 def parse():
@@ -308,7 +323,7 @@ def build_other(name, M, fg, datagen, torch, path=0, router=False, fmt=None):
     if name == "head":
         # the dense model's FP8 head: plain logits, fused greedy pick, and a draft
         # head over the leading 100032 rows (the reduced vocabulary)
-        V, DV = datagen.VOCAB, 100032
+        V, DV = datagen.VOCAB, HEAD_DRAFT_ROWS
         m = datagen.matrix(fg.FP8_ROW, V, H, datagen.tensor_seed("c3", "head"), device=dev)
         Wh = fg.pack(fg.FP8_ROW, m["codes"], m["scales"])
         del m
@@ -590,6 +605,34 @@ def cpu_baseline_products(fg, datagen, torch, name, M, bytes_per_step):
     return baseline_entry(bytes_per_step, legs, per_token=False)
 
 
+def cpu_baseline_head(fg, datagen, torch, M, bytes_per_step, draft_rows):
+    """The FP8 head: the oracle's logits over every 8th row (every 64th at one
+    thread) and the greedy pick of those rows; scaled to one step (logits, the
+    fused pick and the draft pick: 2 x 248320 + draft_rows rows)."""
+    import numpy as np
+
+    import oracle
+
+    H, V = datagen.HIDDEN, datagen.VOCAB
+    m = datagen.matrix(fg.FP8_ROW, V, H, datagen.tensor_seed("c3", "head"), device="cuda")
+    hc, hs = m["codes"].cpu().numpy(), m["scales"].cpu().numpy()
+    del m
+    X = datagen.bf16_normal((M, H), datagen.tensor_seed("head", "x", M), device="cuda").cpu().view(
+        torch.int16).numpy().view(np.uint16)
+
+    def run(th, every):
+        rows = np.arange(0, V, every, dtype=np.int64)
+        y, _ = oracle.gemv(3, hc, hs, 1.0, X, rows=rows, nthreads=th)
+        np.argmax(y, axis=1)
+
+    legs = []
+    for th, every in ((box_threads(), 8), (1, 64)):
+        med, runs = median3(lambda: run(th, every))
+        legs.append((th, med * every * (2 * V + draft_rows) / V,
+                     f"every {every}th head row (logits and their greedy pick), scaled to one step", runs))
+    return baseline_entry(bytes_per_step, legs, per_token=False)
+
+
 # ---- main ---------------------------------------------------------------------------------------
 
 
@@ -696,7 +739,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": counter_traffic(dominant),
+            "traffic": counter_traffic(args.workload, M, resolved_path(args.workload, args.path, M), args.fmt, dominant),
             "avg_us": round(dom_avg, 3),
             "launches_timed": n_dom,
             "timed_by": dom_how,
@@ -712,6 +755,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_moe(fg, datagen, torch, bytes_per_step, M)
         elif args.workload in ("c1", "c2", "c4") and args.fmt == "nvfp4":
             out["cpu_baseline"] = cpu_baseline_products(fg, datagen, torch, args.workload, M, bytes_per_step)
+        elif args.workload == "head":
+            out["cpu_baseline"] = cpu_baseline_head(fg, datagen, torch, M, bytes_per_step, HEAD_DRAFT_ROWS)
     print(json.dumps(out), flush=True)
 
 

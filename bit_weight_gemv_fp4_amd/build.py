@@ -1,7 +1,8 @@
 """Compile the gfx950 HIP sources of this package into libfp4gemv.so (in-tree).
 
 Every .hip file under csrc/ is compiled to an object in parallel, then linked into
-one shared library next to this file.  Flags: gfx950 only, -O3, and packed-FP32
+one shared library next to this file; the measurement programs (csrc/*.cpp, C ABI
+only) are then linked against it.  Flags: gfx950 only, -O3, and packed-FP32
 instruction selection disabled (the kernels use scalar FP32 and bf16 dot
 products).
 """
@@ -17,6 +18,8 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 BUILD = PKG.parent / "_build"
 LIB = PKG / "libfp4gemv.so"
+# stand-alone programs linked against the library (measurement drivers)
+PROGRAMS = {"moe_layer_timing": CSRC / "moe_layer_timing.cpp"}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -67,6 +70,13 @@ def build(verbose: bool = False, jobs: int | None = None, incremental: bool = Fa
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    for name, src in PROGRAMS.items():
+        exe = PKG / name
+        cmd = [HIPCC, *FLAGS, str(src), "-L", str(PKG), "-lfp4gemv", "-Wl,-rpath,$ORIGIN", "-o", str(exe) + ".tmp"]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(str(exe) + ".tmp", exe)
     return LIB
 
 
