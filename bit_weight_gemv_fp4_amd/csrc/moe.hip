@@ -133,7 +133,8 @@ __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
 // pick is the wave maximum of the lanes' heads: first of the high words (the
 // logit's order) by DPP; when exactly one lane holds that value (the usual
 // case) it is the winner, otherwise the full 64-bit maximum breaks the tie by
-// the lower expert index.  The winner drops its head.
+// the lower expert index.  The winner drops its head.  The loop has no branch
+// but the rare tie: lane j keeps pick j and writes it afterwards.
 template <int M>
 __device__ __forceinline__ void pick_sorted(const MoeParams& p, RouteLds<M>& r, int m, int lane, int npick,
                                             float& myv, float& v0) {
@@ -150,6 +151,7 @@ __device__ __forceinline__ void pick_sorted(const MoeParams& p, RouteLds<M>& r, 
   cas_desc(k[2], k[4]); cas_desc(k[3], k[5]);
   cas_desc(k[1], k[4]); cas_desc(k[3], k[6]);
   cas_desc(k[1], k[2]); cas_desc(k[3], k[4]); cas_desc(k[5], k[6]);
+  uint64_t mine = 0ull, first = 0ull;
   for (int j = 0; j < npick; ++j) {
     const uint32_t hi = (uint32_t)(k[0] >> 32);
     const uint32_t top = wave_max_u32(hi);
@@ -164,18 +166,19 @@ __device__ __forceinline__ void pick_sorted(const MoeParams& p, RouteLds<M>& r, 
     } else {
       best = wave_max_key(hi == top ? k[0] : 0ull);
     }
-    if (k[0] == best) {
+    const bool won = k[0] == best;
 #pragma unroll
-      for (int t = 0; t < 7; ++t) k[t] = k[t + 1];
-      k[7] = 0ull;
-    }
-    const float bv = key_value(best);
-    if (j == 0) v0 = bv;  // picks come in descending order
-    if (lane == j) myv = bv;
-    if (lane == 0) {
-      r.ids[m][j] = key_index(best);
-      r.v[m][j] = bv;
-    }
+    for (int t = 0; t < 7; ++t) k[t] = won ? k[t + 1] : k[t];
+    k[7] = won ? 0ull : k[7];
+    mine = lane == j ? best : mine;
+    first = j == 0 ? best : first;
+  }
+  v0 = key_value(first);  // picks come in descending order
+  if (lane < npick) {
+    const float bv = key_value(mine);
+    myv = bv;
+    r.ids[m][lane] = key_index(mine);
+    r.v[m][lane] = bv;
   }
 }
 
