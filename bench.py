@@ -16,7 +16,7 @@ the roofline of the dominant kernel (timed live with HIP events), and the
 FP64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload c3|c3m|c1|c2|c4|c5|head|copy]
-                    [--M vectors] [--path auto|valu|mfma] [--router] [--breakdown]
+                    [--M vectors] [--path auto|valu|mfma] [--router] [--no-breakdown]
 
 Other workloads: c1 one 5120x5120 NVFP4 GEMV; c2 the NVFP4 MLP; c4 the MLP at a
 verify block of M vectors (up to 16); c3m the dense stream in the checkpoint's
@@ -97,7 +97,8 @@ def parse():
     ap.add_argument("--router", action="store_true",
                     help="c5: compute each layer's router logits with an FP8 512x2560 product of x")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="also time every kernel of one step")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip the per-kernel breakdown (each kind's launches timed alone, and its share of the step)")
     ap.add_argument("--path", default="auto", choices=["auto", "valu", "mfma", "a8"],
                     help="kernel path of the NVFP4/MXFP4 products (auto: MFMA from M = 3 on)")
     return ap.parse_args()
@@ -746,8 +747,8 @@ def main():
             "algorithmic_bytes_per_launch": dom_bytes,
         },
     }
-    if args.breakdown:
-        out["breakdown"] = breakdown(step, torch)
+    if not args.no_breakdown:
+        out["breakdown"] = breakdown(step, torch, ms_per_step)
     if not args.no_cpu_baseline:
         if args.workload == "c3":
             out["cpu_baseline"] = cpu_baseline_dense(fg, datagen, torch, bytes_per_step)
@@ -789,8 +790,9 @@ def kind_avg_us(step, torch, kind, reps=5):
     return e0.elapsed_time(e1) * 1e3 / (reps * n)
 
 
-def breakdown(step, torch):
-    """Per-kind average launch time (each kind's launches alone in a graph)."""
+def breakdown(step, torch, ms_per_step):
+    """Per-kind average launch time (each kind's launches alone in a graph), its
+    bandwidth, and the share of one step its launches account for."""
     agg = {}
     for kind, _, b in step.calls:
         a = agg.setdefault(kind, {"launches": 0, "bytes": 0})
@@ -800,6 +802,7 @@ def breakdown(step, torch):
         us = kind_avg_us(step, torch, kind)
         a["avg_us"] = round(us, 3)
         a["GB/s"] = round(a["bytes"] / a["launches"] / (us * 1e-6) / 1e9, 1)
+        a["share_of_step"] = round(a["launches"] * us / step.steps_per_replay / (ms_per_step * 1e3), 4)
     return agg
 
 
