@@ -376,3 +376,17 @@ def test_workspace_check_error_paths():
     assert L.fp4g_workspace_check(fg.OP_MOE, ctypes.byref(moe_desc()), 17, FAKE, 1 << 30, ctypes.byref(n),
                                   None) == E_SHAPE
     assert n.value == 7  # untouched
+
+
+def test_moe_layer_timing_program_rejects_bad_arguments():
+    """The MoE layer timing program (built with the library) links against it and
+    refuses out-of-range arguments before touching a GPU."""
+    import subprocess
+
+    exe = Path(fg.__file__).resolve().parent / "moe_layer_timing"
+    if not exe.exists():
+        pytest.skip("timing program not built")
+    for args in (["0"], ["17"], ["1", "0"], ["1", "65"], ["1", "4", "0"]):
+        r = subprocess.run([str(exe), *args], capture_output=True, text=True, timeout=60)
+        assert r.returncode == 2, (args, r.returncode, r.stderr)
+        assert "usage" in r.stderr
