@@ -137,17 +137,6 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Maximum of a 32-bit value over the 64 lanes, uniform (the same DPP steps).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false));
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
 // Sum of lanes 0..7 (the others must hold 0), uniform: row_shr 1, 2, 4 add
 // pairs, then pairs of pairs, so lane 7 holds ((e7+e6)+(e5+e4))+((e3+e2)+(e1+e0)).
 __device__ __forceinline__ float wave_sum8(float v) {

@@ -130,11 +130,12 @@ __device__ __forceinline__ void cas_desc(uint64_t& a, uint64_t& b) {
 // The K picks of token m from its logits, one wave, E <= 512: each lane holds
 // the pick keys of experts lane + 64 t (t < 8), sorted descending by a 19-
 // comparator network, so the lane's best remaining key is always key[0].  A
-// pick is the wave maximum of the lanes' heads: first of the high words (the
-// logit's order) by DPP; when exactly one lane holds that value (the usual
-// case) it is the winner, otherwise the full 64-bit maximum breaks the tie by
-// the lower expert index.  The winner drops its head.  The loop has no branch
-// but the rare tie: lane j keeps pick j and writes it afterwards.
+// pick is the 64-bit wave maximum of the lanes' heads (DPP; keys are distinct,
+// equal logits ordered by the lower expert index), and the lane holding it
+// drops its head.  The loop has no branch: the shift is by selects, and lane j
+// keeps pick j and writes it afterwards.  (A 32-bit maximum of the high words
+// with a ballot for ties took 17% longer: the scalar round trips cost more
+// than the second word saves.)
 template <int M>
 __device__ __forceinline__ void pick_sorted(const MoeParams& p, RouteLds<M>& r, int m, int lane, int npick,
                                             float& myv, float& v0) {
@@ -153,19 +154,7 @@ __device__ __forceinline__ void pick_sorted(const MoeParams& p, RouteLds<M>& r, 
   cas_desc(k[1], k[2]); cas_desc(k[3], k[4]); cas_desc(k[5], k[6]);
   uint64_t mine = 0ull, first = 0ull;
   for (int j = 0; j < npick; ++j) {
-    const uint32_t hi = (uint32_t)(k[0] >> 32);
-    const uint32_t top = wave_max_u32(hi);
-    const uint64_t tie = __ballot(hi == top);
-    uint64_t best;
-    if (__popcll(tie) == 1) {
-      const int w = __ffsll((unsigned long long)tie) - 1;
-      // readlane returns int: widen it as unsigned, or the low word's top bit
-      // (always set: it holds 0xffffffff - e) would fill the high word
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((uint32_t)k[0], w);
-      best = ((uint64_t)top << 32) | lo;
-    } else {
-      best = wave_max_key(hi == top ? k[0] : 0ull);
-    }
+    const uint64_t best = wave_max_key(k[0]);
     const bool won = k[0] == best;
 #pragma unroll
     for (int t = 0; t < 7; ++t) k[t] = won ? k[t + 1] : k[t];
