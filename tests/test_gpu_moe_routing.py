@@ -60,3 +60,19 @@ def test_no_shared_expert_pick_order():
     X = datagen.bf16_normal((1, 256), 251, device=DEV)
     logits = datagen.router_logits(1, 64, 252, device=DEV)
     check_moe(layer, expert, sh, X, logits, 8)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_layer_timing_program_picks(M):
+    """The C++ layer timing program drives moe_route_gemv through the C ABI on
+    C5-shaped layers and checks every token's picks against a host top-8 of the
+    same logits (it exits non-zero on the first mismatch)."""
+    import subprocess
+    from pathlib import Path
+
+    log("layer timing program", M)
+    exe = Path(fg.__file__).resolve().parent / "moe_layer_timing"
+    assert exe.exists(), "moe_layer_timing is built with the library"
+    r = subprocess.run([str(exe), str(M), "2", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "picks match the host top-8" in r.stdout
