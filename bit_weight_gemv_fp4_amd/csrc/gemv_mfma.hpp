@@ -30,6 +30,8 @@
 //    scales, double-buffered.  The reduction across waves reuses the input's
 //    LDS area, so a workgroup holds no more LDS than its staged input.
 #pragma once
+#include <type_traits>
+
 #include "gemv_kernel.hpp"
 
 namespace fp4g {
@@ -81,6 +83,36 @@ __device__ __forceinline__ void load_mfrag(MFrag<FMT>& f, const uint8_t* tile, i
     } else {
       f.s[r][0] = ld_stream1(sp);
     }
+  }
+}
+
+// A whole tile for the NVFP4 gate/up forms up to kMaxM vectors: its eight code slots
+// and the lane's own row of block scales as stored (one 16-byte load per lane
+// for NVFP4, 8 bytes for MXFP4, as the VALU kernel reads them).  The scales
+// reach the lanes that apply them (rows 16 r + l % 16) through LDS when the
+// tile is consumed, in s, laid out as MFrag's.  Against half tiles with four
+// scale loads each, this took the NVFP4 17408x5120 gate/up pair from 31.0 to
+// 27.8 us at M = 4 (at three waves per SIMD: 144 registers); the plain
+// products keep half tiles (no gain on the down projection).
+template <uint32_t FMT>
+struct MTile {
+  static constexpr int SL = 8;
+  static constexpr int SW = FMT == FP4G_NVFP4 ? 4 : 2;
+  u32x4 q[SL];
+  uint32_t sr[SW];
+  uint32_t s[4][SW];
+};
+
+template <uint32_t FMT>
+__device__ __forceinline__ void load_mtile(MTile<FMT>& f, const uint8_t* tile, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.q[j] = ld_stream(tile + j * 1024 + lane * 16);
+  if constexpr (FMT == FP4G_NVFP4) {
+    const u32x4 v = ld_stream(tile + kCodeBytes + lane * 16);
+    f.sr[0] = v[0], f.sr[1] = v[1], f.sr[2] = v[2], f.sr[3] = v[3];
+  } else {
+    const u32x2 v = ld_stream2(tile + kCodeBytes + lane * 8);
+    f.sr[0] = v[0], f.sr[1] = v[1];
   }
 }
 
@@ -136,19 +168,27 @@ struct MfmaMoe {
   int cd, dff;           // down: chunks per slot; d_ff
 };
 
+// Gate/up forms that stream whole tiles (MTile): NVFP4 up to kMaxM vectors.
+// (MXFP4 keeps half tiles: its gate/up pair went from 28.4 to 30.0 us at M = 4
+// with whole tiles, and the MoE layer with it.)
+template <uint32_t FMT, int M, int NMAT>
+constexpr bool mfma_whole_tiles() {
+  return FMT == FP4G_NVFP4 && NMAT == 2 && M <= kMaxM;
+}
+
 // Waves per SIMD the register allocation aims for.  VGPRs and AGPRs share one
 // file of 512 per lane, so four waves leave 128 registers: enough, without
-// spills, for the plain and gate/up forms up to 8 vectors, the plain form up to
-// 16 and the MoE gate/up (measured 5-25% faster than at three waves).  Gate/up
-// above 8 vectors and the MoE down would spill at that budget; three waves (170
-// registers) fit them, where they would otherwise take 196 and up to 296.
-template <int M, int NMAT, int MODE>
+// spills, for the plain forms up to 16 vectors and the half-tile gate/up forms
+// up to 8 (measured 5-25% faster than at three waves).  Whole-tile gate/up,
+// gate/up above 8 vectors and the MoE down would spill at that budget; three
+// waves (170 registers) fit them.
+template <uint32_t FMT, int M, int NMAT, int MODE>
 constexpr int mfma_waves_per_eu() {
-  return (NMAT == 2 && M > kMaxM) || MODE == 2 ? 3 : 4;
+  return mfma_whole_tiles<FMT, M, NMAT>() || (NMAT == 2 && M > kMaxM) || MODE == 2 ? 3 : 4;
 }
 
 template <uint32_t FMT, int M, int NMAT, int EPI, int MODE = 0>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<M, NMAT, MODE>())))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(mfma_waves_per_eu<FMT, M, NMAT, MODE>())))
 void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   constexpr bool MOE = MODE == 1, MOED = MODE == 2;
   // NVFP4 with up to 8 vectors: both blocks of a slot in one MFMA (A rows 8..15
@@ -162,6 +202,11 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   // the staged-input area, reused once every wave has finished reading it.
   constexpr bool kRedInX = NV > kMfmaRedOwn;
   __shared__ float red_own[kRedInX ? 1 : kWavesPerWg][kRedInX ? 1 : NV][64];
+  // NVFP4 gate/up up to kMaxM vectors streams whole tiles (MTile); their scales
+  // pass through one row of 16 bytes per lane here
+  constexpr bool WHOLE = mfma_whole_tiles<FMT, M, NMAT>();
+  using Frag = std::conditional_t<WHOLE, MTile<FMT>, MFrag<FMT>>;
+  __shared__ u32x4 sc_lds[WHOLE ? kWavesPerWg : 1][WHOLE ? 64 : 1];
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // [M][wg_chunks * 512 + kXPad] bf16, then zeros
   float(*red)[NV][64] = kRedInX ? reinterpret_cast<float(*)[NV][64]>(xs) : reinterpret_cast<float(*)[NV][64]>(red_own);
 
@@ -198,7 +243,7 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   const int64_t tile0 = (int64_t)g * (MOED ? q.cd : p.C);
   // items (chunk, part, matrix), matrix fastest: with NMAT = 2 the even items
   // are gate, the odd ones up
-  constexpr int SL = MFrag<FMT>::SL, PER = 8 / SL;  // parts per tile
+  constexpr int SL = Frag::SL, PER = 8 / SL;  // parts per tile
   auto item_tile = [&](int it) {
     const int cv = c0 + it / (PER * NMAT);
     if constexpr (MOED) {
@@ -209,11 +254,13 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
     return (it % NMAT ? w1 : w0) + (tile0 + cv) * TILE;
   };
   auto item_half = [&](int it) { return (it / NMAT) % PER; };
-
   // first fragment in flight before the input is staged
   const int n_items = (c1 - c0) * PER * NMAT;
-  MFrag<FMT> fa, fb;
-  if (n_items > 0) load_mfrag<FMT>(fa, item_tile(0), item_half(0), lane);
+  Frag fa, fb;
+  if (n_items > 0) {
+    if constexpr (WHOLE) load_mtile<FMT>(fa, item_tile(0), lane);
+    else load_mfrag<FMT>(fa, item_tile(0), item_half(0), lane);
+  }
 
   // stage x[m][256 wg_c0 ..) for m < M (zero past d_in), then the zero area; all
   // loads are issued before the first LDS store
@@ -279,7 +326,22 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[a][r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto consume = [&](MFrag<FMT>& f, int it, f32x4(&ac)[4]) {
+  auto consume = [&](Frag& f, int it, f32x4(&ac)[4]) {
+    if constexpr (WHOLE) {
+      // the tile's scales: each lane writes its own row, then reads the rows
+      // 16 r + cl whose products it holds (one wave's area: the LDS keeps a
+      // wave's accesses in order)
+      if constexpr (FMT == FP4G_NVFP4)
+        sc_lds[wave][lane] = u32x4{f.sr[0], f.sr[1], f.sr[2], f.sr[3]};
+      else
+        sc_lds[wave][lane] = u32x4{f.sr[0], f.sr[1], 0u, 0u};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const u32x4 v = sc_lds[wave][16 * r + cl];
+#pragma unroll
+        for (int w = 0; w < MTile<FMT>::SW; ++w) f.s[r][w] = v[w];
+      }
+    }
     const int cc = c0 + it / (PER * NMAT) - wg_c0;  // chunk within the staged range
     const int half = item_half(it);
     // weights of the lane's four vectors (MoE down: the chunk's slot's
@@ -339,13 +401,16 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   if (n_items > 0) {
     int it = 0;
     for (; it + 2 < n_items; it += 2) {
-      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane);
+      if constexpr (WHOLE) load_mtile<FMT>(fb, item_tile(it + 1), lane);
+      else load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane);
       consume(fa, it, acc[0]);
-      load_mfrag<FMT>(fa, item_tile(it + 2), item_half(it + 2), lane);
+      if constexpr (WHOLE) load_mtile<FMT>(fa, item_tile(it + 2), lane);
+      else load_mfrag<FMT>(fa, item_tile(it + 2), item_half(it + 2), lane);
       consume(fb, it + 1, acc[NMAT - 1]);
     }
     if (it + 1 < n_items) {
-      load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane);
+      if constexpr (WHOLE) load_mtile<FMT>(fb, item_tile(it + 1), lane);
+      else load_mfrag<FMT>(fb, item_tile(it + 1), item_half(it + 1), lane);
       consume(fa, it, acc[0]);
       consume(fb, it + 1, acc[NMAT - 1]);
     } else {
