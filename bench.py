@@ -50,9 +50,18 @@ TRAFFIC_SOURCES = ("bit_weight_gemv_fp4_amd/build.py", "bit_weight_gemv_fp4_amd/
 
 
 def traffic_sources_hash():
+    """First 16 hex digits of a sha256 over the kernel sources' code: comments
+    and runs of white space are dropped first, so that the committed counters
+    stay valid across edits that cannot change a kernel."""
     import hashlib
+    import re
 
-    return hashlib.sha256(b"".join((ROOT / q).read_bytes() for q in TRAFFIC_SOURCES)).hexdigest()[:16]
+    def code(text):
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        return " ".join(text.split())
+
+    return hashlib.sha256("\n".join(code((ROOT / q).read_text()) for q in TRAFFIC_SOURCES).encode()).hexdigest()[:16]
 
 
 def resolved_path(workload, path, M):

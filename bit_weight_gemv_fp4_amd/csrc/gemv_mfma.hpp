@@ -27,7 +27,8 @@
 //    other half), so one MFMA still gives both blocks' sums separately; with
 //    M > 8 each block takes its own MFMA.
 //  * A work item is kMfmaSlots code slots of one tile (half of it) and their
-//    scales, double-buffered.  The reduction across waves reuses the input's
+//    scales, double-buffered; the NVFP4 gate/up forms up to 8 vectors take
+//    whole tiles instead (MTile).  The reduction across waves reuses the input's
 //    LDS area, so a workgroup holds no more LDS than its staged input.
 #pragma once
 #include <type_traits>
@@ -86,14 +87,15 @@ __device__ __forceinline__ void load_mfrag(MFrag<FMT>& f, const uint8_t* tile, i
   }
 }
 
-// A whole tile for the NVFP4 gate/up forms up to kMaxM vectors: its eight code slots
-// and the lane's own row of block scales as stored (one 16-byte load per lane
-// for NVFP4, 8 bytes for MXFP4, as the VALU kernel reads them).  The scales
-// reach the lanes that apply them (rows 16 r + l % 16) through LDS when the
-// tile is consumed, in s, laid out as MFrag's.  Against half tiles with four
-// scale loads each, this took the NVFP4 17408x5120 gate/up pair from 31.0 to
-// 27.8 us at M = 4 (at three waves per SIMD: 144 registers); the plain
-// products keep half tiles (no gain on the down projection).
+// A whole tile, for the NVFP4 gate/up forms up to kMaxM vectors: its eight code
+// slots and the lane's own row of block scales as stored (one 16-byte load per
+// lane, as the VALU kernel reads them; 8 bytes for MXFP4).  The scales reach
+// the lanes that apply them (rows 16 r + l % 16) through LDS when the tile is
+// consumed, into s, laid out as MFrag's.  Against half tiles with four scale
+// loads each (whose 128-byte scale lines both halves of a tile fetch), this
+// took the 17408x5120 gate/up pair from 30.7 to 27.0 us at M = 4, at three
+// waves per SIMD (144 registers); the plain products keep half tiles (no gain
+// on the down projection).
 template <uint32_t FMT>
 struct MTile {
   static constexpr int SL = 8;
@@ -254,6 +256,7 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
     return (it % NMAT ? w1 : w0) + (tile0 + cv) * TILE;
   };
   auto item_half = [&](int it) { return (it / NMAT) % PER; };
+
   // first fragment in flight before the input is staged
   const int n_items = (c1 - c0) * PER * NMAT;
   Frag fa, fb;
