@@ -562,10 +562,32 @@ struct MoeLayout {
 // registers and is still the fastest measured).  k_moe_down fits 16 waves per
 // CU up to M = 5, like the dense kernel.
 inline Plan plan_up(int64_t R, int64_t C, int M) { return plan_latency(R, C, 12, {4, 8, 12}); }
-inline Plan plan_dn(int64_t R, int64_t C, int M) { return plan_latency(R, C, M <= 5 ? 16 : 12, {4, 8, 16}); }
+// Down projection on the VALU kernel.  At four vectors (the last count before
+// the matrix cores take over) each tile costs four v_dot2 per weight pair, and
+// spreading the tiles over every SIMD outweighs the tree: four-wave workgroups
+// with one chunk per wave (C5 shapes, measured per layer with the gate/up plan
+// below: 50.3 -> 48.1 us; the latency plan's 16-wave workgroups covered 160 of
+// the 256 CUs).  Fewer vectors keep the latency plan (one chunk per wave was
+// 0.8-1.2 us slower at one and two vectors, 2.3 us at three).
+inline Plan plan_dn(int64_t R, int64_t C, int M) {
+  if (M == 4) {
+    const int64_t wg_chunks = 4, S = (C + wg_chunks - 1) / wg_chunks;
+    return Plan{(int)S, (int)((C + S - 1) / S), 4};
+  }
+  return plan_latency(R, C, M <= 5 ? 16 : 12, {4, 8, 16});
+}
 // gate/up plan and exchange units per lane for M vectors (either kernel; the
-// W4A8 path always runs on the matrix cores, planned like the bf16 ones)
+// W4A8 path always runs on the matrix cores, planned like the bf16 ones).  On
+// the matrix cores, once the union's row groups alone fill the CUs, K is not
+// split unless the staged input needs it (no tree: C5 shapes, per layer, 55.6 ->
+// 50.3 us at four vectors, 72.2 -> 70.6 at six, unchanged at three and eight;
+// the W4A8 path keeps the shared plan).
 inline Plan plan_gu(int64_t R, int64_t C, int M, bool a8) {
+  if (!a8 && M >= kMoeMfmaMinM && R >= kCUs) {
+    const int64_t max_chunks = kMfmaXBytes / (M * 512);
+    const int64_t S = (C + max_chunks - 1) / max_chunks, wg_chunks = (C + S - 1) / S;
+    return Plan{(int)((C + wg_chunks - 1) / wg_chunks), (int)wg_chunks, kWavesPerWg};
+  }
   return a8 || M >= kMoeMfmaMinM ? plan_mfma(R, C, 2, M) : plan_up(R, C, M);
 }
 inline int units_gu(int M, bool a8) { return a8 || M >= kMoeMfmaMinM ? kMoeMfmaUnits : M; }

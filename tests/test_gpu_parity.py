@@ -597,6 +597,19 @@ def test_config5_moe_layer(M):
     check_moe(layer, expert, sh, X, logits, 8)
 
 
+@pytest.mark.parametrize("M", [4, 6])
+def test_config5_moe_layer_nvfp4(M):
+    """The same layer with NVFP4 experts and tensor scales other than 1 (the
+    matrix-core gate/up without a K split once the union's row groups fill the
+    CUs; at M = 4 the VALU down with one chunk per wave)."""
+    log("C5 moe nvfp4", M)
+    layer, expert, sh = build_moe(fg.NVFP4, 512, 8, 2560, 768, seed=6, tscales=(0.5, 2.0, 1.5),
+                                  sh_tscales=(1.25, 0.75, 2.0))
+    X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("C5nx", M), device=DEV)
+    logits = datagen.router_logits(M, 512, datagen.tensor_seed("C5nl", M), device=DEV)
+    check_moe(layer, expert, sh, X, logits, 8)
+
+
 def test_config5_lm_head():
     log("C5 head")
     W, host = make(fg.FP8_ROW, 157184, 2560, seed=500)
