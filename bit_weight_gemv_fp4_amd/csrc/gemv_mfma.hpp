@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "gemv_kernel.hpp"
+#include "moe_route.hpp"
 
 namespace fp4g {
 
@@ -168,7 +169,15 @@ struct MfmaMoe {
   const float* coef;     // down: [slot][M]
   const uint16_t* hbuf;  // down: bf16 [slot][M][d_ff]
   int cd, dff;           // down: chunks per slot; d_ff
+  MoeParams rp;          // gate/up up to kMfmaMoeRouteM vectors: routing inputs and tables
 };
+
+// MoE gate/up forms that route the tokens themselves (one wave per token, each
+// workgroup for itself; workgroup 0 also writes the routing tables for the down
+// half), instead of reading a routing launch's tables: the launch and its two
+// dependent table reads leave the layer's critical path.  Above four vectors a
+// wave would route several tokens in turn, so those keep the routing launch.
+constexpr int kMfmaMoeRouteM = 4;
 
 // Gate/up forms that stream whole tiles (MTile): NVFP4 up to kMaxM vectors.
 // (MXFP4 keeps half tiles: its gate/up pair went from 28.4 to 30.0 us at M = 4
@@ -209,6 +218,8 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   constexpr bool WHOLE = mfma_whole_tiles<FMT, M, NMAT>();
   using Frag = std::conditional_t<WHOLE, MTile<FMT>, MFrag<FMT>>;
   __shared__ u32x4 sc_lds[WHOLE ? kWavesPerWg : 1][WHOLE ? 64 : 1];
+  constexpr bool ROUTE = MOE && M <= kMfmaMoeRouteM;
+  __shared__ RouteLds<ROUTE ? M : 1> rl;
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // [M][wg_chunks * 512 + kXPad] bf16, then zeros
   float(*red)[NV][64] = kRedInX ? reinterpret_cast<float(*)[NV][64]>(xs) : reinterpret_cast<float(*)[NV][64]>(red_own);
 
@@ -224,8 +235,15 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
   if constexpr (MOE) {
     slot = uniform(gt / q.rg);
     g = gt - slot * q.rg;
-    if (slot >= q.route[0]) return;  // past the realised union: no byte read
-    expert = q.route[1 + slot];
+    if constexpr (ROUTE) {
+      route_tokens<M, kWavesPerWg>(q.rp, rl);
+      if (blockIdx.x == 0) write_route_tables<M, kWavesPerWg>(q.rp, rl);
+      if (slot >= rl.n_slots) return;  // past the realised union: no byte read
+      expert = rl.uni[slot];
+    } else {
+      if (slot >= q.route[0]) return;
+      expert = q.route[1 + slot];
+    }
     w0 = expert >= 0 ? p.w[0] + (uint64_t)expert * q.stride[0] : q.sh[0];
     w1 = expert >= 0 ? p.w[1] + (uint64_t)expert * q.stride[1] : q.sh[1];
   }
@@ -491,8 +509,11 @@ void k_gemv_mfma(GemvParams p, MfmaMoe q) {
             if (expert < 0) {
               q.hdbg[((int64_t)m * q.nh + q.k) * d_out + row] = hv;
             } else {
-              for (int j = 0; j < q.k; ++j)
-                if (q.ids[m * q.k + j] == expert) q.hdbg[((int64_t)m * q.nh + j) * d_out + row] = hv;
+              for (int j = 0; j < q.k; ++j) {
+                // the picks: this workgroup's own routing, or the routing launch's table
+                const int id = ROUTE ? rl.ids[ROUTE ? m : 0][j] : q.ids[m * q.k + j];
+                if (id == expert) q.hdbg[((int64_t)m * q.nh + j) * d_out + row] = hv;
+              }
             }
           }
         }
