@@ -29,12 +29,13 @@
 //             experts need no combine step; the K shares meet in the exchange
 //             tree, whose survivor writes Y.
 //
-// From M = 3 vectors on, the gate/up half runs on the matrix cores instead:
-// k_moe_route (one workgroup; the union through an LDS bitmap) routes the
-// tokens once and writes the tables, then the matrix-core product
-// (gemv_mfma.hpp) takes each slot's expert from them, and
-// k_moe_down follows as above; from M = 5 on the down half also runs on the
-// matrix-core kernel (its down mode).  Measured crossovers set both thresholds.
+// From M = 3 vectors on, the gate/up half runs on the matrix cores instead
+// (gemv_mfma.hpp).  Up to 4 vectors its workgroups route the tokens themselves
+// (one wave per token, the union through an LDS bitmap; workgroup 0 writes the
+// tables); above that k_moe_route (one workgroup) routes once and writes the
+// tables that the matrix-core product reads.  k_moe_down follows as above;
+// from M = 5 on the down half also runs on the matrix-core kernel (its down
+// mode).  Measured crossovers set the thresholds.
 // Verify blocks of 9..16 tokens (feed, "DFlash2: drafting a block in one pass":
 // 11 positions) take the same three launches, the routing workgroup with one
 // wave per token.  With 8-bit activations (W4A8, fp4g_moe.act) every M takes
