@@ -586,10 +586,11 @@ def test_moe_ties_and_repeat():
     assert torch.equal(Y1, Y2)
 
 
-@pytest.mark.parametrize("M", [1, 4, 6, 8])
+@pytest.mark.parametrize("M", [1, 3, 4, 6, 8])
 def test_config5_moe_layer(M):
     """Ling-3.0-flash-shaped MoE layer: 512 MXFP4 experts 768x2560 / 2560x768, top-8 + shared
-    (M = 1: VALU gate/up and down; 4: matrix-core gate/up; 6, 8: both halves on the matrix cores)."""
+    (M = 1: VALU gate/up and down; 3, 4: matrix-core gate/up whose workgroups route the
+    tokens themselves; 6, 8: a routing launch, then both halves on the matrix cores)."""
     log("C5 moe", M)
     layer, expert, sh = build_moe(fg.MXFP4, 512, 8, 2560, 768, seed=5)
     X = datagen.bf16_normal((M, 2560), datagen.tensor_seed("C5x", M), device=DEV)
