@@ -18,9 +18,11 @@ Sources for what is computed (the pages carry no code):
     FP8 output layer; sec. 8: M tokens touch the union of their experts, about
     512 * (1 - (1 - 8/512)^M) of them.
 
-Parity pins: see tests/test_oracle_pins.py.  Parity unpinned: the bf16 rounding
-of the MLP intermediate h (pinned only through the tolerance bound) and the
-end-to-end MoE output (pinned stage by stage).
+Parity pins: see tests/test_oracle_pins.py (the MoE layer end to end through its
+invariants: identical experts ignore the routing, top-1 is the argmax expert's
+output, the output is the gate-weighted sum).  Parity unpinned: the bf16 rounding
+of the MLP intermediate h, which this oracle keeps in FP64 (the GPU's h is held
+to it within the tolerance bound plus half a bf16 step).
 """
 from __future__ import annotations
 
