@@ -65,6 +65,25 @@ def check_h(H_gpu, gate, up, X_bits, rows=None):
     assert not bad.any(), f"{bad.sum()} h values out of bound"
 
 
+def check_mlp_e2e(Y_gpu, H_gpu, gate, up, down, X_bits, rows):
+    """Dense MLP end to end against the pure FP64 oracle (h kept in FP64): on the
+    given output rows, |y - y_oracle| <= TOL sum_i |d[r][i] h^[i]| + sum_i
+    |d[r][i]| hb[i] (1.0001 slack for the bound's own rounding), hb the h bound of
+    every intermediate -- the bound the gate/up and down checks imply."""
+    r = oracle.gate_up_silu(gate, up, X_bits)
+    hb = h_bound(r, r["h"])
+    assert np.all(np.abs(H_gpu.detach().float().cpu().double().numpy().reshape(r["h"].shape) - r["h"]) <= hb)
+    y_ref, _ = oracle.gemv(down["format"], down["codes"], down["scales"], down["tensor_scale"], r["h"], rows=rows)
+    _, A_h = oracle.gemv(down["format"], down["codes"], down["scales"], down["tensor_scale"],
+                         bits(H_gpu).reshape(r["h"].shape), rows=rows)
+    _, A_hb = oracle.gemv(down["format"], down["codes"], down["scales"], down["tensor_scale"], hb, rows=rows)
+    y = Y_gpu.detach().cpu().double().numpy().reshape(y_ref.shape[0], -1)[:, rows]
+    bound = TOL * A_h + A_hb
+    ratio = float(np.max(np.abs(y - y_ref) / np.maximum(bound, 1e-300)))
+    log(f"mlp end-to-end against the derived bound: worst ratio {ratio:.3g}")
+    assert np.all(np.abs(y - y_ref) <= 1.0001 * bound)
+
+
 def build_moe(fmt, E, k, hidden, dff, seed, shared=True, tscales=(1.0, 1.0, 1.0), sh_tscales=(1.0, 1.0, 1.0),
               scales=None, sh_scales=None, act=0):
     """An MoE layer of E routed experts (and a shared one if `shared`), packed

@@ -21,7 +21,7 @@ import torch
 import bit_weight_gemv_fp4_amd as fg
 import datagen
 import oracle
-from gpu_common import (DEV, TOL, bits, build_moe, check_h, check_moe, check_product, h_bound, log, make,
+from gpu_common import (DEV, TOL, bits, check_mlp_e2e, build_moe, check_h, check_moe, check_product, h_bound, log, make,
                         sample_rows)
 from oracle import layout
 
@@ -542,6 +542,7 @@ def test_config2_and_4_mlp(M, path):
     check_h(H, hg, hu, bits(X), rows=rows)
     drows = sample_rows(5120, 160, seed=M + 10)
     check_product(Y, hd, bits(H), rows=drows)  # down, given the GPU's own h
+    check_mlp_e2e(Y, H, hg, hu, hd, bits(X), drows)  # end to end, h in FP64
 
 
 @pytest.mark.parametrize("shape", [(12288, 5120), (5120, 12288), (7680, 5120)])
