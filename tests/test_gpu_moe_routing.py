@@ -32,9 +32,11 @@ def test_routing_ties(M):
 
 
 @pytest.mark.parametrize("E,k", [(100, 8), (512, 1), (640, 8), (1024, 6)])
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_routing_expert_counts(E, k, M):
-    """Partial last lane of keys (100), a single pick, and the scan path above 512."""
+    """Partial last lane of keys (100), a single pick, and the scan path above 512
+    (M = 1, 2: the VALU gate/up's routing; 3, 4: the matrix-core gate/up
+    workgroups routing for themselves)."""
     log("routing experts", E, k, M)
     layer, expert, sh = build_moe(fg.MXFP4, E, k, 256, 128, seed=22)
     X = datagen.bf16_normal((M, 256), datagen.tensor_seed("fex", E, k, M), device=DEV)
@@ -42,7 +44,7 @@ def test_routing_expert_counts(E, k, M):
     check_moe(layer, expert, sh, X, logits, k)
 
 
-@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("M", [1, 2, 4])
 def test_config5_repeated_calls(M):
     """The C5 layer three times in a row on one workspace, new inputs each time."""
     log("C5 repeat", M)
@@ -53,12 +55,14 @@ def test_config5_repeated_calls(M):
         check_moe(layer, expert, sh, X, logits, 8)
 
 
-def test_no_shared_expert_pick_order():
-    """M = 1 without a shared expert: the slots are exactly the K picks."""
-    log("no shared, M = 1")
+@pytest.mark.parametrize("M", [1, 3])
+def test_no_shared_expert_pick_order(M):
+    """Without a shared expert: at M = 1 the slots are exactly the K picks; at
+    M = 3 the union alone (the matrix-core workgroups' own routing)."""
+    log("no shared", M)
     layer, expert, sh = build_moe(fg.MXFP4, 64, 8, 256, 128, seed=25, shared=False)
-    X = datagen.bf16_normal((1, 256), 251, device=DEV)
-    logits = datagen.router_logits(1, 64, 252, device=DEV)
+    X = datagen.bf16_normal((M, 256), 251 + M, device=DEV)
+    logits = datagen.router_logits(M, 64, 252 + M, device=DEV)
     check_moe(layer, expert, sh, X, logits, 8)
 
 
